@@ -1,0 +1,258 @@
+"""CPU oracle for group-wise asymmetric INT4 quantization and dequantize-matmul.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The product path (the HIP
+library and its Python binding) never calls it and shares no code with it.
+
+Plain NumPy, written to be checked against the pages by eye.  Every
+quantization step is a single IEEE-754 float32 operation with
+round-to-nearest-even, so that the integer decisions (codes, zero-points)
+are taken in the same precision as the GPU kernels; the matmul references
+are exact-input float64.
+
+Pages cited (martinuke0.github.io posts):
+  [P1] "Hands-on Build Guide: Group-wise INT4 Weight-only Quantization with
+       Per-channel Scales"
+  [P2] "From-scratch INT4 Weight-only Quantizer with Per-group Scales and
+       Zero-points for LLMs"
+  [P3] "Building a From-Scratch Group-Wise INT4 Quantization Layer for LLaMA
+       Weights"
+  [P4] "Build a GPTQ INT4 Quantization Engine in Python/NumPy"
+  [P5] "From Scratch: Building a GPTQ INT4 Quantizer in Pure Python"
+
+Readings taken where the pages disagree or are silent (each is pinned by a
+test in tests/test_oracle_pins.py):
+  * groups are runs of ``g`` consecutive columns (in_features) of one row
+    ([P1] Architecture Overview; [P2] Architecture Overview, "Group Divisor");
+  * scale = (max - min) / 15 and zero-point = clamp(round(-min/scale), 0, 15)
+    ([P2] Architecture Overview and Step 6), computed with the scale as
+    stored (fp16 or fp32), a stored scale of 0 replaced by 1 ([P4] Step 2);
+  * code q = clamp(round(w/scale + zp), 0, 15) ([P5] Step 2), round half to
+    even; dequantized weight (q - zp) * scale ([P5] Step 4);
+  * two codes per byte, the even column in the low nibble ([P4] Step 4;
+    [P3] Step 1);
+  * per-token activation scale max(max|x|, 1e-8)/127 and
+    clamp(round(x/s), -128, 127) ([P1] Step 3);
+  * matmul y = x . dequant(W)^T ([P3] Step 2; [P4] Step 5), and for the
+    INT8-activation variant y = s_a * (x_int8 . dequant(W)^T) ([P1] Step 5).
+
+Parity pins: every function here is pinned (see tests/test_oracle_pins.py);
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+F16 = np.float16
+
+SZ_DTYPES = {"f32": np.float32, "f16": np.float16}
+
+
+# --------------------------------------------------------------------------
+# Representations.  bf16 has no NumPy dtype, so bf16 tensors are uint16 bits.
+# --------------------------------------------------------------------------
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bits -> float32: a bf16 number is the top half of an fp32."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)
+
+
+def to_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits, round to nearest, ties to even (finite input).
+
+    Drops the low 16 bits of the fp32 pattern after adding half an ulp of the
+    result (0x7FFF plus the result's lowest kept bit, which breaks ties
+    towards an even result).
+    """
+    u = np.ascontiguousarray(a, dtype=F32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    return ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)).astype(np.uint16)
+
+
+def as_f32(w: np.ndarray, kind: str) -> np.ndarray:
+    """Input tensor as exact float32 values ([P5] Step 1 works in float32)."""
+    if kind == "bf16":
+        return widen_bf16(w)
+    if kind == "f32":
+        return np.asarray(w, F32)
+    if kind == "f16":
+        return np.asarray(w, F16).astype(F32)
+    raise ValueError(kind)
+
+
+# --------------------------------------------------------------------------
+# Quantization ([P2] Architecture Overview, Steps 5-6; [P5] Step 2)
+# --------------------------------------------------------------------------
+def split_groups(w32: np.ndarray, g: int) -> np.ndarray:
+    """[N, K] -> [N, K/g, g]: each row cut into runs of g consecutive columns."""
+    n, k = w32.shape
+    if k % g:
+        raise ValueError("K must be a multiple of the group size")
+    return w32.reshape(n, k // g, g)
+
+
+def group_range(w32: np.ndarray, g: int):
+    """Per-group minimum and maximum ([P2] Step 5)."""
+    wg = split_groups(w32, g)
+    return wg.min(axis=2), wg.max(axis=2)
+
+
+def scale_zero(mn: np.ndarray, mx: np.ndarray, sz: str):
+    """Scale and zero-point per group ([P2] Architecture Overview, Step 6).
+
+    scale = fl32(fl32(max - min) / 15), rounded to the storage dtype; a stored
+    scale of zero (constant group) becomes 1 ([P4] Step 2 uses the same
+    guard).  The zero-point uses the stored scale:
+    zp = clamp(rint(fl32(-min / scale)), 0, 15), an integer.
+    Returns (scale_stored [sz dtype], zero_point [int32]).
+    """
+    sd = SZ_DTYPES[sz]
+    s32 = (mx.astype(F32) - mn.astype(F32)) / F32(15.0)
+    s_st = s32.astype(sd)
+    s_st = np.where(s_st == 0, sd(1.0), s_st).astype(sd)
+    s = s_st.astype(F32)
+    zp = np.clip(np.rint(-mn.astype(F32) / s), 0, 15).astype(np.int32)
+    return s_st, zp
+
+
+def quantize_codes(w32: np.ndarray, s_st: np.ndarray, zp: np.ndarray, g: int) -> np.ndarray:
+    """q = clamp(rint(fl32(fl32(w / scale) + zp)), 0, 15)  ([P5] Step 2)."""
+    wg = split_groups(w32, g)
+    s = s_st.astype(F32)[..., None]
+    z = zp.astype(F32)[..., None]
+    q = np.clip(np.rint(wg / s + z), 0, 15).astype(np.uint8)
+    return q.reshape(w32.shape)
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """Two codes per byte; column 2j in the low nibble, 2j+1 in the high one
+    ([P4] Step 4 states this order; [P3] Step 1 builds bytes the same way)."""
+    q = np.asarray(q, np.uint8)
+    if q.shape[-1] % 2:
+        raise ValueError("K must be even")
+    return (q[..., 0::2] | (q[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles: [N, K/2] bytes -> [N, K] codes 0..15."""
+    p = np.asarray(packed, np.uint8)
+    q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    q[..., 0::2] = p & np.uint8(0x0F)
+    q[..., 1::2] = p >> np.uint8(4)
+    return q
+
+
+def quantize_pack_int4(w: np.ndarray, kind: str, g: int, sz: str):
+    """Full quantize + pack of W [N, K].
+
+    Returns (packed uint8 [N, K/2], scales [N, K/g] in sz dtype,
+    zeros [N, K/g] in sz dtype holding the integers 0..15).
+    """
+    w32 = as_f32(w, kind)
+    mn, mx = group_range(w32, g)
+    s_st, zp = scale_zero(mn, mx, sz)
+    q = quantize_codes(w32, s_st, zp, g)
+    return pack_nibbles(q), s_st, zp.astype(SZ_DTYPES[sz])
+
+
+# --------------------------------------------------------------------------
+# Dequantization ([P5] Step 4)
+# --------------------------------------------------------------------------
+def dequant_f32(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g: int) -> np.ndarray:
+    """w_hat = fl32((q - zp) * scale) as float32 [N, K]."""
+    q = unpack_nibbles(packed).astype(np.int32)
+    n, k = q.shape
+    zp = np.asarray(zeros).astype(np.int32)
+    s = np.asarray(scales).astype(F32)
+    d = (q.reshape(n, k // g, g) - zp[..., None]).astype(F32)
+    return (d * s[..., None]).reshape(n, k)
+
+
+def dequant(packed, scales, zeros, g: int, out: str) -> np.ndarray:
+    """dequant_f32 rounded (nearest-even) to the output dtype: "f32" gives
+    float32, "f16" float16, "bf16" bf16 bits."""
+    w = dequant_f32(packed, scales, zeros, g)
+    if out == "f32":
+        return w
+    if out == "f16":
+        return w.astype(F16)
+    if out == "bf16":
+        return to_bf16(w)
+    raise ValueError(out)
+
+
+def dequant_f64(packed, scales, zeros, g: int, rows=None) -> np.ndarray:
+    """Exact (q - zp) * scale in float64 for the matmul references."""
+    p = np.asarray(packed) if rows is None else np.asarray(packed)[rows]
+    s = np.asarray(scales) if rows is None else np.asarray(scales)[rows]
+    z = np.asarray(zeros) if rows is None else np.asarray(zeros)[rows]
+    q = unpack_nibbles(p).astype(np.float64)
+    n, k = q.shape
+    d = q.reshape(n, k // g, g) - z.astype(np.float64)[..., None]
+    return (d * s.astype(np.float64)[..., None]).reshape(n, k)
+
+
+# --------------------------------------------------------------------------
+# Per-token INT8 activations ([P1] Architecture Overview, Step 3)
+# --------------------------------------------------------------------------
+def act_quant_int8(x32: np.ndarray):
+    """s_a = fl32(max(max_k |x|, 1e-8) / 127); xq = clamp(rint(fl32(x/s_a)), -128, 127).
+
+    The 1e-8 floor is applied before the division, as on the page.
+    Returns (xq int8 [M, K], s_a float32 [M]).
+    """
+    x32 = np.asarray(x32, F32)
+    amax = np.max(np.abs(x32), axis=1)
+    s = np.maximum(amax, F32(1e-8)) / F32(127.0)
+    xq = np.clip(np.rint(x32 / s[:, None]), -128, 127).astype(np.int8)
+    return xq, s.astype(F32)
+
+
+# --------------------------------------------------------------------------
+# Matmul references ([P3] Step 2; [P4] Step 5; [P1] Step 5)
+# --------------------------------------------------------------------------
+def _chunks(n: int, step: int):
+    for i in range(0, n, step):
+        yield slice(i, min(n, i + step))
+
+
+def matmul_w4a16_f64(x32: np.ndarray, packed, scales, zeros, g: int, chunk: int = 2048) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * w_hat[n, k] in float64 (x widened exactly).
+
+    Done chunk by chunk over output rows of W so the fp64 weight never exists
+    whole; the matmul itself is NumPy's (a library primitive).
+    """
+    x64 = np.asarray(x32, F32).astype(np.float64)
+    n = np.asarray(packed).shape[0]
+    y = np.empty((x64.shape[0], n), np.float64)
+    for sl in _chunks(n, chunk):
+        w64 = dequant_f64(packed, scales, zeros, g, rows=sl)
+        y[:, sl] = x64 @ w64.T
+    return y
+
+
+def matmul_w4a8_f64(xq: np.ndarray, s_a: np.ndarray, packed, scales, zeros, g: int,
+                    chunk: int = 2048) -> np.ndarray:
+    """y[m, n] = s_a[m] * sum_k xq[m, k] * w_hat[n, k] in float64."""
+    x64 = np.asarray(xq).astype(np.float64)
+    sa = np.asarray(s_a, F32).astype(np.float64)
+    n = np.asarray(packed).shape[0]
+    y = np.empty((x64.shape[0], n), np.float64)
+    for sl in _chunks(n, chunk):
+        w64 = dequant_f64(packed, scales, zeros, g, rows=sl)
+        y[:, sl] = x64 @ w64.T
+    return y * sa[:, None]
+
+
+# --------------------------------------------------------------------------
+# Comparison metric for matmul outputs
+# --------------------------------------------------------------------------
+def max_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    """max |y - ref| / max |ref|  (infinity-norm relative error)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(y - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return num
+    return num / den

@@ -1,0 +1,425 @@
+"""Checks that pin the oracle to things other than itself.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with what the
+pages or the mathematics fix: values printed on the pages, hand-derived
+worked examples (tests/golden/), closed forms, invariants, library routines
+for special cases, and brute force on tiny inputs.  They are plain functions
+so that tests/test_oracle_mutations.py can run all of them against an oracle
+with a planted mistake and require that at least one fails.
+
+The oracle is reached through the module object ``O`` (never through names
+imported from it) so that a planted mistake is seen by every check.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle.w4_oracle as O
+from tests import brute_force as BF
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+f32 = np.float32
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+# ---------------------------------------------------------------------------
+# Packing
+# ---------------------------------------------------------------------------
+def check_pack_page_vector():
+    """Page vector (GPTQ engine page, 'The tests') under the Step 4 convention."""
+    gv = _golden("pack_vector.json")
+    codes = np.array([gv["codes"]], np.uint8)
+    assert (codes.astype(int) - 8).tolist() == [gv["signed_values"]]
+    packed = O.pack_nibbles(codes)
+    want = [int(h, 16) for h in gv["packed_bytes_hex"]]
+    assert packed.tolist() == [want], (packed.tolist(), want)
+    assert O.unpack_nibbles(packed).tolist() == codes.tolist()
+
+
+def check_pack_exhaustive():
+    """All 256 bytes unpack to (low, high) and pack back exactly."""
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = O.unpack_nibbles(b)
+    assert q.shape == (1, 512)
+    assert np.array_equal(q[0, 0::2], np.arange(256) % 16)
+    assert np.array_equal(q[0, 1::2], np.arange(256) // 16)
+    assert np.array_equal(O.pack_nibbles(q), b)
+
+
+# ---------------------------------------------------------------------------
+# Worked example: scale, zero-point, ties (tests/golden/worked_example_g32.json)
+# ---------------------------------------------------------------------------
+def worked_example_group():
+    """The 32 values of the worked example, interleaved, plus expected codes."""
+    u = 2.0 ** -6
+    lv = [((j - 5) * u, j) for j in range(16)]
+    mid_codes = _golden("worked_example_g32.json")["expected"]["midpoint_codes"]
+    md = [((j - 4.5) * u, mid_codes[j]) for j in range(15)]
+    order = [lv[15], md[0], lv[0], md[14]]
+    rest_l = lv[1:15]
+    rest_m = md[1:14]
+    for i in range(max(len(rest_l), len(rest_m))):
+        if i < len(rest_l):
+            order.append(rest_l[i])
+        if i < len(rest_m):
+            order.append(rest_m[i])
+    order.append(lv[7])
+    assert len(order) == 32
+    vals = np.array([v for v, _ in order], np.float32)
+    codes = np.array([c for _, c in order], np.uint8)
+    return vals, codes
+
+
+def check_worked_example():
+    gv = _golden("worked_example_g32.json")
+    vals, codes = worked_example_group()
+    u = 2.0 ** -6
+    for sz in ("f32", "f16"):
+        for kind in ("f32", "bf16"):
+            w = vals.reshape(1, 32) if kind == "f32" else O.to_bf16(vals).reshape(1, 32)
+            p, s, z = O.quantize_pack_int4(w, kind, 32, sz)
+            assert float(s[0, 0]) == u, (sz, kind, float(s[0, 0]))
+            assert float(z[0, 0]) == gv["expected"]["zero_point"]
+            assert np.array_equal(O.unpack_nibbles(p)[0], codes), (O.unpack_nibbles(p)[0], codes)
+            wh = O.dequant_f32(p, s, z, 32)[0]
+            lv = np.array([abs(v / u - round(v / u)) < 1e-12 for v in vals.astype(float)])
+            assert np.array_equal(wh[lv], vals[lv])  # levels reproduce exactly
+            assert np.array_equal(wh, ((codes.astype(np.float64) - 5) * u).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Degenerate, clamped and extreme groups
+# ---------------------------------------------------------------------------
+def check_degenerate_groups():
+    w = np.zeros((2, 64), np.float32)
+    w[1, :32] = 3.0
+    w[1, 32:] = -3.0
+    for sz in ("f32", "f16"):
+        p, s, z = O.quantize_pack_int4(w, "f32", 32, sz)
+        q = O.unpack_nibbles(p)
+        assert float(s[0, 0]) == 1.0 and float(z[0, 0]) == 0.0 and not q[0, :32].any()
+        assert float(s[1, 0]) == 1.0 and float(z[1, 0]) == 0.0 and (q[1, :32] == 3).all()
+        assert float(s[1, 1]) == 1.0 and float(z[1, 1]) == 3.0 and (q[1, 32:] == 0).all()
+        wh = O.dequant_f32(p, s, z, 32)
+        assert np.array_equal(wh[:2], w[:2])
+        # the stored zero-point of a zero-range group is +0.0, never -0.0
+        assert not np.signbit(np.asarray(z, np.float32)).any()
+
+
+def check_tiny_range_scales():
+    """fp16 subnormal scales are kept; a scale that underflows fp16 becomes 1."""
+    g = 32
+    w = np.zeros((2, g), np.float32)
+    w[0] = (np.arange(g) % 16).astype(np.float32) * np.float32(2.0 ** -20)  # range 15*2^-20
+    w[1] = (np.arange(g) % 16).astype(np.float32) * np.float32(2.0 ** -27)  # range 15*2^-27
+    p, s, z = O.quantize_pack_int4(w, "f32", g, "f16")
+    assert float(s[0, 0]) == 2.0 ** -20  # fp16 subnormal, exact
+    assert float(z[0, 0]) == 0.0
+    assert np.array_equal(O.unpack_nibbles(p)[0], (np.arange(g) % 16).astype(np.uint8))
+    assert float(s[1, 0]) == 1.0 and float(z[1, 0]) == 0.0
+    assert not O.unpack_nibbles(p)[1].any()
+    # with fp32 scales nothing underflows
+    p2, s2, z2 = O.quantize_pack_int4(w, "f32", g, "f32")
+    assert float(s2[1, 0]) == 2.0 ** -27
+    assert np.array_equal(O.unpack_nibbles(p2)[1], (np.arange(g) % 16).astype(np.uint8))
+
+
+def check_clamped_zero_point():
+    """All-positive group: zp clamps to 0 and the top codes saturate at 15;
+    all-negative group: zp clamps to 15 and the low codes saturate at 0."""
+    g = 32
+    w = np.zeros((2, g), np.float32)
+    w[0] = np.linspace(1.0, 2.5, g, dtype=np.float32)
+    w[1] = -np.linspace(1.0, 2.5, g, dtype=np.float32)
+    for sz in ("f32", "f16"):
+        p, s, z = O.quantize_pack_int4(w, "f32", g, sz)
+        q = O.unpack_nibbles(p)
+        assert float(z[0, 0]) == 0.0 and q[0].max() == 15 and q[0, -1] == 15
+        assert float(z[1, 0]) == 15.0 and q[1].min() == 0 and q[1, -1] == 0
+        sv = float(s[0, 0])
+        assert abs(sv - 0.1) < 1e-3
+        # codes are the clamped nearest levels
+        want = np.clip(np.rint(w[0].astype(np.float64) / sv), 0, 15)
+        assert np.array_equal(q[0], want.astype(np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# Group axis, per-group scales: each group is the per-tensor quantizer of
+# "From Scratch: Building a GPTQ INT4 Quantizer in Pure Python" (Step 2)
+# applied to that run of g columns.
+# ---------------------------------------------------------------------------
+def check_groups_are_row_runs():
+    rng = np.random.default_rng(11)
+    n, k, g = 3, 96, 32
+    w = rng.normal(0, 0.02, (n, k)).astype(np.float32)
+    w[1, 40] = 0.5  # an outlier confined to group (1, 1)
+    p, s, z = O.quantize_pack_int4(w, "f32", g, "f16")
+    q = O.unpack_nibbles(p)
+    for r in range(n):
+        for gi in range(k // g):
+            vals = [f32(v) for v in w[r, gi * g:(gi + 1) * g]]
+            st, zp, codes = BF.quantize_group(vals, "f16")
+            assert float(s[r, gi]) == float(st) and float(z[r, gi]) == zp
+            assert q[r, gi * g:(gi + 1) * g].tolist() == codes
+    big = float(s[1, 1])
+    assert all(float(s[r, gi]) < big / 4 for r in range(n) for gi in range(3) if (r, gi) != (1, 1))
+
+
+# ---------------------------------------------------------------------------
+# Brute force on tiny random inputs: bit-exact agreement
+# ---------------------------------------------------------------------------
+def check_brute_force_quantize():
+    rng = np.random.default_rng(5)
+    for (n, k, g) in ((4, 64, 32), (3, 64, 64), (8, 32, 32)):
+        w = rng.normal(0, 0.05, (n, k)).astype(np.float32)
+        w[0, 3] = 0.5
+        w[-1, :g] = np.abs(w[-1, :g])  # an all-positive group (clamped zp)
+        for sz in ("f32", "f16"):
+            for kind in ("f32", "bf16"):
+                src = w if kind == "f32" else O.to_bf16(w)
+                w32 = w if kind == "f32" else O.widen_bf16(src)
+                p, s, z = O.quantize_pack_int4(src, kind, g, sz)
+                bp, bs, bz = BF.quantize_pack(w32, g, sz)
+                assert np.array_equal(p, bp), (n, k, g, sz, kind)
+                assert np.array_equal(s.view(np.uint8), bs.view(np.uint8))
+                assert np.array_equal(z.view(np.uint8), bz.view(np.uint8))
+                d = O.dequant_f32(p, s, z, g)
+                assert np.array_equal(d.view(np.uint32), BF.dequant(p, s, z, g).view(np.uint32))
+
+
+def check_brute_force_act_quant():
+    rng = np.random.default_rng(6)
+    x = rng.normal(0, 1, (5, 48)).astype(np.float32)
+    x[1] *= 20.0
+    x[2] = 0.0
+    x[3] = x[3] * np.float32(1e-12)
+    xq, sa = O.act_quant_int8(x)
+    bq, bs = BF.act_quant(x)
+    assert np.array_equal(xq, bq) and np.array_equal(sa.view(np.uint32), bs.view(np.uint32))
+
+
+def check_brute_force_matmul():
+    """fp64 references agree with correctly rounded dot products (fsum)."""
+    rng = np.random.default_rng(7)
+    n, k, g, m = 6, 64, 32, 3
+    w = rng.normal(0, 0.02, (n, k)).astype(np.float32)
+    x = rng.normal(0, 1, (m, k)).astype(np.float32)
+    p, s, z = O.quantize_pack_int4(w, "f32", g, "f32")
+    wh = BF.dequant(p, s, z, g)  # fl32 values
+    w64 = O.dequant_f64(p, s, z, g)
+    # the fp64 dequant is the exact (q-zp)*s; its fp32 rounding is the fp32 dequant
+    assert np.array_equal(w64.astype(np.float32), wh)
+    y = O.matmul_w4a16_f64(x, p, s, z, g)
+    for i in range(m):
+        for j in range(n):
+            ref = BF.dot_exact(x[i], w64[j])
+            assert abs(y[i, j] - ref) <= 1e-12 * (1 + abs(ref)), (i, j, y[i, j], ref)
+    xq, sa = O.act_quant_int8(x)
+    y8 = O.matmul_w4a8_f64(xq, sa, p, s, z, g)
+    for i in range(m):
+        for j in range(n):
+            ref = float(sa[i]) * BF.dot_exact(xq[i], w64[j])
+            assert abs(y8[i, j] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+# ---------------------------------------------------------------------------
+# Closed forms: exact matmuls with no tolerance
+# ---------------------------------------------------------------------------
+def _integer_weights(rng, n, k, g):
+    """Integers in [0, 15], every group holding both 0 and 15."""
+    w = rng.integers(0, 16, (n, k))
+    for r in range(n):
+        for gi in range(k // g):
+            a, b = rng.choice(g, 2, replace=False)
+            w[r, gi * g + a] = 0
+            w[r, gi * g + b] = 15
+    return w
+
+
+def check_exact_integer_matmul():
+    """W in [0,15] with 0 and 15 in each group quantizes to s=1, zp=0, q=W;
+    with integer x the fp64 product equals the integer product exactly."""
+    rng = np.random.default_rng(8)
+    for (n, k, g, m, sz) in ((64, 64, 32, 3, "f16"), (24, 256, 32, 5, "f32"), (24, 256, 32, 5, "f16")):
+        wi = _integer_weights(rng, n, k, g)
+        xi = rng.integers(-8, 9, (m, k))
+        p, s, z = O.quantize_pack_int4(wi.astype(np.float32), "f32", g, sz)
+        assert (np.asarray(s, np.float32) == 1).all() and (np.asarray(z, np.float32) == 0).all()
+        assert np.array_equal(O.unpack_nibbles(p), wi.astype(np.uint8))
+        y = O.matmul_w4a16_f64(xi.astype(np.float32), p, s, z, g)
+        assert y.shape == (m, n)
+        assert np.array_equal(y, (xi @ wi.T).astype(np.float64))
+
+
+def check_codes_nearest_stored_level():
+    """Every code is a nearest level of the grid (q - zp) * s_stored, q in
+    0..15: neither neighbouring code would reconstruct w more closely (round
+    to nearest on the stored grid; exact ties may go either way)."""
+    rng = np.random.default_rng(14)
+    n, k, g = 64, 512, 128
+    w = rng.normal(0, 0.02, (n, k)).astype(np.float32)
+    for sz in ("f16", "f32"):
+        p, s, z = O.quantize_pack_int4(w, "f32", g, sz)
+        q = O.unpack_nibbles(p).astype(np.int64).reshape(n, k // g, g)
+        sv = np.asarray(s, np.float64)[..., None]
+        zv = np.asarray(z, np.float64)[..., None]
+        wv = w.astype(np.float64).reshape(n, k // g, g)
+        err = np.abs(wv - (q - zv) * sv)
+        for d in (-1, 1):
+            qn = q + d
+            ok = (qn >= 0) & (qn <= 15)
+            errn = np.abs(wv - (qn - zv) * sv)
+            # allow only rounding-level differences (fp32 division of w by s)
+            assert (err[ok] <= errn[ok] + sv.repeat(g, 2)[ok] * 2.0 ** -20).all(), sz
+
+
+def check_exact_scaled_matmul():
+    """Per-group power-of-two scales and zero-points, exactly representable:
+    W[r, group] = 2^e * (Q - Z).  Quantization must return (2^e, Z, Q) for
+    every (row, group), and the matmul must equal the exact rational result."""
+    rng = np.random.default_rng(9)
+    n, k, g, m = 6, 128, 32, 3
+    ng = k // g
+    Q = _integer_weights(rng, n, k, g)
+    E = rng.integers(-9, -3, (n, ng))
+    Z = rng.integers(0, 16, (n, ng))
+    w = np.zeros((n, k), np.float64)
+    for r in range(n):
+        for gi in range(ng):
+            w[r, gi * g:(gi + 1) * g] = (2.0 ** E[r, gi]) * (Q[r, gi * g:(gi + 1) * g] - Z[r, gi])
+    w32 = w.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), w)
+    xi = rng.integers(-127, 128, (m, k))
+    for sz in ("f32", "f16"):
+        p, s, z = O.quantize_pack_int4(w32, "f32", g, sz)
+        assert np.array_equal(np.asarray(s, np.float64), 2.0 ** E)
+        assert np.array_equal(np.asarray(z, np.float64), Z.astype(np.float64))
+        assert np.array_equal(O.unpack_nibbles(p), Q.astype(np.uint8))
+        assert np.array_equal(O.dequant_f32(p, s, z, g), w32)
+        y = O.matmul_w4a16_f64(xi.astype(np.float32), p, s, z, g)
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(int(xi[i, c])) * Fraction(float(w[j, c])) for c in range(k))
+                assert y[i, j] == float(exact)
+        # W4A8 with a non-unit activation scale: x = 2^-3 * xi, amax = 127/8
+        xs = (xi.astype(np.float64) / 8.0)
+        xs[:, 0] = 127.0 / 8.0
+        xq, sa = O.act_quant_int8(xs.astype(np.float32))
+        assert (sa == np.float32(0.125)).all()
+        assert np.array_equal(xq.astype(np.int64), (xs * 8).astype(np.int64))
+        y8 = O.matmul_w4a8_f64(xq, sa, p, s, z, g)
+        assert np.array_equal(y8, xs @ w.T)
+
+
+# ---------------------------------------------------------------------------
+# Activation quantization closed forms
+# ("Hands-on Build Guide: Group-wise INT4 ...", Step 3)
+# ---------------------------------------------------------------------------
+def check_act_quant_closed_forms():
+    k = 64
+    x = np.zeros((4, k), np.float32)
+    x[0] = np.arange(-32, 32)
+    x[0, 5] = 127.0                      # amax 127 -> s = 1, xq = x
+    x[1] = 0.0                           # all-zero token: s = fl32(1e-8)/127
+    x[2] = (np.arange(k) % 9 - 4 + 0.5) * 0.25  # ties: x/s = j + 0.5 with s = 0.25
+    x[2, 0] = 31.75                      # amax 31.75 -> s = 0.25
+    x[3] = -x[0]
+    xq, sa = O.act_quant_int8(x)
+    assert sa[0] == 1.0 and np.array_equal(xq[0].astype(np.float32), x[0])
+    assert sa[1] == np.float32(np.float32(1e-8) / np.float32(127.0)) and not xq[1].any()
+    assert sa[2] == 0.25
+    t = x[2, 1:].astype(np.float64) / 0.25
+    # every t is an exact .5 tie: half-even picks the even neighbour
+    want = np.array([(math.floor(v) if math.floor(v) % 2 == 0 else math.floor(v) + 1) for v in t])
+    assert np.array_equal(xq[2, 1:].astype(np.int64), want)
+    assert xq[2, 0] == 127
+    assert sa[3] == 1.0 and np.array_equal(xq[3].astype(np.float32), x[3])
+    assert xq.min() >= -127
+
+
+def check_act_quant_invariants():
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 1, (16, 512)).astype(np.float32)
+    x[:, rng.choice(512, 26, replace=False)] *= 20
+    xq, sa = O.act_quant_int8(x)
+    assert xq.min() >= -127 and xq.max() <= 127
+    assert (np.abs(xq).max(axis=1) == 127).all()
+    err = np.abs(x.astype(np.float64) - xq.astype(np.float64) * sa[:, None].astype(np.float64))
+    assert (err <= sa[:, None] * 0.5 * (1 + 2.0 ** -16)).all()
+
+
+# ---------------------------------------------------------------------------
+# Invariants on a realistic matrix
+# ---------------------------------------------------------------------------
+def quant_invariants(w32: np.ndarray, g: int, sz: str, mse_band=None):
+    """zp in [0, 15]; |w - w_hat| <= (s/2)(1 + slack) wherever the zero-point
+    was not clamped; MSE close to s^2/12.  Returns (max ratio, count above s/2)."""
+    src = w32
+    p, s, z = O.quantize_pack_int4(src, "f32", g, sz)
+    zf = np.asarray(z, np.float32)
+    assert (zf >= 0).all() and (zf <= 15).all() and (zf == np.rint(zf)).all()
+    wh = O.dequant_f64(p, s, z, g)
+    n, k = w32.shape
+    sv = np.asarray(s, np.float64)
+    err = np.abs(w32.astype(np.float64) - wh).reshape(n, k // g, g)
+    mn = w32.reshape(n, k // g, g).min(axis=2)
+    raw = np.rint(-mn.astype(np.float32) / np.asarray(s, np.float32))
+    free = (raw >= 0) & (raw <= 15)
+    slack = 2.0 ** -6 if sz == "f16" else 2.0 ** -16
+    ratio = err.max(axis=2) / (sv / 2)
+    assert (ratio[free] <= 1 + slack).all(), float(ratio[free].max())
+    above = int((err > (sv / 2)[..., None]).sum())
+    if mse_band is not None:
+        mse_ratio = float((err ** 2).mean() / (sv ** 2 / 12).mean())
+        assert mse_band[0] < mse_ratio < mse_band[1], mse_ratio
+    return float(ratio[free].max()), above
+
+
+def check_invariants_small_config():
+    """256x256 fp32 single layer, g=32, fp32 scales (the first workload)."""
+    from workloads import weight
+    w = weight("W1").as_f32()
+    quant_invariants(w, 32, "f32", mse_band=(0.95, 1.05))
+    quant_invariants(w, 32, "f16", mse_band=(0.95, 1.05))
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding of the oracle against the library routine (torch)
+# ---------------------------------------------------------------------------
+def check_bf16_rounding_vs_torch():
+    import torch
+    rng = np.random.default_rng(13)
+    a = rng.normal(0, 1, 4096).astype(np.float32)
+    # exact ties: low 16 bits = 0x8000 with even and odd kept parts
+    ties = (np.arange(64, dtype=np.uint32) << 16 | 0x3F800000 | 0x8000).view(np.float32)
+    a = np.concatenate([a, ties, -ties, np.float32([0.0, -0.0, 1e-40, 3.0e38])])
+    ours = O.to_bf16(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(O.widen_bf16(ours), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def check_max_rel_err():
+    r = np.array([[1.0, -4.0], [2.0, 0.5]])
+    y = r + np.array([[0.0, 0.04], [-0.02, 0.0]])
+    assert abs(O.max_rel_err(y, r) - 0.01) < 1e-15
+
+
+ALL_CHECKS = [
+    check_pack_page_vector, check_pack_exhaustive, check_worked_example,
+    check_degenerate_groups, check_tiny_range_scales, check_clamped_zero_point,
+    check_groups_are_row_runs, check_brute_force_quantize, check_brute_force_act_quant,
+    check_brute_force_matmul, check_exact_integer_matmul, check_codes_nearest_stored_level,
+    check_exact_scaled_matmul,
+    check_act_quant_closed_forms, check_act_quant_invariants, check_invariants_small_config,
+    check_bf16_rounding_vs_torch, check_max_rel_err,
+]

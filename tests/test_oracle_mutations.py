@@ -1,0 +1,185 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutation replaces one oracle function (on the CPU, via monkeypatch) with
+a plausible wrong version: a dropped term, a wrong sign, a wrong rounding, a
+transposed operand, the other nibble order.  The pin suite must then fail at
+least one check.  This is evidence that the pins constrain the oracle, not a
+test of the GPU path.
+"""
+import numpy as np
+import pytest
+
+import oracle.w4_oracle as O
+from tests import oracle_pins as P
+
+F32 = np.float32
+_orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
+
+
+def _pack_high_even(q):
+    q = np.asarray(q, np.uint8)
+    return ((q[..., 0::2] << np.uint8(4)) | q[..., 1::2]).astype(np.uint8)
+
+
+def _unpack_high_even(p):
+    p = np.asarray(p, np.uint8)
+    q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    q[..., 0::2] = p >> np.uint8(4)
+    q[..., 1::2] = p & np.uint8(0x0F)
+    return q
+
+
+def _unpack_swapped_only(p):
+    return _unpack_high_even(p)
+
+
+def _codes_round_half_up(w32, s_st, zp, g):
+    wg = O.split_groups(w32, g)
+    t = wg / s_st.astype(F32)[..., None] + zp.astype(F32)[..., None]
+    return np.clip(np.floor(t + F32(0.5)), 0, 15).astype(np.uint8).reshape(w32.shape)
+
+
+def _codes_round_then_shift(w32, s_st, zp, g):
+    wg = O.split_groups(w32, g)
+    t = np.rint(wg / s_st.astype(F32)[..., None]) + zp.astype(F32)[..., None]
+    return np.clip(t, 0, 15).astype(np.uint8).reshape(w32.shape)
+
+
+def _codes_with_unrounded_scale_factory():
+    # quantize with the fp32 scale although the fp16 one is stored
+    def scale_zero(mn, mx, sz):
+        sd = O.SZ_DTYPES[sz]
+        s32 = (mx.astype(F32) - mn.astype(F32)) / F32(15.0)
+        s32 = np.where(s32 == 0, F32(1.0), s32)
+        zp = np.clip(np.rint(-mn.astype(F32) / s32), 0, 15).astype(np.int32)
+        _state["s32"] = s32
+        return s32.astype(sd), zp
+
+    def quantize_codes(w32, s_st, zp, g):
+        return _orig["quantize_codes"](w32, _state["s32"], zp, g)
+
+    return scale_zero, quantize_codes
+
+
+_state = {}
+
+
+def _scale_zero_sign_flip(mn, mx, sz):
+    s_st, zp = _orig["scale_zero"](mn, mx, sz)
+    s = s_st.astype(F32)
+    return s_st, np.clip(np.rint(mn.astype(F32) / s), 0, 15).astype(np.int32)
+
+
+def _scale_zero_div16(mn, mx, sz):
+    sd = O.SZ_DTYPES[sz]
+    s_st = ((mx - mn) / F32(16.0)).astype(sd)
+    s_st = np.where(s_st == 0, sd(1.0), s_st).astype(sd)
+    zp = np.clip(np.rint(-mn / s_st.astype(F32)), 0, 15).astype(np.int32)
+    return s_st, zp
+
+
+def _scale_zero_no_guard(mn, mx, sz):
+    sd = O.SZ_DTYPES[sz]
+    with np.errstate(all="ignore"):
+        s_st = ((mx - mn) / F32(15.0)).astype(sd)
+        zp = np.clip(np.nan_to_num(np.rint(-mn / s_st.astype(F32))), 0, 15).astype(np.int32)
+    return s_st, zp
+
+
+def _scale_zero_guard_before_rounding(mn, mx, sz):
+    sd = O.SZ_DTYPES[sz]
+    s32 = (mx - mn) / F32(15.0)
+    s32 = np.where(s32 == 0, F32(1.0), s32)
+    s_st = s32.astype(sd)
+    with np.errstate(all="ignore"):
+        zp = np.clip(np.nan_to_num(np.rint(-mn / s_st.astype(F32))), 0, 15).astype(np.int32)
+    return s_st, zp
+
+
+def _dequant_plus_zp(packed, scales, zeros, g):
+    q = O.unpack_nibbles(packed).astype(np.int32)
+    n, k = q.shape
+    d = (q.reshape(n, k // g, g) + np.asarray(zeros).astype(np.int32)[..., None]).astype(F32)
+    return (d * np.asarray(scales).astype(F32)[..., None]).reshape(n, k)
+
+
+def _dequant64_plus_zp(packed, scales, zeros, g, rows=None):
+    return _dequant_plus_zp(packed if rows is None else packed[rows],
+                            scales if rows is None else scales[rows],
+                            zeros if rows is None else zeros[rows], g).astype(np.float64)
+
+
+def _split_strided(w32, g):
+    n, k = w32.shape
+    return w32.reshape(n, g, k // g).transpose(0, 2, 1)
+
+
+def _matmul_untransposed(x32, packed, scales, zeros, g, chunk=2048):
+    w64 = O.dequant_f64(packed, scales, zeros, g)
+    return np.asarray(x32, F32).astype(np.float64) @ w64
+
+
+def _act_clip_after(x32):
+    amax = np.max(np.abs(x32), axis=1)
+    s = np.maximum(amax / F32(127.0), F32(1e-8)).astype(F32)
+    xq = np.clip(np.rint(x32 / s[:, None]), -128, 127).astype(np.int8)
+    return xq, s
+
+
+def _act_div128(x32):
+    amax = np.max(np.abs(x32), axis=1)
+    s = (np.maximum(amax, F32(1e-8)) / F32(128.0)).astype(F32)
+    xq = np.clip(np.rint(x32 / s[:, None]), -128, 127).astype(np.int8)
+    return xq, s
+
+
+def _w4a8_no_act_scale(xq, s_a, packed, scales, zeros, g, chunk=2048):
+    return _orig["matmul_w4a8_f64"](xq, np.ones_like(s_a), packed, scales, zeros, g, chunk)
+
+
+def _to_bf16_truncate(a):
+    return (np.ascontiguousarray(a, F32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _dequant64_wrong_group(packed, scales, zeros, g, rows=None):
+    # scale/zero of the next group (a shifted index)
+    s = np.roll(np.asarray(scales), 1, axis=1)
+    z = np.roll(np.asarray(zeros), 1, axis=1)
+    return _orig["dequant_f64"](packed, s, z, g, rows)
+
+
+_uq_sz, _uq_codes = _codes_with_unrounded_scale_factory()
+
+MUTATIONS = {
+    "pack_high_nibble_even": {"pack_nibbles": _pack_high_even, "unpack_nibbles": _unpack_high_even},
+    "unpack_swapped_only": {"unpack_nibbles": _unpack_swapped_only},
+    "round_half_up": {"quantize_codes": _codes_round_half_up},
+    "round_before_zero_point": {"quantize_codes": _codes_round_then_shift},
+    "zero_point_sign": {"scale_zero": _scale_zero_sign_flip},
+    "scale_over_16": {"scale_zero": _scale_zero_div16},
+    "no_zero_scale_guard": {"scale_zero": _scale_zero_no_guard},
+    "guard_before_fp16_rounding": {"scale_zero": _scale_zero_guard_before_rounding},
+    "quantize_with_unrounded_scale": {"scale_zero": _uq_sz, "quantize_codes": _uq_codes},
+    "dequant_adds_zero_point": {"dequant_f32": _dequant_plus_zp, "dequant_f64": _dequant64_plus_zp},
+    "groups_strided_not_runs": {"split_groups": _split_strided},
+    "matmul_untransposed": {"matmul_w4a16_f64": _matmul_untransposed},
+    "act_floor_after_divide": {"act_quant_int8": _act_clip_after},
+    "act_scale_over_128": {"act_quant_int8": _act_div128},
+    "w4a8_drops_act_scale": {"matmul_w4a8_f64": _w4a8_no_act_scale},
+    "bf16_truncates": {"to_bf16": _to_bf16_truncate},
+    "dequant_shifted_group_index": {"dequant_f64": _dequant64_wrong_group},
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    for attr, fn in MUTATIONS[name].items():
+        monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for check in P.ALL_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except Exception as exc:  # AssertionError or a shape error: caught either way
+            failed.append((check.__name__, type(exc).__name__))
+    assert failed, f"planted mistake {name!r} passed every pin"
