@@ -1,0 +1,190 @@
+"""ctypes binding of libw4.so.
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in include/w4.h.  PyTorch supplies device memory and the
+current stream.  There is no CPU fallback: if the library is missing or a
+tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("W4_LIB", os.path.join(HERE, "libw4.so"))
+
+W4_F32, W4_F16, W4_BF16 = 0, 1, 2
+W4_OK, W4_EINVAL, W4_EUNSUPPORTED, W4_EHIP = 0, -1, -2, -3
+
+_DT = {torch.float32: W4_F32, torch.float16: W4_F16, torch.bfloat16: W4_BF16}
+
+# (name, restype, argtypes) of every exported function, in header order.
+_VP, _I, _I64, _I32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32
+SIGNATURES = [
+    ("quantize_pack_int4", _I, [_VP, _I, _I64, _I64, _I32, _VP, _VP, _VP, _I, _VP]),
+    ("dequant_int4", _I, [_VP, _VP, _VP, _I, _I64, _I64, _I32, _VP, _I, _VP]),
+    ("quantize_act_int8", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP]),
+    ("w4a16_matmul", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
+    ("w4a8_matmul", _I, [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
+    ("w4_status_string", ctypes.c_char_p, [_I]),
+    ("w4_last_error", ctypes.c_char_p, []),
+    ("w4_version", ctypes.c_char_p, []),
+]
+
+_lib = None
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libw4.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"libw4.so not found at {p}: build it first "
+            "(python -m dequant_gemm_quantize_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != W4_OK:
+        lib = load()
+        msg = lib.w4_last_error().decode() or lib.w4_status_string(status).decode()
+        raise W4Error(status, msg)
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _gpu(*ts: torch.Tensor) -> torch.device:
+    dev = None
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libw4 runs on the GPU only: every tensor must be on a cuda (HIP) device")
+        if not t.is_contiguous():
+            raise ValueError("libw4 expects contiguous row-major tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+# ---------------------------------------------------------------------------
+# Public wrappers (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def quantize_pack_int4(w: torch.Tensor, group_size: int, sz_dtype: torch.dtype = torch.float16,
+                       out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """W [N, K] (fp32 or bf16) -> (packed uint8 [N, K/2], scales [N, K/g], zeros [N, K/g])."""
+    lib = load()
+    n, k = w.shape
+    dev = _gpu(w)
+    if out is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, k // group_size), dtype=sz_dtype, device=dev)
+        zeros = torch.empty((n, k // group_size), dtype=sz_dtype, device=dev)
+    else:
+        packed, scales, zeros = out
+        _gpu(packed, scales, zeros)
+    _check(lib.quantize_pack_int4(_ptr(w), _dtype_code(w.dtype), n, k, group_size, _ptr(packed),
+                                  _ptr(scales), _ptr(zeros), _dtype_code(scales.dtype), _stream(dev)))
+    return packed, scales, zeros
+
+
+def dequant_int4(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, group_size: int,
+                 out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """(packed, scales, zeros) -> dequantized W [N, K] in out_dtype."""
+    lib = load()
+    n, half = packed.shape
+    k = 2 * half
+    dev = _gpu(packed, scales, zeros)
+    if scales.dtype != zeros.dtype:
+        raise ValueError("scales and zeros must share a dtype")
+    w = torch.empty((n, k), dtype=out_dtype, device=dev) if out is None else out
+    _gpu(w)
+    _check(lib.dequant_int4(_ptr(packed), _ptr(scales), _ptr(zeros), _dtype_code(scales.dtype), n, k,
+                            group_size, _ptr(w), _dtype_code(w.dtype), _stream(dev)))
+    return w
+
+
+def quantize_act_int8(x: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """x [M, K] (fp32 or bf16) -> (xq int8 [M, K], x_scale float32 [M])."""
+    lib = load()
+    m, k = x.shape
+    dev = _gpu(x)
+    if out is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xs = torch.empty((m,), dtype=torch.float32, device=dev)
+    else:
+        xq, xs = out
+        _gpu(xq, xs)
+    _check(lib.quantize_act_int8(_ptr(x), _dtype_code(x.dtype), m, k, _ptr(xq), _ptr(xs), _stream(dev)))
+    return xq, xs
+
+
+def w4a16_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                 group_size: int, out_dtype: Optional[torch.dtype] = None,
+                 out: Optional[torch.Tensor] = None):
+    """y [M, N] = x [M, K] . dequant(W)^T; out_dtype defaults to x's dtype."""
+    lib = load()
+    m, k = x.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k:
+        raise ValueError(f"packed has {packed.shape[1] * 2} columns of codes, x has K={k}")
+    dev = _gpu(x, packed, scales, zeros)
+    y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=dev) if out is None else out
+    _gpu(y)
+    _check(lib.w4a16_matmul(_ptr(x), _dtype_code(x.dtype), m, k, _ptr(packed), _ptr(scales),
+                            _ptr(zeros), _dtype_code(scales.dtype), n, group_size, _ptr(y),
+                            _dtype_code(y.dtype), _stream(dev)))
+    return y
+
+
+def w4a8_matmul(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                zeros: torch.Tensor, group_size: int, out_dtype: torch.dtype = torch.bfloat16,
+                out: Optional[torch.Tensor] = None):
+    """y [M, N] = x_scale[m] * (xq [M, K] . dequant(W)^T)."""
+    lib = load()
+    m, k = xq.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k:
+        raise ValueError(f"packed has {packed.shape[1] * 2} columns of codes, xq has K={k}")
+    dev = _gpu(xq, x_scale, packed, scales, zeros)
+    y = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
+    _gpu(y)
+    _check(lib.w4a8_matmul(_ptr(xq), _ptr(x_scale), m, k, _ptr(packed), _ptr(scales), _ptr(zeros),
+                           _dtype_code(scales.dtype), n, group_size, _ptr(y), _dtype_code(y.dtype),
+                           _stream(dev)))
+    return y
+
+
+def version() -> str:
+    return load().w4_version().decode()

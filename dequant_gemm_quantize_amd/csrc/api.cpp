@@ -1,0 +1,180 @@
+// C ABI of libw4: argument validation, kernel selection, error reporting.
+// Every check happens before any HIP call, so an invalid request enqueues
+// nothing.  No exception leaves this file.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "w4_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return W4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(W4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks of the weight-side arguments (shape, group, scale dtype).
+int check_weights(const char* fn, int64_t n, int64_t k, int32_t g, int sz_dtype) {
+  if (n < 0) return fail(W4_EINVAL, "%s: n = %lld < 0", fn, (long long)n);
+  if (k <= 0) return fail(W4_EINVAL, "%s: k = %lld must be > 0", fn, (long long)k);
+  if (g <= 0 || g % 32 != 0)
+    return fail(W4_EINVAL, "%s: group_size = %d must be a positive multiple of 32", fn, g);
+  if (k % g != 0)
+    return fail(W4_EINVAL, "%s: k = %lld is not a multiple of group_size = %d", fn, (long long)k, g);
+  if (sz_dtype != W4_F32 && sz_dtype != W4_F16)
+    return fail(W4_EINVAL, "%s: scale dtype %d must be W4_F32 or W4_F16", fn, sz_dtype);
+  // keep flat element counts far from int64 overflow
+  if (n > ((int64_t)1 << 40) / k)
+    return fail(W4_EINVAL, "%s: n * k = %lld * %lld is too large", fn, (long long)n, (long long)k);
+  return W4_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p) {
+  if (p == nullptr) return fail(W4_EINVAL, "%s: %s is NULL", fn, name);
+  if (!aligned16(p)) return fail(W4_EINVAL, "%s: %s is not 16-byte aligned", fn, name);
+  return W4_OK;
+}
+
+#define W4_TRY(expr)              \
+  do {                            \
+    const int rc_ = (expr);       \
+    if (rc_ != W4_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK: success";
+    case W4_EINVAL: return "W4_EINVAL: invalid argument";
+    case W4_EUNSUPPORTED: return "W4_EUNSUPPORTED: request not supported by this build";
+    case W4_EHIP: return "W4_EHIP: HIP runtime error";
+    default: return "unknown w4 status";
+  }
+}
+
+const char* w4_last_error(void) { return g_last_error; }
+
+const char* w4_version(void) { return "w4 0.1.0 gfx950"; }
+
+int quantize_pack_int4(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                       uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                       hipStream_t stream) {
+  static const char* fn = "quantize_pack_int4";
+  W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
+  if (w_dtype != W4_F32 && w_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: w dtype %d must be W4_F32 or W4_BF16", fn, w_dtype);
+  if (n == 0) return ok();
+  W4_TRY(check_ptr(fn, "w", w));
+  W4_TRY(check_ptr(fn, "packed", packed));
+  W4_TRY(check_ptr(fn, "scales", scales));
+  W4_TRY(check_ptr(fn, "zeros", zeros));
+  return hip_status(w4::launch_quantize_pack(w, w_dtype, n, k, group_size, packed, scales, zeros,
+                                             sz_dtype, stream),
+                    fn);
+}
+
+int dequant_int4(const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                 int64_t n, int64_t k, int32_t group_size, void* w_out, int out_dtype,
+                 hipStream_t stream) {
+  static const char* fn = "dequant_int4";
+  W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
+  if (out_dtype != W4_F32 && out_dtype != W4_F16 && out_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: out dtype %d must be W4_F32, W4_F16 or W4_BF16", fn, out_dtype);
+  if (n == 0) return ok();
+  W4_TRY(check_ptr(fn, "packed", packed));
+  W4_TRY(check_ptr(fn, "scales", scales));
+  W4_TRY(check_ptr(fn, "zeros", zeros));
+  W4_TRY(check_ptr(fn, "w_out", w_out));
+  return hip_status(
+      w4::launch_dequant(packed, scales, zeros, sz_dtype, n, k, group_size, w_out, out_dtype, stream),
+      fn);
+}
+
+int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* xq,
+                      float* x_scale, hipStream_t stream) {
+  static const char* fn = "quantize_act_int8";
+  if (x_dtype != W4_F32 && x_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: x dtype %d must be W4_F32 or W4_BF16", fn, x_dtype);
+  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
+  if (k <= 0 || k % 8 != 0)
+    return fail(W4_EINVAL, "%s: k = %lld must be a positive multiple of 8", fn, (long long)k);
+  if (m > 0x7fffffffLL) return fail(W4_EINVAL, "%s: m = %lld is too large", fn, (long long)m);
+  if (m > ((int64_t)1 << 40) / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  if (m == 0) return ok();
+  W4_TRY(check_ptr(fn, "x", x));
+  W4_TRY(check_ptr(fn, "xq", xq));
+  if (x_scale == nullptr) return fail(W4_EINVAL, "%s: x_scale is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(x_scale) & 3u) != 0)
+    return fail(W4_EINVAL, "%s: x_scale is not 4-byte aligned", fn);
+  return hip_status(w4::launch_act_quant(x, x_dtype, m, k, xq, x_scale, stream), fn);
+}
+
+int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                 const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                 int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
+  static const char* fn = "w4a16_matmul";
+  W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
+  if (x_dtype != W4_F32 && x_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: x dtype %d must be W4_F32 or W4_BF16", fn, x_dtype);
+  if (y_dtype != W4_F32 && y_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: y dtype %d must be W4_F32 or W4_BF16", fn, y_dtype);
+  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
+  if (m > ((int64_t)1 << 40) / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  if (m == 0 || n == 0) return ok();
+  W4_TRY(check_ptr(fn, "x", x));
+  W4_TRY(check_ptr(fn, "packed", packed));
+  W4_TRY(check_ptr(fn, "scales", scales));
+  W4_TRY(check_ptr(fn, "zeros", zeros));
+  W4_TRY(check_ptr(fn, "y", y));
+  return hip_status(w4::launch_w4a16_generic(x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
+                                             group_size, y, y_dtype, stream),
+                    fn);
+}
+
+int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
+                const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                int64_t n, int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
+  static const char* fn = "w4a8_matmul";
+  W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
+  if (y_dtype != W4_F32 && y_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: y dtype %d must be W4_F32 or W4_BF16", fn, y_dtype);
+  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
+  if (m > ((int64_t)1 << 40) / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  if (m == 0 || n == 0) return ok();
+  W4_TRY(check_ptr(fn, "xq", xq));
+  W4_TRY(check_ptr(fn, "packed", packed));
+  W4_TRY(check_ptr(fn, "scales", scales));
+  W4_TRY(check_ptr(fn, "zeros", zeros));
+  W4_TRY(check_ptr(fn, "y", y));
+  if (x_scale == nullptr) return fail(W4_EINVAL, "%s: x_scale is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(x_scale) & 3u) != 0)
+    return fail(W4_EINVAL, "%s: x_scale is not 4-byte aligned", fn);
+  return hip_status(w4::launch_w4a8_generic(xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n,
+                                            group_size, y, y_dtype, stream),
+                    fn);
+}
+
+}  // extern "C"

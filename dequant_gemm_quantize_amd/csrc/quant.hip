@@ -1,0 +1,320 @@
+// Quantize + pack, dequantize, and per-token INT8 activation kernels.
+//
+// All three are memory-bound streaming kernels.  Their float32 arithmetic is
+// the definition itself -- IEEE division (correctly rounded), rint with ties
+// to even, round-to-nearest-even narrowing -- so the outputs are bit-exact.
+// Contraction into FMA is switched off in this file: nothing here may fuse.
+#include "w4_common.h"
+#include "w4_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace w4 {
+
+// ---------------------------------------------------------------------------
+// Element loads: 8 consecutive elements of chunk c (element index 8c..8c+7).
+// ---------------------------------------------------------------------------
+template <typename TIn> struct Load8;
+template <> struct Load8<float> {  // fp32 input: two 16-byte loads
+  __device__ static void run(const void* base, int64_t c, float (&v)[8]) {
+    const f32x4* p = (const f32x4*)base + 2 * c;
+    f32x4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <> struct Load8<__bf16> {  // bf16 input: one 16-byte load, exact widening
+  __device__ static void run(const void* base, int64_t c, float (&v)[8]) {
+    u32x4 a = ((const u32x4*)base)[c];
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  }
+};
+
+// Scale and zero-point of one group from its range ("From-scratch INT4
+// Weight-only Quantizer with Per-group Scales and Zero-points for LLMs",
+// Architecture Overview and Step 6): scale = (max - min)/15 rounded to the
+// storage type, 0 -> 1; zp = clamp(rint(-min/scale), 0, 15) with that scale.
+template <typename TS>
+__device__ __forceinline__ void scale_zero(float mn, float mx, TS& s_store, float& s, int& zp) {
+  float s32 = (mx - mn) / 15.0f;
+  TS st = (TS)s32;
+  if (st == (TS)0.0f) st = (TS)1.0f;
+  s_store = st;
+  s = (float)st;
+  float z = rintf(-mn / s);
+  z = fminf(fmaxf(z, 0.0f), 15.0f);
+  zp = (int)z;
+}
+
+// Code of one weight ("From Scratch: Building a GPTQ INT4 Quantizer in Pure
+// Python", Step 2): clamp(rint(w/scale + zp), 0, 15).
+__device__ __forceinline__ uint32_t code_of(float w, float s, float zpf) {
+  float t = rintf(w / s + zpf);
+  t = fminf(fmaxf(t, 0.0f), 15.0f);
+  return (uint32_t)t;
+}
+
+// Eight codes -> one 32-bit word; element i sits in nibble i, so byte j holds
+// the even column in its low nibble ("Build a GPTQ INT4 Quantization Engine in
+// Python/NumPy", Step 4).
+__device__ __forceinline__ uint32_t pack8(const float (&v)[8], float s, float zpf) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= code_of(v[i], s, zpf) << (4 * i);
+  return word;
+}
+
+// ---------------------------------------------------------------------------
+// Quantize + pack, power-of-two groups of 32..512 elements.
+// The tensor is treated as a flat run of N*K elements: with K % g == 0 a
+// group never crosses a row, and flat group index == row * (K/g) + group.
+// Each lane owns one 8-element chunk; L = g/8 neighbouring lanes share a
+// group and reduce its min/max with xor butterflies.  U chunks per lane are
+// loaded up front (U*16 bytes of bf16 in flight per lane).
+// ---------------------------------------------------------------------------
+template <typename TIn, typename TS, int L, int U>
+__global__ __launch_bounds__(256) void k_quantize_pack_sub(const void* __restrict__ w,
+                                                          int64_t nchunks,
+                                                          uint32_t* __restrict__ packed,
+                                                          TS* __restrict__ scales,
+                                                          TS* __restrict__ zeros) {
+  const int64_t base = (int64_t)blockIdx.x * (256 * U) + threadIdx.x;
+  float v[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    if (c < nchunks) {
+      Load8<TIn>::run(w, c, v[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    float mn = v[u][0], mx = v[u][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, v[u][i]);
+      mx = fmaxf(mx, v[u][i]);
+    }
+    mn = group_min<L>(mn);
+    mx = group_max<L>(mx);
+    TS st;
+    float s;
+    int zp;
+    scale_zero<TS>(mn, mx, st, s, zp);
+    const uint32_t word = pack8(v[u], s, (float)zp);
+    if (c < nchunks) {
+      packed[c] = word;
+      if ((threadIdx.x & (L - 1)) == 0) {
+        const int64_t gi = c / L;
+        scales[gi] = st;
+        zeros[gi] = (TS)(float)zp;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantize + pack, any group size that is a multiple of 8: one wave per
+// group, two passes over the group (the second pass reads it from cache).
+// ---------------------------------------------------------------------------
+template <typename TIn, typename TS>
+__global__ __launch_bounds__(256) void k_quantize_pack_wave(const void* __restrict__ w,
+                                                           int64_t ngroups, int cpg,
+                                                           uint32_t* __restrict__ packed,
+                                                           TS* __restrict__ scales,
+                                                           TS* __restrict__ zeros) {
+  const int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (grp >= ngroups) return;  // uniform per wave
+  const int64_t c0 = grp * cpg;
+  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+  for (int c = lane; c < cpg; c += kWave) {
+    float v[8];
+    Load8<TIn>::run(w, c0 + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
+    }
+  }
+  mn = group_min<kWave>(mn);
+  mx = group_max<kWave>(mx);
+  TS st;
+  float s;
+  int zp;
+  scale_zero<TS>(mn, mx, st, s, zp);
+  for (int c = lane; c < cpg; c += kWave) {
+    float v[8];
+    Load8<TIn>::run(w, c0 + c, v);
+    packed[c0 + c] = pack8(v, s, (float)zp);
+  }
+  if (lane == 0) {
+    scales[grp] = st;
+    zeros[grp] = (TS)(float)zp;
+  }
+}
+
+template <typename TIn, typename TS>
+static hipError_t launch_qp(const void* w, int64_t n, int64_t k, int g, uint8_t* packed, void* scales,
+                            void* zeros, hipStream_t st) {
+  const int64_t nchunks = n * k / 8;
+  uint32_t* pk = (uint32_t*)packed;
+  TS* sc = (TS*)scales;
+  TS* zr = (TS*)zeros;
+  constexpr int U = sizeof(TIn) == 2 ? 4 : 2;
+  const int64_t per_block = 256 * U;
+  const dim3 grid((unsigned)((nchunks + per_block - 1) / per_block));
+  switch (g) {
+    case 32:
+      k_quantize_pack_sub<TIn, TS, 4, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      break;
+    case 64:
+      k_quantize_pack_sub<TIn, TS, 8, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      break;
+    case 128:
+      k_quantize_pack_sub<TIn, TS, 16, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      break;
+    case 256:
+      k_quantize_pack_sub<TIn, TS, 32, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      break;
+    case 512:
+      k_quantize_pack_sub<TIn, TS, 64, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      break;
+    default: {
+      const int64_t ngroups = n * (k / g);
+      const dim3 g2((unsigned)((ngroups + 3) / 4));
+      k_quantize_pack_wave<TIn, TS><<<g2, 256, 0, st>>>(w, ngroups, g / 8, pk, sc, zr);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
+                                uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                                hipStream_t st) {
+  const bool in_bf16 = (w_dtype == W4_BF16);
+  const bool s_f16 = (sz_dtype == W4_F16);
+  if (in_bf16 && s_f16) return launch_qp<__bf16, _Float16>(w, n, k, g, packed, scales, zeros, st);
+  if (in_bf16) return launch_qp<__bf16, float>(w, n, k, g, packed, scales, zeros, st);
+  if (s_f16) return launch_qp<float, _Float16>(w, n, k, g, packed, scales, zeros, st);
+  return launch_qp<float, float>(w, n, k, g, packed, scales, zeros, st);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize ("From Scratch: Building a GPTQ INT4 Quantizer in Pure Python",
+// Step 4): w = fl32((q - zp) * scale), rounded to the output type.
+// One lane per 32-bit word (8 codes); grid-stride over the flat tensor.
+// ---------------------------------------------------------------------------
+template <typename TS, int OUT>
+__global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ packed,
+                                                const void* __restrict__ scales,
+                                                const void* __restrict__ zeros, int64_t nchunks,
+                                                int cpg, void* __restrict__ out) {
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * 256) {
+    const uint32_t word = packed[c];
+    const int64_t gi = c / cpg;
+    const float s = ScaleT<TS>::load(scales, gi);
+    const int zp = (int)ScaleT<TS>::load(zeros, gi);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)((int)((word >> (4 * i)) & 15u) - zp) * s;
+    if constexpr (OUT == W4_F32) {
+      f32x4* o = (f32x4*)out + 2 * c;
+      o[0] = f32x4{v[0], v[1], v[2], v[3]};
+      o[1] = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        h[i] = (OUT == W4_F16) ? f32_to_f16_bits(v[i]) : f32_to_bf16_bits(v[i]);
+      ((u32x4*)out)[c] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                               h[6] | (h[7] << 16)};
+    }
+  }
+}
+
+template <typename TS>
+static hipError_t launch_dq(const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
+                            int64_t k, int g, void* out, int out_dtype, hipStream_t st) {
+  const int64_t nchunks = n * k / 8;
+  int64_t blocks = (nchunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  const dim3 grid((unsigned)blocks);
+  const uint32_t* pk = (const uint32_t*)packed;
+  if (out_dtype == W4_F32)
+    k_dequant<TS, W4_F32><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, g / 8, out);
+  else if (out_dtype == W4_F16)
+    k_dequant<TS, W4_F16><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, g / 8, out);
+  else
+    k_dequant<TS, W4_BF16><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, g / 8, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* packed, const void* scales, const void* zeros,
+                          int sz_dtype, int64_t n, int64_t k, int g, void* out, int out_dtype,
+                          hipStream_t st) {
+  if (sz_dtype == W4_F16)
+    return launch_dq<_Float16>(packed, scales, zeros, n, k, g, out, out_dtype, st);
+  return launch_dq<float>(packed, scales, zeros, n, k, g, out, out_dtype, st);
+}
+
+// ---------------------------------------------------------------------------
+// Per-token INT8 activations ("Hands-on Build Guide: Group-wise INT4
+// Weight-only Quantization with Per-channel Scales", Step 3).
+// One 256-lane block per token: pass 1 finds max|x|, pass 2 (re-reading the
+// row from cache) writes clamp(rint(x / s), -128, 127).
+// ---------------------------------------------------------------------------
+template <typename TX>
+__global__ __launch_bounds__(256) void k_act_quant(const void* __restrict__ x, int64_t k,
+                                                  int8_t* __restrict__ xq,
+                                                  float* __restrict__ x_scale) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int64_t nch = k / 8;
+  const int64_t c0 = row * nch;
+  float amax = 0.0f;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    Load8<TX>::run(x, c0 + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = group_max<kWave>(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = fmaxf(amax, 1e-8f) / 127.0f;
+  for (int64_t c = threadIdx.x; c < nch; c += 256) {
+    float v[8];
+    Load8<TX>::run(x, c0 + c, v);
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float t = rintf(v[i] / s);
+      t = fminf(fmaxf(t, -128.0f), 127.0f);
+      b[i] = (uint32_t)((int)t) & 0xffu;
+    }
+    ((u32x2*)xq)[c0 + c] =
+        u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+              b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+  }
+  if (threadIdx.x == 0) x_scale[row] = s;
+}
+
+hipError_t launch_act_quant(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* xq,
+                            float* x_scale, hipStream_t st) {
+  const dim3 grid((unsigned)m);
+  if (x_dtype == W4_BF16)
+    k_act_quant<__bf16><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+  else
+    k_act_quant<float><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,29 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+// Launchers assume validated arguments and enqueue on the given stream.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/w4.h"
+
+namespace w4 {
+
+hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
+                                uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                                hipStream_t st);
+hipError_t launch_dequant(const uint8_t* packed, const void* scales, const void* zeros,
+                          int sz_dtype, int64_t n, int64_t k, int g, void* out, int out_dtype,
+                          hipStream_t st);
+hipError_t launch_act_quant(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* xq,
+                            float* x_scale, hipStream_t st);
+hipError_t launch_w4a16_generic(const void* x, int x_dtype, int64_t m, int64_t k,
+                                const uint8_t* packed, const void* scales, const void* zeros,
+                                int sz_dtype, int64_t n, int g, void* y, int y_dtype,
+                                hipStream_t st);
+hipError_t launch_w4a8_generic(const int8_t* xq, const float* xs, int64_t m, int64_t k,
+                               const uint8_t* packed, const void* scales, const void* zeros,
+                               int sz_dtype, int64_t n, int g, void* y, int y_dtype,
+                               hipStream_t st);
+
+}  // namespace w4

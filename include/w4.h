@@ -1,0 +1,148 @@
+/*
+ * w4.h -- C ABI of libw4: group-wise asymmetric INT4 weight quantization and
+ * the dequantize-matmul that consumes it, for AMD Instinct MI355X (gfx950).
+ *
+ * Method (martinuke0.github.io posts):
+ *   [P1] "Hands-on Build Guide: Group-wise INT4 Weight-only Quantization with
+ *        Per-channel Scales"
+ *   [P2] "From-scratch INT4 Weight-only Quantizer with Per-group Scales and
+ *        Zero-points for LLMs"
+ *   [P3] "Building a From-Scratch Group-Wise INT4 Quantization Layer for
+ *        LLaMA Weights"
+ *   [P4] "Build a GPTQ INT4 Quantization Engine in Python/NumPy"
+ *   [P5] "From Scratch: Building a GPTQ INT4 Quantizer in Pure Python"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Shapes: N = out_features, K = in_features, M = tokens, g = group size.
+ *    W is [N, K] ("nn.Linear" layout), x is [M, K], y is [M, N].  Every
+ *    tensor is dense, row-major, with no padding between rows.
+ *  - A group is a run of g consecutive elements of one row of W (along K).
+ *    Requirements: g % 32 == 0, K % g == 0.  scales and zeros are [N, K/g].
+ *  - packed is uint8 [N, K/2]; byte j of row n holds the code of column 2j in
+ *    its low nibble and of column 2j+1 in its high nibble ([P4] Step 4).
+ *  - zeros are stored in the same dtype as scales and hold the integers
+ *    0..15 exactly (+0.0 for zero).
+ *  - Pointers are device pointers (hipMalloc'd or equivalent) and must be
+ *    16-byte aligned.  The caller owns every buffer; the library never
+ *    allocates, frees or synchronizes.  Work is enqueued on `stream` (0 = the
+ *    null stream) and is asynchronous: outputs are valid once the stream has
+ *    reached that point.  Calls on one stream are ordered; calls on different
+ *    streams that write the same buffer race.
+ *  - Errors: arguments are validated before any HIP call; an invalid call
+ *    returns W4_EINVAL and enqueues nothing.  A failed launch returns W4_EHIP.
+ *    w4_last_error() gives a message for the last failure on the calling
+ *    thread.  No C++ exception crosses this interface.
+ *  - M == 0 or N == 0 is a valid empty call: it returns W4_OK and enqueues
+ *    nothing.  K must be > 0.
+ *  - Inputs must be finite; NaN or Inf inputs, and group ranges that overflow
+ *    the scale dtype (fp16 scales: (max - min) / 15 > 65504), give unspecified
+ *    (but memory-safe) results.
+ */
+#ifndef W4_H_
+#define W4_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types (the `*_dtype` arguments). */
+enum w4_dtype { W4_F32 = 0, W4_F16 = 1, W4_BF16 = 2 };
+
+/* Return codes. */
+enum w4_status {
+  W4_OK = 0,
+  W4_EINVAL = -1,       /* bad argument: null/misaligned pointer, bad shape or dtype */
+  W4_EUNSUPPORTED = -2, /* valid request this build does not implement */
+  W4_EHIP = -3          /* the HIP runtime reported an error */
+};
+
+/*
+ * quantize_pack_int4 -- group-wise asymmetric INT4 round-to-nearest + pack.
+ *
+ * For each group G of W ([P2] Architecture Overview and Steps 5-6;
+ * [P5] Step 2), in IEEE float32 with round-to-nearest-even:
+ *   mn = min(G), mx = max(G)
+ *   scale  = (mx - mn) / 15, rounded to sz_dtype; a stored 0 becomes 1
+ *   zp     = clamp(rint(-mn / scale), 0, 15)   (with the stored scale)
+ *   q(w)   = clamp(rint(w / scale + zp), 0, 15)  (rint: ties to even)
+ * and the codes are packed two per byte, even column in the low nibble.
+ *
+ *   w        [N, K] input weights, w_dtype W4_F32 or W4_BF16
+ *   packed   [N, K/2] uint8 output
+ *   scales   [N, K/g] output, sz_dtype W4_F32 or W4_F16
+ *   zeros    [N, K/g] output, same dtype as scales
+ * The outputs are bit-for-bit those of the definition above.
+ */
+int quantize_pack_int4(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                       uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                       hipStream_t stream);
+
+/*
+ * dequant_int4 -- w_out[n, k] = (q[n, k] - zp[n, k/g]) * scale[n, k/g]
+ * ([P5] Step 4), computed as one float32 product of the exact integer
+ * difference and the scale, then rounded (nearest-even) to out_dtype
+ * (W4_F32, W4_F16 or W4_BF16).  w_out is [N, K].  Bit-exact; this is the
+ * unfused form, used to check and compare the fused matmuls.
+ */
+int dequant_int4(const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                 int64_t n, int64_t k, int32_t group_size, void* w_out, int out_dtype,
+                 hipStream_t stream);
+
+/*
+ * quantize_act_int8 -- per-token dynamic INT8 activations ([P1]
+ * Architecture Overview, Step 3), in IEEE float32:
+ *   x_scale[m] = max(max_k |x[m, k]|, 1e-8) / 127
+ *   xq[m, k]   = clamp(rint(x[m, k] / x_scale[m]), -128, 127)
+ *   x        [M, K] input, x_dtype W4_F32 or W4_BF16; K % 8 == 0
+ *   xq       [M, K] int8 output;  x_scale [M] float32 output.
+ * Bit-exact.
+ */
+int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* xq,
+                      float* x_scale, hipStream_t stream);
+
+/*
+ * w4a16_matmul -- y = x . dequant(W)^T  ([P3] Step 2; [P4] Step 5), fused:
+ * the packed weights are read from memory once per output tile and
+ * dequantized in registers/LDS; no dequantized weight matrix is written.
+ *   x   [M, K], x_dtype W4_BF16 or W4_F32
+ *   y   [M, N], y_dtype W4_BF16 or W4_F32 (float32 accumulation, one
+ *       rounding to y_dtype at the end)
+ * Accuracy: max|y - y_exact| / max|y_exact| <= 1e-2 for bf16 y and
+ * <= 3e-3 for fp32 y, y_exact being the float64 product of the same x and
+ * the exactly dequantized weights.  Small M (decode) and large M (prefill)
+ * use different kernels; both meet the same bound.  Results are
+ * deterministic (no atomics; a fixed reduction order per shape).
+ */
+int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                 const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                 int32_t group_size, void* y, int y_dtype, hipStream_t stream);
+
+/*
+ * w4a8_matmul -- y[m, n] = x_scale[m] * sum_k xq[m, k] * dequant(W)[n, k]
+ * ([P1] Architecture Overview, Step 5), with xq/x_scale as produced by
+ * quantize_act_int8.  Per group the integer sum of xq * (q - zp) is exact
+ * (int32); it is scaled in float32.  y [M, N], y_dtype W4_BF16 or W4_F32.
+ * Same accuracy bound and determinism as w4a16_matmul.
+ */
+int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
+                const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                int64_t n, int32_t group_size, void* y, int y_dtype, hipStream_t stream);
+
+/* Static description of a w4_status value (never NULL). */
+const char* w4_status_string(int status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* w4_last_error(void);
+
+/* Library version string, e.g. "w4 0.1.0 gfx950". */
+const char* w4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H_ */

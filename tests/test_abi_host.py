@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/w4.h declares, and
+reject invalid arguments with W4_EINVAL *before* touching the HIP runtime.
+On a machine without a GPU any HIP call would fail, so a W4_EINVAL status
+with the expected message shows the check ran first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+LIB = os.path.join(ROOT, "dequant_gemm_quantize_amd", "libw4.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libw4.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import dequant_gemm_quantize_amd as w4
+    return w4.load()
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for want in ("quantize_pack_int4", "dequant_int4", "quantize_act_int8", "w4a16_matmul",
+                 "w4a8_matmul", "w4_status_string", "w4_last_error", "w4_version"):
+        assert want in names, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_binding_covers_the_header():
+    from dequant_gemm_quantize_amd import _lib
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == declared_functions()
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, 7):
+        assert lib.w4_status_string(code)
+    assert b"W4_EINVAL" in lib.w4_status_string(-1)
+    assert lib.w4_version().startswith(b"w4 ")
+
+
+# pointer values used for validation only; they are never dereferenced
+A = 0x10000  # 16-byte aligned
+U = 0x10004  # misaligned
+
+
+def _err(lib):
+    return lib.w4_last_error().decode()
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, 2, 4, 100, 32, A, A, A, 1, None), "not a multiple of group_size"),
+    ((A, 2, 4, 128, 48, A, A, A, 1, None), "multiple of 32"),
+    ((A, 2, 4, 128, 0, A, A, A, 1, None), "multiple of 32"),
+    ((A, 2, 4, 0, 32, A, A, A, 1, None), "k = 0"),
+    ((A, 2, -1, 128, 32, A, A, A, 1, None), "n = -1"),
+    ((A, 1, 4, 128, 32, A, A, A, 1, None), "w dtype"),
+    ((A, 2, 4, 128, 32, A, A, A, 2, None), "scale dtype"),
+    ((None, 2, 4, 128, 32, A, A, A, 1, None), "w is NULL"),
+    ((U, 2, 4, 128, 32, A, A, A, 1, None), "w is not 16-byte aligned"),
+    ((A, 2, 4, 128, 32, A, U, A, 1, None), "scales is not 16-byte aligned"),
+    ((A, 2, 4, 128, 32, A, A, None, 1, None), "zeros is NULL"),
+    ((A, 2, 1 << 30, 1 << 20, 32, A, A, A, 1, None), "too large"),
+])
+def test_quantize_pack_rejects(lib, args, msg):
+    assert lib.quantize_pack_int4(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+def test_empty_calls_are_noops(lib):
+    assert lib.quantize_pack_int4(None, 2, 0, 128, 32, None, None, None, 1, None) == 0
+    assert lib.dequant_int4(None, None, None, 1, 0, 128, 32, None, 2, None) == 0
+    assert lib.quantize_act_int8(None, 2, 0, 128, None, None, None) == 0
+    assert lib.w4a16_matmul(None, 2, 0, 128, None, None, None, 1, 64, 128, None, 2, None) == 0
+    assert lib.w4a16_matmul(None, 2, 3, 128, None, None, None, 1, 0, 128, None, 2, None) == 0
+    assert lib.w4a8_matmul(None, None, 0, 128, None, None, None, 1, 64, 128, None, 2, None) == 0
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, 2, 1, 100, A, A, A, 1, 64, 32, A, 2, None), "not a multiple of group_size"),
+    ((A, 1, 1, 128, A, A, A, 1, 64, 32, A, 2, None), "x dtype"),
+    ((A, 2, 1, 128, A, A, A, 1, 64, 32, A, 1, None), "y dtype"),
+    ((A, 2, -2, 128, A, A, A, 1, 64, 32, A, 2, None), "m = -2"),
+    ((U, 2, 1, 128, A, A, A, 1, 64, 32, A, 2, None), "x is not 16-byte aligned"),
+    ((A, 2, 1, 128, None, A, A, 1, 64, 32, A, 2, None), "packed is NULL"),
+    ((A, 2, 1, 128, A, A, A, 1, 64, 32, U, 2, None), "y is not 16-byte aligned"),
+    ((A, 2, 1, 128, A, A, A, 5, 64, 32, A, 2, None), "scale dtype"),
+])
+def test_w4a16_rejects(lib, args, msg):
+    assert lib.w4a16_matmul(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, A, 1, 100, A, A, A, 1, 64, 32, A, 2, None), "not a multiple of group_size"),
+    ((A, None, 1, 128, A, A, A, 1, 64, 32, A, 2, None), "x_scale is NULL"),
+    ((A, A + 2, 1, 128, A, A, A, 1, 64, 32, A, 2, None), "x_scale is not 4-byte aligned"),
+    ((A, A, 1, 128, A, A, A, 1, 64, 32, A, 1, None), "y dtype"),
+    ((None, A, 1, 128, A, A, A, 1, 64, 32, A, 2, None), "xq is NULL"),
+])
+def test_w4a8_rejects(lib, args, msg):
+    assert lib.w4a8_matmul(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, 2, 4, 100, A, A, None), "multiple of 8"),
+    ((A, 1, 4, 128, A, A, None), "x dtype"),
+    ((A, 2, 4, 128, A, None, None), "x_scale is NULL"),
+    ((U, 2, 4, 128, A, A, None), "x is not 16-byte aligned"),
+])
+def test_act_quant_rejects(lib, args, msg):
+    assert lib.quantize_act_int8(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, A, A, 1, 4, 128, 32, A, 7, None), "out dtype"),
+    ((A, A, A, 1, 4, 128, 32, U, 2, None), "w_out is not 16-byte aligned"),
+])
+def test_dequant_rejects(lib, args, msg):
+    assert lib.dequant_int4(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import dequant_gemm_quantize_amd as w4
+    with pytest.raises(ValueError, match="GPU only"):
+        w4.quantize_pack_int4(torch.zeros(4, 128), 32)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "dequant_gemm_quantize_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("no oracle", ""), f

@@ -1,0 +1,228 @@
+"""GPU parity: w4a16_matmul and w4a8_matmul vs the oracle's float64 products.
+
+Bars (stated with the method's target): max|y - y64| / max|y64| <= 1e-2 for
+bf16 outputs and <= 3e-3 for fp32 outputs; bit-exact where the exact result
+is representable (integer constructions).  Small M takes the decode kernels,
+large M the MFMA kernels; the shapes below reach every path, with ragged
+tails in M, N and K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.w4_oracle as O
+import workloads as WL
+from tests.gpu_util import TORCH_SZ, Canary, bits, to_dev, to_host, y_as_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 3e-3}
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def w4():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dequant_gemm_quantize_amd as m
+    m.load()
+    return m
+
+
+def make_weights(n, k, g, sz, seed, sigma=0.02):
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0, sigma, (n, k)).astype(np.float32)
+    w.reshape(-1)[rng.choice(n * k, max(1, n * k // 1000), replace=False)] = 0.5
+    return O.quantize_pack_int4(w, "f32", g, sz)
+
+
+def dev_weights(P, S, Z, sz):
+    return to_dev(P, "u8"), to_dev(S, sz), to_dev(Z, sz)
+
+
+def run_w4a16(w4, x_np, xkind, dw, g, ykind, canary=True):
+    m = x_np.shape[0]
+    n = dw[0].shape[0]
+    xt = to_dev(x_np, xkind)
+    if canary:
+        c = Canary((m, n), TDT[ykind])
+        w4.w4a16_matmul(xt, *dw, g, out=c.tensor)
+        c.check()
+        return c.tensor
+    y = w4.w4a16_matmul(xt, *dw, g, out_dtype=TDT[ykind])
+    torch.cuda.synchronize()
+    return y
+
+
+SHAPES = [  # (m, n, k, g)
+    (1, 300, 640, 128), (2, 77, 384, 128), (4, 300, 1024, 128), (8, 129, 640, 128),
+    (1, 64, 640, 32), (3, 40, 384, 96),
+    (9, 300, 640, 128), (16, 256, 512, 128), (17, 300, 384, 128), (33, 129, 640, 128),
+    (64, 520, 1024, 128), (130, 300, 640, 128), (256, 512, 768, 128), (100, 96, 640, 64),
+]
+
+
+@pytest.mark.parametrize("m,n,k,g", SHAPES)
+@pytest.mark.parametrize("sz", ["f16", "f32"])
+def test_w4a16_bf16(w4, m, n, k, g, sz):
+    P, S, Z = make_weights(n, k, g, sz, seed=m * 1000 + n + k)
+    x = WL.bf16_round_bits(np.random.default_rng(m + 5).normal(0, 1, (m, k)).astype(np.float32))
+    y = run_w4a16(w4, x, "bf16", dev_weights(P, S, Z, sz), g, "bf16")
+    ref = O.matmul_w4a16_f64(O.widen_bf16(x), P, S, Z, g)
+    err = O.max_rel_err(y_as_f64(y), ref)
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 256, 256, 32), (3, 100, 384, 128), (19, 64, 640, 64)])
+@pytest.mark.parametrize("ykind", ["f32", "bf16"])
+def test_w4a16_f32_activations(w4, m, n, k, g, ykind):
+    P, S, Z = make_weights(n, k, g, "f32", seed=n + k)
+    x = np.random.default_rng(m).normal(0, 1, (m, k)).astype(np.float32)
+    y = run_w4a16(w4, x, "f32", dev_weights(P, S, Z, "f32"), g, ykind)
+    ref = O.matmul_w4a16_f64(x, P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (8, 48, 512), (16, 64, 256), (40, 300, 1024), (256, 256, 2048)])
+def test_w4a16_exact_integers(w4, m, n, k):
+    """W integers 0..15 (each group holding 0 and 15 -> scale 1, zp 0), x
+    integers in [-8, 8]: every partial sum is an exact integer below 2^24, so
+    the bf16 output must equal the correctly rounded exact product bit for bit."""
+    g = 128 if k % 128 == 0 else 32
+    rng = np.random.default_rng(m + n + k)
+    wi = rng.integers(0, 16, (n, k))
+    for r in range(n):
+        for gi in range(k // g):
+            a, b = rng.choice(g, 2, replace=False)
+            wi[r, gi * g + a], wi[r, gi * g + b] = 0, 15
+    xi = rng.integers(-8, 9, (m, k))
+    wt = to_dev(wi.astype(np.float32), "f32")
+    p, s, z = w4.quantize_pack_int4(wt, g, torch.float16)
+    y = w4.w4a16_matmul(to_dev(WL.bf16_round_bits(xi.astype(np.float32)), "bf16"), p, s, z, g)
+    want = O.to_bf16((xi @ wi.T).astype(np.float32))
+    got = to_host(y)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def test_w4a16_deterministic(w4):
+    P, S, Z = make_weights(512, 1024, 128, "f16", seed=4)
+    dw = dev_weights(P, S, Z, "f16")
+    for m in (1, 8, 64):
+        x = WL.bf16_round_bits(np.random.default_rng(m).normal(0, 1, (m, 1024)).astype(np.float32))
+        a = to_host(run_w4a16(w4, x, "bf16", dw, 128, "bf16", canary=False))
+        b = to_host(run_w4a16(w4, x, "bf16", dw, 128, "bf16", canary=False))
+        assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads
+# ---------------------------------------------------------------------------
+_QCACHE = {}
+
+
+def quantized(name, g, sz):
+    key = (name, g, sz)
+    if key not in _QCACHE:
+        t = WL.weight(name)
+        _QCACHE.clear()
+        _QCACHE[key] = (t, O.quantize_pack_int4(t.data, t.kind, g, sz))
+    return _QCACHE[key]
+
+
+def test_workload_single_layer_fp32(w4):
+    """256x256 fp32 layer, g=32, fp32 scales, fp32 x and y (tolerance 3e-3)."""
+    t, (P, S, Z) = quantized("W1", 32, "f32")
+    x = WL.activation(1, 1, 256)
+    y = run_w4a16(w4, x.data, "f32", dev_weights(P, S, Z, "f32"), 32, "f32")
+    ref = O.matmul_w4a16_f64(x.as_f32(), P, S, Z, 32)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("name", ["Wa", "Wb"])
+@pytest.mark.parametrize("m", [1, 4, 8, 16, 32])
+def test_workload_llama_decode(w4, name, m):
+    """Llama-7B shapes at M = 1 (decode) and 4..32 (small batch)."""
+    t, (P, S, Z) = quantized(name, 128, "f16")
+    x = WL.activation(2 if m == 1 else 3, m, 4096)
+    y = run_w4a16(w4, x.data, "bf16", dev_weights(P, S, Z, "f16"), 128, "bf16")
+    ref = O.matmul_w4a16_f64(x.as_f32(), P, S, Z, 128)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,k", [("Wb", 4096), ("Wd", 11008)])
+def test_workload_prefill(w4, name, k):
+    """M = 2048 prefill; the oracle checks 96 sampled tokens (plus the first
+    and last) against every output column."""
+    t, (P, S, Z) = quantized(name, 128, "f16")
+    x = WL.activation(4, 2048, k)
+    y = run_w4a16(w4, x.data, "bf16", dev_weights(P, S, Z, "f16"), 128, "bf16")
+    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(9).choice(2048, 96, replace=False)]))
+    ref = O.matmul_w4a16_f64(x.as_f32()[rows], P, S, Z, 128)
+    got = y_as_f64(y)[rows]
+    assert O.max_rel_err(got, ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# W4A8
+# ---------------------------------------------------------------------------
+def run_w4a8(w4, x_np, xkind, dw, g, ykind="bf16"):
+    xq, xs = w4.quantize_act_int8(to_dev(x_np, xkind))
+    m, n = x_np.shape[0], dw[0].shape[0]
+    c = Canary((m, n), TDT[ykind])
+    w4.w4a8_matmul(xq, xs, *dw, g, out=c.tensor)
+    c.check()
+    return c.tensor, to_host(xq), to_host(xs)
+
+
+W8_SHAPES = [(1, 300, 640, 128), (5, 129, 1024, 128), (8, 64, 384, 32), (16, 300, 640, 128),
+             (40, 129, 1024, 128), (130, 256, 512, 128), (64, 96, 640, 64)]
+
+
+@pytest.mark.parametrize("m,n,k,g", W8_SHAPES)
+@pytest.mark.parametrize("ykind", ["bf16", "f32"])
+def test_w4a8(w4, m, n, k, g, ykind):
+    P, S, Z = make_weights(n, k, g, "f16", seed=m + 3 * n + k, sigma=0.015)
+    rng = np.random.default_rng(m + 11)
+    x = rng.normal(0, 1, (m, k)).astype(np.float32)
+    x[:, rng.choice(k, max(1, k // 20), replace=False)] *= 20
+    xb = WL.bf16_round_bits(x)
+    y, xq, xs = run_w4a8(w4, xb, "bf16", dev_weights(P, S, Z, "f16"), g, ykind)
+    oq, os_ = O.act_quant_int8(O.widen_bf16(xb))
+    assert np.array_equal(xq, oq) and np.array_equal(bits(xs), bits(os_))
+    ref = O.matmul_w4a8_f64(oq, os_, P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 8192), (8, 48, 1024), (16, 64, 1024), (64, 256, 8192)])
+def test_w4a8_exact_integers(w4, m, n, k):
+    """x integers with |x| <= 127 and 127 present (scale 1, xq = x); W integer
+    codes with scale 1, zp 0: y is an exact integer below 2^24 and the bf16
+    output must be its correctly rounded value."""
+    g = 128
+    rng = np.random.default_rng(7 * m + n)
+    wi = rng.integers(0, 16, (n, k))
+    for r in range(n):
+        for gi in range(k // g):
+            a, b = rng.choice(g, 2, replace=False)
+            wi[r, gi * g + a], wi[r, gi * g + b] = 0, 15
+    xi = rng.integers(-127, 128, (m, k))
+    xi[:, 0] = 127
+    p, s, z = w4.quantize_pack_int4(to_dev(wi.astype(np.float32), "f32"), g, torch.float16)
+    xq, xs = w4.quantize_act_int8(to_dev(WL.bf16_round_bits(xi.astype(np.float32)), "bf16"))
+    assert (to_host(xs) == 1.0).all()
+    y = w4.w4a8_matmul(xq, xs, p, s, z, g)
+    want = O.to_bf16((xi @ wi.T).astype(np.float32))
+    assert np.array_equal(to_host(y), want)
+
+
+@pytest.mark.parametrize("m", [1, 512])
+def test_workload_w4a8(w4, m):
+    """70B-class MLP projection [28672, 8192], heavy-tailed activations; M = 1
+    checked in full, M = 512 on 48 sampled tokens (plus first and last)."""
+    t, (P, S, Z) = quantized("We", 128, "f16")
+    x = WL.activation(5, m, 8192)
+    y, xq, xs = run_w4a8(w4, x.data, "bf16", dev_weights(P, S, Z, "f16"), 128)
+    oq, os_ = O.act_quant_int8(x.as_f32())
+    assert np.array_equal(xq, oq) and np.array_equal(bits(xs), bits(os_))
+    rows = np.arange(m) if m == 1 else np.unique(np.concatenate([[0, m - 1], np.random.default_rng(5).choice(m, 48, replace=False)]))
+    ref = O.matmul_w4a8_f64(oq[rows], os_[rows], P, S, Z, 128)
+    assert O.max_rel_err(y_as_f64(y)[rows], ref) <= TOL["bf16"]
