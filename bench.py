@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark of the INT4 dequantize-matmul hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--quick]
+
+One *step* is the decode-time product of the Llama-7B workload: y = x . W^T
+for x bf16 [1, 4096] against both INT4-packed weights, [4096, 4096] and
+[11008, 4096] (group 128, fp16 scales and zero-points), bf16 out.  ``value``
+is algorithmic bytes per step (packed codes + scales + zeros + x + y) over
+the measured step time, in GB/s.  Weight copies are rotated (R copies, > 1 GB
+in total by default) so every step reads its weights from HBM rather than
+from the 256 MB Infinity Cache.  Inputs are resident in HBM before timing.
+
+The JSON line also carries:
+  roofline      the dominant kernel (the [11008, 4096] decode product) timed
+                alone with HIP events on its stream, against 8 TB/s;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample;
+  extra         every other step of the path (quantize + pack, dequantize,
+                INT8 activations, small-batch sweep, M=2048 prefill, W4A8
+                decode and prefill), each with its algorithmic rate.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "int4 dequant-matmul GB/s (% of HBM peak) at M=1; TFLOP/s at M=2048"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (bytes that must cross HBM, flops that must be done)
+# ---------------------------------------------------------------------------
+def w4a16_bytes(m, n, k, g, x_bytes=2, y_bytes=2, sz_bytes=2):
+    return n * k // 2 + 2 * n * (k // g) * sz_bytes + m * k * x_bytes + m * n * y_bytes
+
+
+def w4a8_bytes(m, n, k, g, y_bytes=2, sz_bytes=2):
+    return n * k // 2 + 2 * n * (k // g) * sz_bytes + m * k + 4 * m + m * n * y_bytes
+
+
+def quant_bytes(n, k, g, w_bytes=2, sz_bytes=2):
+    return n * k * w_bytes + n * k // 2 + 2 * n * (k // g) * sz_bytes
+
+
+def src_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dequant_gemm_quantize_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=32, help="distinct weight copies cycled through")
+    ap.add_argument("--quick", action="store_true", help="skip the extra per-step measurements")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dequant_gemm_quantize_amd as w4
+    import workloads as WL
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w4.load()
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(t):
+        if t.kind == "bf16":
+            return torch.from_numpy(t.data.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(t.data).to(dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    def time_region(fn, iters, per_graph=None):
+        """Seconds per call of fn(i), i = 0..iters-1.
+
+        The calls are captured into HIP graphs (per_graph calls each, default
+        all of them) and replayed between two HIP events recorded on the
+        launch stream, so host-side launch cost does not enter the figure.
+        One untimed replay of every graph precedes the timed one.
+        """
+        per = per_graph or iters
+        graphs = []
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        done = 0
+        while done < iters:
+            cnt = min(per, iters - done)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                for i in range(done, done + cnt):
+                    fn(i)
+            graphs.append(gr)
+            done += cnt
+        stream.wait_stream(side)
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        e1.record(stream)
+        e1.synchronize()
+        del graphs
+        return e0.elapsed_time(e1) / 1e3 / iters
+
+    g = 128
+    log("generating Llama-7B decode weights")
+    wa, wb = WL.weight("Wa"), WL.weight("Wb")
+    x1 = to_dev(WL.activation(2, 1, 4096))
+    shapes = {"Wa": (4096, 4096), "Wb": (11008, 4096)}
+
+    # quantize once on the GPU, then clone R copies of the packed weights
+    q = {}
+    for name, t in (("Wa", wa), ("Wb", wb)):
+        wt = to_dev(t)
+        q[name] = w4.quantize_pack_int4(wt, g, torch.float16)
+        del wt
+    R = max(1, args.rotate)
+    copies = {name: [tuple(a.clone() for a in q[name]) for _ in range(R)] for name in q}
+    y_out = {name: torch.empty((1, shapes[name][0]), dtype=torch.bfloat16, device=dev) for name in q}
+    torch.cuda.synchronize()
+
+    def step(i):
+        for name in ("Wa", "Wb"):
+            p, s, z = copies[name][i % R]
+            w4.w4a16_matmul(x1, p, s, z, g, out=y_out[name])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sec = time_region(step, args.steps)
+    step_bytes = sum(w4a16_bytes(1, n, k, g) for n, k in shapes.values())
+    value = step_bytes / sec / 1e9
+    log(f"decode step: {sec * 1e6:.2f} us, {value:.1f} GB/s")
+
+    # dominant kernel alone: the [11008, 4096] decode product
+    def dom(i):
+        p, s, z = copies["Wb"][i % R]
+        w4.w4a16_matmul(x1, p, s, z, g, out=y_out["Wb"])
+
+    for i in range(args.warmup):
+        dom(i)
+    dsec = time_region(dom, args.steps)
+    dbytes = w4a16_bytes(1, 11008, 4096, g)
+    achieved = dbytes / dsec / 1e9
+    roof = {"kernel": "w4a16 decode, W [11008,4096] int4 g128, x bf16 [1,4096]",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_launch_us": round(dsec * 1e6, 3),
+            "bytes_per_launch": dbytes, "traffic": None}
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+        ent = tr.get("w4a16_decode_Wb")
+        if ent and ent.get("src_hash") == src_hash():
+            roof["traffic"] = ent.get("bytes_per_launch")
+    log(f"dominant kernel: {dsec * 1e6:.2f} us/launch, {achieved:.1f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_decode_m1: x bf16 [1,4096] . W^T for W int4 "
+                               "[4096,4096] and [11008,4096], group 128, fp16 scales/zeros, bf16 out",
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
+                   "rotated_weight_copies": R,
+                   "rotated_bytes": int(R * sum(sum(a.numel() * a.element_size() for a in q[nm]) for nm in q)),
+                   "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": roof,
+    }
+    del q
+
+    if not args.quick:
+        result["extra"] = extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copies, x1)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, WL, np, log, wa, wb)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copies, x1):
+    """Rates of every other step of the path; each is timed with HIP events."""
+    out = {}
+    g = 128
+    R = len(copies["Wa"])
+    reps = max(10, min(50, args.steps // 4))
+
+    # small-batch sweep on the Llama-7B shapes (rotated weights)
+    sweep = {}
+    for m in (1, 2, 4, 8, 16, 32):
+        x = to_dev(WL.activation(2 if m == 1 else 3, m, 4096))
+        row = {}
+        for name, (n, k) in (("Wa", (4096, 4096)), ("Wb", (11008, 4096))):
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            fn = lambda i, name=name, x=x, y=y: w4.w4a16_matmul(x, *copies[name][i % R], g, out=y)
+            for i in range(3):
+                fn(i)
+            sec = time_region(fn, reps)
+            b = w4a16_bytes(m, n, k, g)
+            row[name] = {"us": round(sec * 1e6, 3), "GB/s": round(b / sec / 1e9, 1),
+                         "TFLOP/s": round(2 * m * n * k / sec / 1e12, 3)}
+        sweep[f"M={m}"] = row
+    out["w4a16_small_batch"] = sweep
+    log(f"small-batch sweep: {json.dumps(sweep)}")
+
+    # prefill M=2048 on [11008,4096] and [4096,11008]
+    pre = {}
+    for name, (n, k) in (("Wb", (11008, 4096)), ("Wd", (4096, 11008))):
+        t = WL.weight(name)
+        wt = to_dev(t)
+        p, s, z = w4.quantize_pack_int4(wt, g, torch.float16)
+        # quantize + pack rate on this weight (bf16 in)
+        qo = (torch.empty_like(p), torch.empty_like(s), torch.empty_like(z))
+        qsec = time_region(lambda i: w4.quantize_pack_int4(wt, g, torch.float16, out=qo), reps)
+        out.setdefault("quantize_pack", {})[name] = {
+            "us": round(qsec * 1e6, 2), "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}
+        if name == "Wb":
+            dq = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+            dsec = time_region(lambda i: w4.dequant_int4(p, s, z, g, out=dq), reps)
+            out["dequant_int4_bf16"] = {"us": round(dsec * 1e6, 2),
+                                        "GB/s": round((n * k // 2 + 4 * n * (k // g) + 2 * n * k) / dsec / 1e9, 1)}
+            del dq
+        del wt
+        x = to_dev(WL.activation(4, 2048, k))
+        y = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
+        fn = lambda i: w4.w4a16_matmul(x, p, s, z, g, out=y)
+        for i in range(3):
+            fn(i)
+        sec = time_region(fn, reps)
+        tf = 2 * 2048 * n * k / sec / 1e12
+        pre[name] = {"us": round(sec * 1e6, 2), "TFLOP/s": round(tf, 1),
+                     "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+        del x, y, p, s, z
+    out["w4a16_prefill_m2048"] = pre
+    log(f"prefill: {json.dumps(pre)}")
+
+    # W4A8 on the 70B-class MLP projection
+    t = WL.weight("We")
+    wt = to_dev(t)
+    n, k = 28672, 8192
+    p, s, z = w4.quantize_pack_int4(wt, g, torch.float16)
+    qo = (torch.empty_like(p), torch.empty_like(s), torch.empty_like(z))
+    qsec = time_region(lambda i: w4.quantize_pack_int4(wt, g, torch.float16, out=qo), 5)
+    out.setdefault("quantize_pack", {})["We"] = {"us": round(qsec * 1e6, 2),
+                                                 "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}
+    del wt, qo
+    cp8 = [(p, s, z)] + [tuple(a.clone() for a in (p, s, z)) for _ in range(3)]
+    w8 = {}
+    for m in (1, 512):
+        xb = to_dev(WL.activation(5, m, 8192))
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xs = torch.empty((m,), dtype=torch.float32, device=dev)
+        asec = time_region(lambda i: w4.quantize_act_int8(xb, out=(xq, xs)), reps)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        fn = lambda i: w4.w4a8_matmul(xq, xs, *cp8[i % len(cp8)], g, out=y)
+        for i in range(3):
+            fn(i)
+        sec = time_region(fn, reps)
+        b = w4a8_bytes(m, n, k, g)
+        w8[f"M={m}"] = {"act_quant_us": round(asec * 1e6, 2), "us": round(sec * 1e6, 2),
+                        "GB/s": round(b / sec / 1e9, 1), "TOP/s": round(2 * m * n * k / sec / 1e12, 2),
+                        "frac_int8_peak": round(2 * m * n * k / sec / 1e12 / INT8_PEAK_TOPS, 4),
+                        "frac_hbm": round(b / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    out["w4a8_70b_mlp"] = w8
+    log(f"w4a8: {json.dumps(w8)}")
+    del cp8, p, s, z
+
+    # single fp32 layer (latency bound)
+    t1 = WL.weight("W1")
+    w1 = to_dev(t1)
+    p, s, z = w4.quantize_pack_int4(w1, 32, torch.float32)
+    x = to_dev(WL.activation(1, 1, 256))
+    y = torch.empty((1, 256), dtype=torch.float32, device=dev)
+    sec = time_region(lambda i: w4.w4a16_matmul(x, p, s, z, 32, out=y), reps)
+    out["single_layer_fp32_256"] = {"us": round(sec * 1e6, 2)}
+    return out
+
+
+def cpu_baseline(args, WL, np, log, wa, wb):
+    """The oracle (unchanged) on this host: the same decode step, repeated
+    until about --cpu-seconds of CPU work have run."""
+    import oracle.w4_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = None
+    g = 128
+    qa = O.quantize_pack_int4(wa.data, wa.kind, g, "f16")
+    qb = O.quantize_pack_int4(wb.data, wb.kind, g, "f16")
+    x = WL.activation(2, 1, 4096).as_f32()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.matmul_w4a16_f64(x, *qa, g)
+        O.matmul_w4a16_f64(x, *qb, g)
+        steps += 1
+        if time.perf_counter() - t0 > args.cpu_seconds or steps >= 1000:
+            break
+    sec = (time.perf_counter() - t0) / steps
+    step_bytes = w4a16_bytes(1, 4096, 4096, g) + w4a16_bytes(1, 11008, 4096, g)
+    blas_threads = 1
+    if threadpool_info is not None:
+        for info in threadpool_info():
+            if info.get("user_api") == "blas":
+                blas_threads = max(blas_threads, int(info.get("num_threads", 1)))
+    res = {"value": round(step_bytes / sec / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
+           "kind": "oracle",
+           "sample": f"{steps} full decode steps (W4A16 M=1 on [4096,4096] and [11008,4096]): "
+                     f"NumPy unpack/dequantize chunk by chunk in float64 (1 thread) and a BLAS "
+                     f"float64 product ({blas_threads} threads); {sec * 1e3:.1f} ms per step",
+           "ms_per_step": round(sec * 1e3, 3), "host_cpus": os.cpu_count(),
+           "affinity_cpus": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+    log(f"cpu baseline: {res['value']} GB/s over {steps} steps")
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

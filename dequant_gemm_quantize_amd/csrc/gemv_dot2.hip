@@ -1,0 +1,266 @@
+// Decode fused dequantize-GEMV for one or two bf16 tokens (M <= 2), any
+// group size that is a multiple of 32 columns.  VALU-only: no MFMA.
+//
+// Math, per 32-column chunk c of weight row n (inside one group: scale s,
+// zero-point zp) and token m:
+//   sum_k x[m,k] (q[n,k] - zp) s
+//     = s * sum_k x[m,k] (128 + q[n,k])  -  s (128 + zp) * xs[m,c]
+// with xs[m,c] = sum of the chunk's activations ("From Scratch: Building a
+// GPTQ INT4 Quantizer in Pure Python", Step 4, inside the product of
+// "Building a From-Scratch Group-Wise INT4 Quantization Layer for LLaMA
+// Weights", Step 2).  128 + q is an exact bfloat16 built from the nibble
+// with a shift and one and-or; v_dot2_f32_bf16 multiplies two such codes by
+// two activations and accumulates in fp32.
+//
+// Work layout.  A 256-lane workgroup owns 16 weight rows; wave w owns rows
+// 4w .. 4w+3 over all of K.  Lane l covers the 16-byte chunks l, l+64, ...
+// of a row (32 columns each), so every load instruction reads 1 KB of one
+// row contiguously.  The activations of the lane's columns are read once
+// into registers (through LDS, staged by the workgroup) and reused for the
+// wave's four rows; the chunk sums xs are formed once as well.  Each row's
+// 64 partial sums are added with DPP row operations.
+#include "w4_common.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int kRowsWg = 16;    // weight rows per workgroup
+constexpr int kRowsWave = 4;   // weight rows per wave
+constexpr int kMaxCh = 4;      // 16-byte chunks per lane and row (K <= 64 * 4 * 32 = 8192)
+
+__device__ __forceinline__ uint32_t and_or2(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// 8 codes of a word -> 4 bf16 pairs (128 + q) in the order (0,4),(1,5),(2,6),(3,7).
+__device__ __forceinline__ void codes8(uint32_t p, uint32_t (&o)[4]) {
+  o[0] = and_or2(p, 0x000f000fu, 0x43004300u);
+  o[1] = and_or2(p >> 4, 0x000f000fu, 0x43004300u);
+  o[2] = and_or2(p >> 8, 0x000f000fu, 0x43004300u);
+  o[3] = and_or2(p >> 12, 0x000f000fu, 0x43004300u);
+}
+
+// 8 bf16 activations (4 pairs, natural order) -> pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7).
+__device__ __forceinline__ void interleave(const u32x4 v, uint32_t (&o)[4]) {
+  o[0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Sum over the 64 lanes of a wave, result valid in lane 63 (DPP row ops).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  // within rows of 16 lanes
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));  // row_shr:1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));  // row_shr:2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));  // row_shr:4
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));  // row_shr:8
+  // across rows
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+
+template <typename TY>
+__device__ __forceinline__ void put(void* y, int64_t i, float v) {
+  if constexpr (sizeof(TY) == 4) {
+    ((float*)y)[i] = v;
+  } else {
+    ((uint16_t*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// Raw scale / zero-point element (loaded unconverted, converted later).
+template <typename TS> struct SZ;
+template <> struct SZ<_Float16> {
+  typedef uint16_t T;
+  __device__ static float f(T v) { return (float)__builtin_bit_cast(_Float16, v); }
+};
+template <> struct SZ<float> {
+  typedef uint32_t T;
+  __device__ static float f(T v) { return __uint_as_float(v); }
+};
+
+}  // namespace
+
+// CH: 16-byte chunks per lane and row (K = 64 * 32 * CH).
+template <typename TS, typename TY, int MT, int CH>
+__global__ __launch_bounds__(256) void k_w4a16_dot2(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
+    void* __restrict__ y) {
+  // LDS: activations [MT][K] bf16 (natural order; region rounded up to the
+  // staging lanes), scale tile [16][ng] as (s, -s*(128+zp)) float pairs
+  // (region of 1024 pairs).
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  constexpr int XPER_ = (MT * CH * 2048 / 8 + 255) / 256;
+  const int ng = (int)(K / g);
+  u32x4* x_l = (u32x4*)lds;
+  float2* sz_l = (float2*)(lds + XPER_ * 256 * 16);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * kRowsWg;
+
+  // ---- 1. staging loads (activations, scale / zero-point tile), straight
+  //         line: XPER / SPER per thread, indices clamped into range -------
+  constexpr int XPER = (MT * CH * 2048 / 8 + 255) / 256;  // 16-byte activation groups
+  const int xgroups = MT * (int)(K / 8);
+  const u32x4* xg = (const u32x4*)x;
+  u32x4 xv[XPER];
+#pragma unroll
+  for (int r = 0; r < XPER; ++r) {
+    const int i = tid + 256 * r;
+    xv[r] = xg[i < xgroups ? i : xgroups - 1];
+  }
+  const int tile = kRowsWg * ng;  // <= 16 * 64 elements for K <= 8192, g >= 128
+  constexpr int SPER = 4;
+  typedef typename SZ<TS>::T R;
+  R sv[SPER], zv[SPER];
+#pragma unroll
+  for (int r = 0; r < SPER; ++r) {
+    const int e = tid + 256 * r;
+    const int ee = e < tile ? e : tile - 1;
+    const int rr = ee / ng, q = ee - rr * ng;
+    const int64_t row = (n0 + rr) < N ? (n0 + rr) : (N - 1);
+    sv[r] = ((const R*)scales)[row * ng + q];
+    zv[r] = ((const R*)zeros)[row * ng + q];
+  }
+
+  // ---- 2. codes of the wave's rows: kRowsWave x CH 16-byte loads per lane --
+  u32x4 wq[kRowsWave][CH];
+#pragma unroll
+  for (int r = 0; r < kRowsWave; ++r) {
+    int64_t n = n0 + wave * kRowsWave + r;
+    n = n < N ? n : N - 1;
+    const u32x4* row = (const u32x4*)(packed + n * (K / 2));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) wq[r][c] = row[lane + 64 * c];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. LDS stores (wait for the staging loads only) ---------------------
+  // unconditional: the LDS regions have room for every staging lane
+#pragma unroll
+  for (int r = 0; r < XPER; ++r) x_l[tid + 256 * r] = xv[r];
+#pragma unroll
+  for (int r = 0; r < SPER; ++r) {
+    const float sf = SZ<TS>::f(sv[r]);
+    sz_l[tid + 256 * r] = float2{sf, -sf * (128.0f + SZ<TS>::f(zv[r]))};
+  }
+  __syncthreads();
+
+  // ---- activations of this lane's columns, interleaved; chunk sums --------
+  uint32_t xa[MT][CH][16];
+  float xs[MT][CH];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // columns 32*(lane + 64c) .. +31 = 16-byte groups 4*(lane + 64c) .. +3
+      const u32x4* src = x_l + (int64_t)m * (K / 8) + 4 * (lane + 64 * c);
+      float s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = src[q];
+        uint32_t o[4];
+        interleave(v, o);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xa[m][c][4 * q + t] = o[t];
+        s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
+             bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+      }
+      xs[m][c] = s;
+    }
+
+  // ---- rows: dot products, scale, zero-point correction, wave sums --------
+  int gq[CH];  // group of the lane's chunk c
+#pragma unroll
+  for (int c = 0; c < CH; ++c) gq[c] = (32 * (lane + 64 * c)) / g;
+#pragma unroll
+  for (int r = 0; r < kRowsWave; ++r) {
+    const int rr = wave * kRowsWave + r;
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const float2 sc = sz_l[rr * ng + gq[c]];
+      const uint32_t w4[4] = {wq[r][c].x, wq[r][c].y, wq[r][c].z, wq[r][c].w};
+      float d[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) d[m] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t b[4];
+        codes8(w4[t], b);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) d[m] = dot2(b[u], xa[m][c][4 * t + u], d[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc.x, d[m], fmaf(sc.y, xs[m][c], acc[m]));
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float tot = wave_sum_dpp(acc[m]);
+      const int64_t n = n0 + rr;
+      if (lane == 63 && m < M && n < N) put<TY>(y, (int64_t)m * N + n, tot);
+    }
+  }
+}
+
+size_t dot2_lds_bytes(int64_t m, int64_t k, int g) {
+  const int64_t xper = (m * k / 8 + 255) / 256;
+  return (size_t)(xper * 256 * 16 + 4 * 256 * 8);
+}
+
+bool dot2_fits(int64_t m, int64_t k, int g) {
+  return k % 2048 == 0 && g >= 128 && ((m == 1 && k <= 8192) || (m == 2 && k <= 4096));
+}
+
+template <typename TS, typename TY, int MT>
+static void dot2_go(dim3 grid, hipStream_t st, const uint16_t* x, int64_t k, const uint8_t* packed,
+                    const void* scales, const void* zeros, int64_t n, int g, void* y) {
+  const size_t lds = dot2_lds_bytes(MT, k, g);
+  const int ch = (int)(k / 2048);
+  switch (ch) {
+    case 1: k_w4a16_dot2<TS, TY, MT, 1><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 2: k_w4a16_dot2<TS, TY, MT, 2><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 3: k_w4a16_dot2<TS, TY, MT, 3><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    default: k_w4a16_dot2<TS, TY, MT, 4><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+  }
+}
+
+hipError_t launch_w4a16_dot2(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                             const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                             int g, void* y, int y_dtype, hipStream_t st) {
+  const dim3 grid((unsigned)((n + kRowsWg - 1) / kRowsWg));
+  const uint16_t* xb = (const uint16_t*)x;
+  const bool sh = sz_dtype == W4_F16, yf = y_dtype == W4_F32;
+  if (m == 1) {
+    if (sh && yf) dot2_go<_Float16, float, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+    else if (sh) dot2_go<_Float16, __bf16, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+    else if (yf) dot2_go<float, float, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+    else dot2_go<float, __bf16, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+  } else {
+    if (sh && yf) dot2_go<_Float16, float, 2>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+    else if (sh) dot2_go<_Float16, __bf16, 2>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+    else if (yf) dot2_go<float, float, 2>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+    else dot2_go<float, __bf16, 2>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,664 @@
+// Decode-time fused dequantize-matmul for 1 <= M <= 16 tokens (bf16 x),
+// groups that are multiples of 128 columns.  HBM-bound: the kernel exists to
+// stream the packed codes at full bandwidth.
+//
+// Math.  For a 128-column block b of weight row n (inside one group, scale s,
+// zero-point zp) and token m:
+//   sum_k x[m,k] * (q[n,k] - zp) * s
+//     = s * ( sum_k x[m,k] * (128 + q[n,k])  -  (128 + zp) * sum_k x[m,k] )
+// ("From Scratch: Building a GPTQ INT4 Quantizer in Pure Python", Step 4,
+// inside the product of "Building a From-Scratch Group-Wise INT4 Quantization
+// Layer for LLaMA Weights", Step 2).  128 + q is an exact bfloat16 whose low
+// mantissa bits are the code, so a nibble becomes an MFMA operand with one
+// byte permute and one and-or per pair of codes.  Both sums run on the bf16
+// MFMA unit (v_mfma_f32_16x16x32_bf16): the first against the codes, the
+// second against the constant -(128 + zp) of the row, into the same fp32
+// accumulator.  The block result is scaled by s with one FMA per output.
+//
+// Work layout.  A 256-lane workgroup owns 16 weight rows (one MFMA column
+// each) over all of K; its four waves split K into contiguous ranges and add
+// their 16x16 partial tiles through LDS at the end.  Lane l serves weight row
+// (l mod 16) and k-group (l div 16): per block it loads 16 bytes of packed
+// codes (32 consecutive columns), and, when token (l mod 16) < M, the 32
+// matching activations (64 bytes).  Packed loads for up to 8 blocks are in
+// flight per lane before the first MFMA.
+#include "w4_common.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+namespace {
+
+#ifndef W4_SKINNY_WAVES
+#define W4_SKINNY_WAVES 4
+#endif
+#ifndef W4_SKINNY_XDIST
+#define W4_SKINNY_XDIST 2
+#endif
+#ifndef W4_SKINNY_CHUNK
+#define W4_SKINNY_CHUNK 8
+#endif
+constexpr int kRows = 16;                // weight rows per workgroup
+constexpr int kWaves = W4_SKINNY_WAVES;  // waves per workgroup (K split)
+constexpr int kChunk = W4_SKINNY_CHUNK;  // 128-column blocks whose codes are loaded ahead
+constexpr int kXDist = W4_SKINNY_XDIST;  // activation prefetch distance (blocks)
+
+// (a & b) | c in one VALU instruction (v_and_or_b32).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// (q[2v], q[2v+1]) of a packed 8-code word as a bf16 pair (128 + q each).
+__device__ __forceinline__ uint32_t code_pair(uint32_t p, uint32_t p4, uint32_t v) {
+  // byte v of p holds codes 2v (low nibble) and 2v+1; byte v of p >> 4 holds
+  // code 2v+1 in its low nibble.  Bytes 1 and 3 of the result are zero.
+  const uint32_t sel = v | 0x0c00u | ((4u + v) << 16) | 0x0c000000u;
+  const uint32_t t = __builtin_amdgcn_perm(p4, p, sel);
+  return and_or(t, 0x000f000fu, 0x43004300u);
+}
+
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t p) {
+  const uint32_t p4 = p >> 4;
+  u32x4 r;
+  r.x = code_pair(p, p4, 0);
+  r.y = code_pair(p, p4, 1);
+  r.z = code_pair(p, p4, 2);
+  r.w = code_pair(p, p4, 3);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <typename TY>
+__device__ __forceinline__ void store_out(void* y, int64_t i, float v) {
+  if constexpr (sizeof(TY) == 4) {
+    ((float*)y)[i] = v;
+  } else {
+    ((uint16_t*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+}  // namespace
+
+// Raw (unconverted) scale / zero-point element of the storage dtype.
+template <typename TS> struct RawSZ;
+template <> struct RawSZ<_Float16> {
+  typedef uint16_t T;
+  __device__ static float scale(T v) { return (float)__builtin_bit_cast(_Float16, v); }
+  __device__ static uint32_t zero(T v) { return (uint32_t)(float)__builtin_bit_cast(_Float16, v); }
+};
+template <> struct RawSZ<float> {
+  typedef uint32_t T;
+  __device__ static float scale(T v) { return __uint_as_float(v); }
+  __device__ static uint32_t zero(T v) { return (uint32_t)__uint_as_float(v); }
+};
+
+// CH consecutive 128-column blocks starting at block c0, no branches: all
+// packed-code, scale and zero-point loads are issued first; activations are
+// prefetched two blocks ahead of the MFMAs that consume them.  Each block
+// accumulates into its own MFMA accumulator, so the block chains are
+// independent; the scales are applied after the last MFMA of the chunk.
+// gi(i) = group index of block c0 + i (precomputed by the caller).
+template <int CH, typename TS>
+__device__ __forceinline__ void skinny_chunk(const u32x4* __restrict__ wrow,
+                                             const u32x4* __restrict__ xrow,
+                                             const typename RawSZ<TS>::T* __restrict__ srow,
+                                             const typename RawSZ<TS>::T* __restrict__ zrow,
+                                             const int (&gi)[CH], int c0, f32x4& acc) {
+  typedef typename RawSZ<TS>::T R;
+  u32x4 wq[CH];
+  R sr[CH], zr[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) wq[i] = __builtin_nontemporal_load(wrow + 4 * (c0 + i));
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    sr[i] = srow[gi[i]];
+    zr[i] = zrow[gi[i]];
+  }
+  constexpr int D = CH < kXDist ? CH : kXDist;
+  u32x4 xa[D + 1][4];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xa[i][t] = xrow[16 * (c0 + i) + t];
+  // keep every load above in flight before any arithmetic (the scheduler
+  // would otherwise sink them next to their uses and serialize the latency)
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 gacc[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if (i + D < CH) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xa[(i + D) % (D + 1)][t] = xrow[16 * (c0 + i + D) + t];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint32_t zb = (0xc300u | RawSZ<TS>::zero(zr[i])) * 0x00010001u;  // bf16 pair -(128+zp)
+    const bf16x8 bz = __builtin_bit_cast(bf16x8, u32x4{zb, zb, zb, zb});
+    const uint32_t w4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+    gacc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, xa[i % (D + 1)][t]);
+      gacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, codes_to_bf16(w4[t]), gacc[i], 0, 0, 0);
+      gacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bz, gacc[i], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const float sc = RawSZ<TS>::scale(sr[i]);
+    acc.x = fmaf(sc, gacc[i].x, acc.x);
+    acc.y = fmaf(sc, gacc[i].y, acc.y);
+    acc.z = fmaf(sc, gacc[i].z, acc.z);
+    acc.w = fmaf(sc, gacc[i].w, acc.w);
+  }
+}
+
+// Group index of each block of a chunk: blocks per group is 1 for g = 128
+// (the common case, no arithmetic) and bpg otherwise.
+template <int CH, bool BPG1>
+__device__ __forceinline__ void chunk_groups(int c0, int bpg, int (&gi)[CH]) {
+  if (BPG1) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) gi[i] = c0 + i;
+  } else {
+    int q = c0 / bpg, r = c0 - q * bpg;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      gi[i] = q;
+      if (++r == bpg) { r = 0; ++q; }
+    }
+  }
+}
+
+template <int CH, typename TS, bool BPG1>
+__device__ __forceinline__ void run_chunk(const u32x4* wrow, const u32x4* xrow,
+                                          const typename RawSZ<TS>::T* srow,
+                                          const typename RawSZ<TS>::T* zrow, int bpg, int c0,
+                                          f32x4& acc) {
+  int gi[CH];
+  chunk_groups<CH, BPG1>(c0, bpg, gi);
+  skinny_chunk<CH, TS>(wrow, xrow, srow, zrow, gi, c0, acc);
+}
+
+template <typename TS, typename TY, bool BPG1>
+__global__ __launch_bounds__(64 * kWaves) void k_w4a16_skinny(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
+    void* __restrict__ y) {
+  typedef typename RawSZ<TS>::T R;
+  __shared__ f32x4 part[kWaves][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 15;     // weight row in the tile; token row of the x operand
+  const int kg = lane >> 4;    // 32-column group inside a 128-column block
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t n = (n0 + j < N) ? (n0 + j) : (N - 1);  // ragged tail: read a valid row
+
+  const int nblk = (int)(K / 128);
+  const int b0 = (wave * nblk) / kWaves;
+  const int b1 = ((wave + 1) * nblk) / kWaves;
+  const int64_t ng = K / g;
+  const int bpg = g / 128;  // 128-column blocks per group
+
+  const u32x4* wrow = (const u32x4*)(packed + n * (K / 2)) + kg;  // block b at + 4*b
+  // Operand rows m >= M read token 0 again: their results are never stored.
+  const int jx = j < M ? j : 0;
+  const u32x4* xrow = (const u32x4*)(x + (int64_t)jx * K) + kg * 4;  // block b at + 16*b
+  const R* srow = (const R*)scales + n * ng;
+  const R* zrow = (const R*)zeros + n * ng;
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int c0 = b0;
+  for (; c0 + kChunk <= b1; c0 += kChunk) run_chunk<kChunk, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc);
+  if (kChunk > 4 && c0 + 4 <= b1) { run_chunk<4, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc); c0 += 4; }
+  if (kChunk > 2 && c0 + 2 <= b1) { run_chunk<2, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc); c0 += 2; }
+  if (c0 < b1) run_chunk<1, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc);
+
+  // lane holds D[i][j] for token i = 4*kg + r, weight row j = lane mod 16
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 s = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f32x4 o = part[w][lane];
+      s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
+    }
+    if (n0 + j < N) {
+      const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        if (m < M) store_out<TY>(y, (int64_t)m * N + n0 + j, v[r]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel with the activations staged in LDS (used when M * K * 2 bytes
+// fits the LDS budget of 64 KB: M <= 4 at K = 4096, M = 1 at K = 8192).  Same math and work layout as
+// above, with two differences that cut registers and VALU work:
+//  * the block's codes are expanded in the order (0,4), (1,5), (2,6), (3,7)
+//    of each 8-code word -- seven instructions per word (shift + and-or) --
+//    and the activations are stored in LDS in that same order, so the MFMA
+//    still pairs every code with its own activation;
+//  * operands are read from LDS just before use (ds_read_b128), so no
+//    activation registers are held across blocks.
+// ---------------------------------------------------------------------------
+#ifndef W4_DECODE_LDS_BYTES
+#define W4_DECODE_LDS_BYTES 65536
+#endif
+constexpr int kDecodeLds = W4_DECODE_LDS_BYTES;
+
+// Codes 0..7 of a word as bf16 pairs (128+q) in the order (0,4),(1,5),(2,6),(3,7).
+__device__ __forceinline__ bf16x8 codes_to_bf16_interleaved(uint32_t p) {
+  u32x4 r;
+  r.x = and_or(p, 0x000f000fu, 0x43004300u);
+  r.y = and_or(p >> 4, 0x000f000fu, 0x43004300u);
+  r.z = and_or(p >> 8, 0x000f000fu, 0x43004300u);
+  r.w = and_or(p >> 12, 0x000f000fu, 0x43004300u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 8 bf16 activations (x0..x7 as 4 pairs) -> pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7).
+__device__ __forceinline__ u32x4 interleave8(u32x4 v) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // lo(v.x), lo(v.z)
+  r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // hi(v.x), hi(v.z)
+  r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+  return r;
+}
+
+// One chunk of CH blocks.  Loads are issued in the order scale/zero-point,
+// then codes, so that (vmcnt retires in order) block i waits only for its own
+// codes: the MFMAs of block i overlap the arrival of blocks i+1 .. CH-1.
+// MFMAs of CH consecutive blocks whose codes are already loaded (wq); block
+// i waits only for its own codes (vmcnt retires in order).  Scale and
+// zero-point of every block come from the LDS tile.
+template <int CH>
+__device__ __forceinline__ void decode_math(const u32x4 (&wq)[CH], const u32x4* __restrict__ xl,
+                                            const float* __restrict__ s_l,
+                                            const uint32_t* __restrict__ zb_l, int c0,
+                                            f32x4& acc) {
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const uint32_t zb = zb_l[c0 + i];
+    const bf16x8 bz = __builtin_bit_cast(bf16x8, u32x4{zb, zb, zb, zb});
+    const uint32_t w4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+    f32x4 ga = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, xl[16 * (c0 + i) + t]);
+      ga = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, codes_to_bf16_interleaved(w4[t]), ga, 0, 0, 0);
+      ga = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bz, ga, 0, 0, 0);
+    }
+    const float sc = s_l[c0 + i];
+    acc.x = fmaf(sc, ga.x, acc.x);
+    acc.y = fmaf(sc, ga.y, acc.y);
+    acc.z = fmaf(sc, ga.z, acc.z);
+    acc.w = fmaf(sc, ga.w, acc.w);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void decode_loads(const u32x4* __restrict__ wrow, int c0, u32x4 (&wq)[CH]) {
+#pragma unroll
+  for (int i = 0; i < CH; ++i) wq[i] = wrow[4 * (c0 + i)];
+}
+
+// c0: absolute block (codes in memory); r0: block relative to the wave's
+// first block (LDS slices).
+template <int CH>
+__device__ __forceinline__ void decode_blocks(const u32x4* __restrict__ wrow,
+                                              const u32x4* __restrict__ xl,
+                                              const float* __restrict__ s_l,
+                                              const uint32_t* __restrict__ zb_l, int c0, int r0,
+                                              f32x4& acc) {
+  u32x4 wq[CH];
+  decode_loads<CH>(wrow, c0, wq);
+  __builtin_amdgcn_sched_barrier(0);
+  decode_math<CH>(wq, xl, s_l, zb_l, r0, acc);
+}
+
+// LDS layout of the decode kernel (dynamic shared memory), one private
+// region per wave -- staging needs no workgroup barrier:
+//   sc[16][nblk]  float   scale of (tile row, block), absolute block index
+//   zb[16][nblk]  uint32  bf16 pair -(128 + zp) of (tile row, block)
+//   x [M][nw*16]  16-byte groups of the wave's activations, interleaved order
+// followed by part[WAVES][64] f32x4 for the final cross-wave sum.  A wave
+// fills only the blocks it uses, except on the fast path (one block per
+// group) where it stores the whole scale / zero-point tile unconditionally.
+__host__ __device__ inline int64_t decode_wave_blocks(int64_t k, int waves) {
+  const int64_t nblk = k / 128;
+  return (nblk + waves - 1) / waves;  // upper bound of blocks per wave
+}
+__host__ __device__ inline int64_t decode_wave_bytes(int64_t m, int64_t k, int waves) {
+  return 16 * (k / 128) * 8 + m * decode_wave_blocks(k, waves) * 256;
+}
+size_t decode_lds_bytes(int64_t m, int64_t k, int waves) {
+  return (size_t)(waves * decode_wave_bytes(m, k, waves) + waves * 64 * 16);
+}
+
+// Staging of one wave: XPER 16-byte activation loads and SPER 16-byte loads
+// of each of the scale / zero-point tiles per lane (compile-time, exact), or
+// 0 for element loops.
+template <typename TS, typename TY, int WAVES, int XPER, int SPER>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
+    void* __restrict__ y) {
+  typedef typename RawSZ<TS>::T R;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int j = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t n = (n0 + j < N) ? (n0 + j) : (N - 1);
+  const int nblk = (int)(K / 128);
+  const int ng = (int)(K / g);
+  const int bpg = g / 128;
+  const int b0 = (wave * nblk) / WAVES;
+  const int b1 = ((wave + 1) * nblk) / WAVES;
+  const int nwb = b1 - b0;                                  // this wave's blocks
+  const int nw = (int)decode_wave_blocks(K, WAVES);         // region stride
+  unsigned char* base = lds + (int64_t)wave * decode_wave_bytes(M, K, WAVES);
+  float* sc_l = (float*)base;                               // [16][nblk]
+  uint32_t* zb_l = (uint32_t*)(base + 16 * nblk * 4);       // [16][nblk]
+  u32x4* xs_l = (u32x4*)(base + 16 * nblk * 8);             // [M][nw*16]
+  f32x4* part = (f32x4*)(lds + (int64_t)WAVES * decode_wave_bytes(M, K, WAVES));
+
+  const R* sg = (const R*)scales;
+  const R* zg = (const R*)zeros;
+  const u32x4* xg = (const u32x4*)x;
+  const int64_t tile0 = n0 * ng;                 // first scale element of the tile
+  const int64_t last = N * ng - 1;               // last valid scale element
+  const u32x4* wrow = (const u32x4*)(packed + n * (K / 2)) + kg;
+
+  // ---- 1. staging loads, 2. codes of the first chunk -----------------------
+  constexpr bool fast = XPER > 0;
+  constexpr int kXP = XPER > 0 ? XPER : 1, kSP = SPER > 0 ? SPER : 1;
+  u32x4 xv[kXP], sv[kSP], zv[kSP];
+  if (fast) {
+    // activations: groups (m, b0*16 .. b1*16) of every token m < M
+#pragma unroll
+    for (int r = 0; r < kXP; ++r) {
+      const int i = lane + 64 * r;               // group index inside the slice
+      const int m = i / (nwb * 16), c = i - m * (nwb * 16);
+      xv[r] = xg[(int64_t)m * (K / 8) + b0 * 16 + c];
+    }
+    // scale / zero-point tile: 16 rows x ng elements, contiguous in memory
+    constexpr int per16 = 16 / (int)sizeof(R);   // elements per 16-byte load
+#pragma unroll
+    for (int r = 0; r < kSP; ++r) {
+      int64_t e = tile0 + (int64_t)(lane + 64 * r) * per16;
+      e = e + per16 - 1 <= last ? e : last + 1 - per16;  // ragged last tile: stay in bounds
+      sv[r] = *(const u32x4*)(sg + e);
+      zv[r] = *(const u32x4*)(zg + e);
+    }
+  }
+  const bool first_full = nwb >= kChunk;
+  u32x4 wq0[kChunk];
+  if (first_full) decode_loads<kChunk>(wrow, b0, wq0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. LDS stores of the wave's slices (no workgroup barrier) -----------
+  if (fast) {
+#pragma unroll
+    for (int r = 0; r < kXP; ++r) xs_l[lane + 64 * r] = interleave8(xv[r]);
+    constexpr int per16 = 16 / (int)sizeof(R);
+    // the fast path has g == 128 (group == block == tile column): store the
+    // whole tile, every lane, no conditions
+#pragma unroll
+    for (int r = 0; r < kSP; ++r) {
+      const R* se = (const R*)&sv[r];
+      const R* ze = (const R*)&zv[r];
+      const int e0 = (lane + 64 * r) * per16;
+#pragma unroll
+      for (int t = 0; t < per16; ++t) {
+        sc_l[e0 + t] = RawSZ<TS>::scale(se[t]);
+        zb_l[e0 + t] = (0xc300u | RawSZ<TS>::zero(ze[t])) * 0x00010001u;
+      }
+    }
+  } else {
+    for (int i = lane; i < M * nwb * 16; i += 64) {
+      const int m = i / (nwb * 16), c = i - m * (nwb * 16);
+      xs_l[i] = interleave8(xg[(int64_t)m * (K / 8) + b0 * 16 + c]);
+    }
+    for (int e = lane; e < 16 * nwb; e += 64) {
+      const int row = e / nwb, b = b0 + (e - row * nwb);
+      int64_t ge = (n0 + row < N ? n0 + row : N - 1) * ng + b / bpg;
+      sc_l[row * nblk + b] = RawSZ<TS>::scale(sg[ge]);
+      zb_l[row * nblk + b] = (0xc300u | RawSZ<TS>::zero(zg[ge])) * 0x00010001u;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS stores are done
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- 4. MFMAs over the wave's blocks (block-relative LDS indices) --------
+  const int jx = j < M ? j : 0;  // operand rows m >= M repeat token 0 (never stored)
+  const u32x4* xl = xs_l + jx * (nwb * 16) + kg * 4;  // indexed by block relative to b0
+  const float* s_l = sc_l + j * nblk + b0;   // indexed by block relative to b0
+  const uint32_t* z_l = zb_l + j * nblk + b0;
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int c0 = b0;
+  if (first_full) {
+    decode_math<kChunk>(wq0, xl, s_l, z_l, 0, acc);
+    c0 += kChunk;
+  }
+  for (; c0 + kChunk <= b1; c0 += kChunk) decode_blocks<kChunk>(wrow, xl, s_l, z_l, c0, c0 - b0, acc);
+  if (kChunk > 4 && c0 + 4 <= b1) { decode_blocks<4>(wrow, xl, s_l, z_l, c0, c0 - b0, acc); c0 += 4; }
+  if (kChunk > 2 && c0 + 2 <= b1) { decode_blocks<2>(wrow, xl, s_l, z_l, c0, c0 - b0, acc); c0 += 2; }
+  if (c0 < b1) decode_blocks<1>(wrow, xl, s_l, z_l, c0, c0 - b0, acc);
+
+  // ---- 5. cross-wave sum of the partial tiles, store -----------------------
+  part[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 sum = part[lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      const f32x4 o = part[w * 64 + lane];
+      sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
+    }
+    if (n0 + j < N) {
+      const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        if (m < M) store_out<TY>(y, (int64_t)m * N + n0 + j, v[r]);
+      }
+    }
+  }
+}
+
+// Fast decode kernel for the common shapes: one block per group (g = 128),
+// every wave owns exactly NWB blocks (NWB % 8 == 0), the activation slice is
+// XPER 16-byte loads per lane and the scale / zero-point tile SPER 16-byte
+// loads per lane.  Everything is compile-time, so every load is
+// straight-line code: staging loads, then the codes of the first 8 blocks,
+// then the LDS stores while the codes are in flight.
+template <typename TS, typename TY, int WAVES, int XPER, int SPER, int NWB>
+__global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode_fast(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N,
+    void* __restrict__ y) {
+  typedef typename RawSZ<TS>::T R;
+  static_assert(NWB % kChunk == 0, "whole chunks per wave");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
+  const int64_t n = (n0 + j < N) ? (n0 + j) : (N - 1);
+  const int nblk = NWB * WAVES;  // == K / 128 == number of groups
+  const int b0 = wave * NWB;
+  const int64_t wbytes = 16 * (int64_t)nblk * 8 + (int64_t)M * NWB * 256;
+  unsigned char* base = lds + wave * wbytes;
+  float* sc_l = (float*)base;                          // [16][nblk]
+  uint32_t* zb_l = (uint32_t*)(base + 16 * nblk * 4);  // [16][nblk]
+  u32x4* xs_l = (u32x4*)(base + 16 * nblk * 8);        // [M][NWB*16]
+  f32x4* part = (f32x4*)(lds + WAVES * wbytes);
+
+  const R* sg = (const R*)scales;
+  const R* zg = (const R*)zeros;
+  const u32x4* xg = (const u32x4*)x;
+  const u32x4* wrow = (const u32x4*)(packed + n * (K / 2)) + kg;
+  constexpr int per16 = 16 / (int)sizeof(R);
+  const int64_t tile0 = n0 * nblk;
+  const int64_t last = N * nblk - 1;
+
+  u32x4 xv[XPER], sv[SPER], zv[SPER];
+#pragma unroll
+  for (int r = 0; r < XPER; ++r) {
+    const int i = lane + 64 * r;  // group inside the wave's slice: token i / (NWB*16)
+    const int m = i / (NWB * 16), c = i - m * (NWB * 16);
+    xv[r] = xg[(int64_t)m * (K / 8) + b0 * 16 + c];
+  }
+#pragma unroll
+  for (int r = 0; r < SPER; ++r) {
+    int64_t e = tile0 + (int64_t)(lane + 64 * r) * per16;
+    e = e + per16 - 1 <= last ? e : last + 1 - per16;  // ragged last tile: stay in bounds
+    sv[r] = *(const u32x4*)(sg + e);
+    zv[r] = *(const u32x4*)(zg + e);
+  }
+  u32x4 wq0[kChunk];
+  decode_loads<kChunk>(wrow, b0, wq0);
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int r = 0; r < XPER; ++r) xs_l[lane + 64 * r] = interleave8(xv[r]);
+#pragma unroll
+  for (int r = 0; r < SPER; ++r) {
+    const R* se = (const R*)&sv[r];
+    const R* ze = (const R*)&zv[r];
+    const int e0 = (lane + 64 * r) * per16;
+#pragma unroll
+    for (int t = 0; t < per16; ++t) {
+      sc_l[e0 + t] = RawSZ<TS>::scale(se[t]);
+      zb_l[e0 + t] = (0xc300u | RawSZ<TS>::zero(ze[t])) * 0x00010001u;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS stores are done
+  __builtin_amdgcn_wave_barrier();
+
+  const int jx = j < M ? j : 0;  // operand rows m >= M repeat token 0 (never stored)
+  const u32x4* xl = xs_l + jx * (NWB * 16) + kg * 4;
+  const float* s_l = sc_l + j * nblk + b0;
+  const uint32_t* z_l = zb_l + j * nblk + b0;
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  decode_math<kChunk>(wq0, xl, s_l, z_l, 0, acc);
+#pragma unroll
+  for (int c = kChunk; c < NWB; c += kChunk) decode_blocks<kChunk>(wrow, xl, s_l, z_l, b0 + c, c, acc);
+
+  part[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 sum = part[lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) {
+      const f32x4 o = part[w * 64 + lane];
+      sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
+    }
+    if (n0 + j < N) {
+      const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kg + r;
+        if (m < M) store_out<TY>(y, (int64_t)m * N + n0 + j, v[r]);
+      }
+    }
+  }
+}
+
+#ifndef W4_DECODE_WAVES
+#define W4_DECODE_WAVES 4
+#endif
+
+bool decode_lds_fits(int64_t m, int64_t k) {
+  return decode_lds_bytes(m, k, W4_DECODE_WAVES) <= (size_t)kDecodeLds;
+}
+
+template <typename TS, typename TY>
+static void decode_go(dim3 grid, hipStream_t st, const uint16_t* x, int M, int64_t k,
+                      const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
+                      int g, void* y) {
+  constexpr int W = W4_DECODE_WAVES;
+  const size_t lds = decode_lds_bytes(M, k, W);
+  const int64_t nblk = k / 128, ng = k / g;
+  // exact straight-line staging when every wave has the same block count,
+  // its activation slice is a whole number of 64-lane rounds and the
+  // scale / zero-point tile is a whole number of 1 KB rounds
+  const bool even = nblk % W == 0;
+  const int64_t xgroups = M * (nblk / W) * 16;
+  const int64_t tile_bytes = 16 * ng * (int64_t)sizeof(TS);
+  const bool bpg1 = (g == 128);
+  int xper = 0, sper = 0;
+  if (even && bpg1 && xgroups % 64 == 0 && tile_bytes % 1024 == 0) {
+    xper = (int)(xgroups / 64);
+    sper = (int)(tile_bytes / 1024);
+  }
+#define W4_DEC(XP, SP) \
+  k_w4a16_decode<TS, TY, W, XP, SP><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, g, y)
+#define W4_DEC_FAST(XP, SP, NWB) \
+  k_w4a16_decode_fast<TS, TY, W, XP, SP, NWB><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, y)
+  const int64_t nwb = nblk / W;
+  if (xper == 2 && sper == 1 && nwb == 8) W4_DEC_FAST(2, 1, 8);        // M = 1, K = 4096, fp16 s/z
+  else if (xper == 4 && sper == 2 && nwb == 16) W4_DEC_FAST(4, 2, 16); // M = 1, K = 8192, fp16 s/z
+  else if (xper == 4 && sper == 1 && nwb == 8) W4_DEC_FAST(4, 1, 8);   // M = 2, K = 4096
+  else if (xper == 8 && sper == 1 && nwb == 8) W4_DEC_FAST(8, 1, 8);   // M = 4, K = 4096
+  else if (xper == 2 && sper == 2 && nwb == 8) W4_DEC_FAST(2, 2, 8);   // M = 1, K = 4096, fp32 s/z
+  else W4_DEC(0, 0);
+#undef W4_DEC_FAST
+#undef W4_DEC
+}
+
+hipError_t launch_w4a16_decode(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                               const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                               int g, void* y, int y_dtype, hipStream_t st) {
+  const dim3 grid((unsigned)((n + kRows - 1) / kRows));
+  const uint16_t* xb = (const uint16_t*)x;
+  const int M = (int)m;
+  if (sz_dtype == W4_F16) {
+    if (y_dtype == W4_F32) decode_go<_Float16, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+    else decode_go<_Float16, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+  } else {
+    if (y_dtype == W4_F32) decode_go<float, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+    else decode_go<float, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+  }
+  return hipGetLastError();
+}
+
+template <typename TS, typename TY>
+static void skinny_go(dim3 grid, hipStream_t st, const uint16_t* x, int M, int64_t k,
+                      const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
+                      int g, void* y) {
+  if (g == 128)
+    k_w4a16_skinny<TS, TY, true><<<grid, 64 * kWaves, 0, st>>>(x, M, k, packed, scales, zeros, n, g, y);
+  else
+    k_w4a16_skinny<TS, TY, false><<<grid, 64 * kWaves, 0, st>>>(x, M, k, packed, scales, zeros, n, g, y);
+}
+
+hipError_t launch_w4a16_skinny(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                               const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                               int g, void* y, int y_dtype, hipStream_t st) {
+  const dim3 grid((unsigned)((n + kRows - 1) / kRows));
+  const uint16_t* xb = (const uint16_t*)x;
+  const int M = (int)m;
+  if (sz_dtype == W4_F16) {
+    if (y_dtype == W4_F32) skinny_go<_Float16, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+    else skinny_go<_Float16, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+  } else {
+    if (y_dtype == W4_F32) skinny_go<float, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+    else skinny_go<float, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4
