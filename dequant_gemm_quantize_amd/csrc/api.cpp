@@ -164,6 +164,10 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
     return hip_status(w4::launch_w4a16_skinny(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
                       fn);
+  if (x_dtype == W4_BF16 && w4::gemm_fits(m, k, group_size))
+    return hip_status(w4::launch_w4a16_gemm(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                            group_size, y, y_dtype, stream),
+                      fn);
   return hip_status(w4::launch_w4a16_generic(x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
                                              group_size, y, y_dtype, stream),
                     fn);

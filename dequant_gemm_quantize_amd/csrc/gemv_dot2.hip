@@ -12,12 +12,12 @@
 // with a shift and one and-or; v_dot2_f32_bf16 multiplies two such codes by
 // two activations and accumulates in fp32.
 //
-// Work layout.  A 256-lane workgroup owns 16 weight rows; wave w owns rows
-// 4w .. 4w+3 over all of K.  Lane l covers the 16-byte chunks l, l+64, ...
+// Work layout.  A 256-lane workgroup owns 4 * RW weight rows; wave w owns
+// rows RW*w .. RW*w + RW-1 over all of K.  Lane l covers the 16-byte chunks l, l+64, ...
 // of a row (32 columns each), so every load instruction reads 1 KB of one
 // row contiguously.  The activations of the lane's columns are read once
 // into registers (through LDS, staged by the workgroup) and reused for the
-// wave's four rows; the chunk sums xs are formed once as well.  Each row's
+// wave's rows; the chunk sums xs are formed once as well.  Each row's
 // 64 partial sums are added with DPP row operations.
 #include "w4_common.h"
 #include "w4_internal.h"
@@ -26,8 +26,11 @@ namespace w4 {
 
 namespace {
 
-constexpr int kRowsWg = 16;    // weight rows per workgroup
-constexpr int kRowsWave = 4;   // weight rows per wave
+#ifndef W4_DOT2_RW
+#define W4_DOT2_RW 4
+#endif
+constexpr int kRowsWave = W4_DOT2_RW;    // weight rows per wave
+constexpr int kRowsWg = 4 * kRowsWave;   // weight rows per workgroup (4 waves)
 constexpr int kMaxCh = 4;      // 16-byte chunks per lane and row (K <= 64 * 4 * 32 = 8192)
 
 __device__ __forceinline__ uint32_t and_or2(uint32_t a, uint32_t b, uint32_t c) {
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
     xv[r] = xg[i < xgroups ? i : xgroups - 1];
   }
   const int tile = kRowsWg * ng;  // <= 16 * 64 elements for K <= 8192, g >= 128
-  constexpr int SPER = 4;
+  constexpr int SPER = (kRowsWg * 64 + 255) / 256;
   typedef typename SZ<TS>::T R;
   R sv[SPER], zv[SPER];
 #pragma unroll
@@ -176,9 +179,10 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
         uint32_t o[4];
         interleave(v, o);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) xa[m][c][4 * q + t] = o[t];
-        s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) +
-             bf16_hi(v.z) + bf16_lo(v.w) + bf16_hi(v.w);
+        for (int t = 0; t < 4; ++t) {
+          xa[m][c][4 * q + t] = o[t];
+          s = dot2(o[t], 0x3f803f80u, s);  // + x_a * 1.0 + x_b * 1.0
+        }
       }
       xs[m][c] = s;
     }
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
 
 size_t dot2_lds_bytes(int64_t m, int64_t k, int g) {
   const int64_t xper = (m * k / 8 + 255) / 256;
-  return (size_t)(xper * 256 * 16 + 4 * 256 * 8);
+  return (size_t)(xper * 256 * 16 + ((kRowsWg * 64 + 255) / 256) * 256 * 8);
 }
 
 bool dot2_fits(int64_t m, int64_t k, int g) {
