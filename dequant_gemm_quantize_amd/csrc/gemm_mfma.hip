@@ -10,13 +10,17 @@
 // activation tile.  No dequantized matrix ever reaches memory.
 //
 // Tiling.  Workgroup tile 256 (M) x 128 (N), K in steps of 64, both operand
-// tiles double-buffered in LDS (rows padded by 16 bytes).  Four waves in a
-// 2 x 2 arrangement, each owning a 128 x 64 block of the output: 4 x 2 MFMA
-// tiles of 32 x 32, 128 fp32 accumulators per lane.  The next K step's
-// global loads are in flight while the current one runs on the MFMA units.
+// tiles double-buffered in LDS (rows padded by 16 bytes).  Eight waves (two
+// per SIMD: a wave alone cannot pull LDS fast enough to feed its MFMAs) in a
+// 4 x 2 arrangement, each owning a 64 x 64 block of the output: 2 x 2 MFMA
+// tiles of 32 x 32, 64 fp32 accumulators per lane.  The global loads of the
+// following K steps are in flight (held in registers, W4_GEMM_DEPTH steps
+// deep) while the current one runs on the MFMA units.
 // Tiles are numbered so that consecutive workgroups (which the dispatcher
 // spreads over the 8 XCDs) share an N block and each XCD keeps working on
 // the same M block of x, which then stays in that XCD's L2.
+#include <type_traits>
+
 #include "w4_common.h"
 #include "w4_internal.h"
 
@@ -24,6 +28,9 @@ namespace w4 {
 
 namespace {
 
+#ifndef W4_GEMM_DEPTH
+#define W4_GEMM_DEPTH 4
+#endif
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int LDS_ROW = BK + 8;  // bf16 elements per LDS row (+16 bytes of padding)
 constexpr int A_STAGE = BM * LDS_ROW;
@@ -72,7 +79,7 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v) {
 }  // namespace
 
 template <typename TS, typename TY>
-__global__ __launch_bounds__(256, 1) void k_w4a16_gemm(
+__global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
     void* __restrict__ y, int tiles_m, int tiles_n) {
@@ -97,95 +104,128 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*128, cols wn*64
+  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*64, cols wn*64
 
   // ---- global -> register assignment ----------------------------------------
-  // x: 8 rounds of 32 rows; lane (t & 7) takes 16 bytes of a row's 128.
+  // x: 4 rounds of 64 rows; lane (t & 7) takes 16 bytes of a row's 128.
   const int xr = tid >> 3, xc = tid & 7;
-  const u32x4* xp[8];
+  const uint16_t* xt = x + m0 * K;  // tile base (uniform); per-lane offsets below
+  int xo[4];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    int64_t row = m0 + xr + 32 * r;
+  for (int r = 0; r < 4; ++r) {
+    int64_t row = m0 + xr + 64 * r;
     row = row < M ? row : M - 1;
-    xp[r] = (const u32x4*)(x + row * K) + xc;  // + 8 * kstep
+    xo[r] = (int)((row - m0) * K) + 8 * xc;  // elements, + 64 * kstep
   }
-  // W: 2 lanes per row, 16 bytes (32 codes) each.
-  const int wr = tid >> 1, wh = tid & 1;
+  // W: 4 lanes per row, 8 bytes (16 codes) each.
+  const int wr = tid >> 2, wq4 = tid & 3;
   int64_t wrow = n0 + wr;
   wrow = wrow < N ? wrow : N - 1;
-  const u32x4* wp = (const u32x4*)(packed + wrow * (K / 2)) + wh;  // + 2 * kstep
+  const uint32_t* wp = (const uint32_t*)(packed + wrow * (K / 2)) + 2 * wq4;  // + 8 * kstep
   const int64_t ng = K / g;
   const R* sp = (const R*)scales + wrow * ng;
   const R* zp = (const R*)zeros + wrow * ng;
 
+  // Global data runs D K-steps ahead of the MFMAs, in D register stages
+  // (stage = K-step mod D): loads for step ks + D are issued while step ks
+  // computes, and step ks + 1 is dequantized into the other LDS buffer after
+  // it.  Every wait is then for loads issued D - 1 steps earlier.
+  constexpr int D = W4_GEMM_DEPTH;
   const int nks = (int)(K / BK);
-  u32x4 xv[8], wv;
-  R sv, zv;
-  auto gload = [&](int ks) {
+  u32x4 xv[D][4];
+  u32x2 wv[D];
+  R sv[D], zv[D];
+  // Loads past the last K step are clamped to it (a few redundant loads)
+  // so that the main loop has no conditional loads: the compiler can then
+  // wait for exactly the stage it needs instead of for every load.
+  auto gload = [&](int ks, auto stage) {
+    constexpr int u = decltype(stage)::value;
+    ks = ks < nks ? ks : nks - 1;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) xv[r] = xp[r][8 * ks];
-    wv = wp[2 * ks];
-    const int gi = (ks * BK + 32 * wh) / g;
-    sv = sp[gi];
-    zv = zp[gi];
+    for (int r = 0; r < 4; ++r) xv[u][r] = *(const u32x4*)(xt + xo[r] + 64 * ks);
+    wv[u] = *(const u32x2*)(wp + 8 * ks);
+    const int gi = (ks * BK + 16 * wq4) / g;
+    sv[u] = sp[gi];
+    zv[u] = zp[gi];
   };
-  auto lstore = [&](int stage) {
-    uint16_t* a = sA + stage * A_STAGE;
+  auto lstore = [&](int lstage, auto stage) {
+    constexpr int u = decltype(stage)::value;
+    uint16_t* a = sA + lstage * A_STAGE;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) *(u32x4*)(a + (xr + 32 * r) * LDS_ROW + 8 * xc) = xv[r];
-    const float s = GS<TS>::f(sv);
-    const float b = -GS<TS>::f(zv) * s;
-    uint16_t* bp = sB + stage * B_STAGE + wr * LDS_ROW + 32 * wh;
-    *(u32x4*)(bp + 0) = dequant8(wv.x, s, b);
-    *(u32x4*)(bp + 8) = dequant8(wv.y, s, b);
-    *(u32x4*)(bp + 16) = dequant8(wv.z, s, b);
-    *(u32x4*)(bp + 24) = dequant8(wv.w, s, b);
+    for (int r = 0; r < 4; ++r) *(u32x4*)(a + (xr + 64 * r) * LDS_ROW + 8 * xc) = xv[u][r];
+    const float s = GS<TS>::f(sv[u]);
+    const float b = -GS<TS>::f(zv[u]) * s;
+    uint16_t* bp = sB + lstage * B_STAGE + wr * LDS_ROW + 16 * wq4;
+    *(u32x4*)(bp + 0) = dequant8(wv[u].x, s, b);
+    *(u32x4*)(bp + 8) = dequant8(wv[u].y, s, b);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
   const int l32 = lane & 31, lk = 8 * (lane >> 5);
-  for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < nks) gload(ks + 1);
-    const uint16_t* a = sA + cur * A_STAGE + (wm * 128 + l32) * LDS_ROW + lk;
-    const uint16_t* b = sB + cur * B_STAGE + (wn * 64 + l32) * LDS_ROW + lk;
+  auto mma = [&](int lstage) {
+    const uint16_t* a = sA + lstage * A_STAGE + (wm * 64 + l32) * LDS_ROW + lk;
+    const uint16_t* b = sB + lstage * B_STAGE + (wn * 64 + l32) * LDS_ROW + lk;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[4], bfr[2];
+      bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(a + 32 * i * LDS_ROW + 16 * kk);
+      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(a + 32 * i * LDS_ROW + 16 * kk);
 #pragma unroll
       for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)(b + 32 * j * LDS_ROW + 16 * kk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < nks) lstore(cur ^ 1);
+  };
+
+  // prologue: steps 0 .. D-1 in flight, step 0 in LDS buffer 0
+  gload(0, std::integral_constant<int, 0>{});
+  if constexpr (D > 1) gload(1, std::integral_constant<int, 1 % D>{});
+  if constexpr (D > 2) gload(2, std::integral_constant<int, 2 % D>{});
+  if constexpr (D > 3) gload(3, std::integral_constant<int, 3 % D>{});
+  lstore(0, std::integral_constant<int, 0>{});
+  __syncthreads();
+
+  // One K step, unconditional: loads for ks + D, MFMAs on buffer ks & 1,
+  // dequantize step ks + 1 into the other buffer (past the end this writes
+  // the idle buffer, which is never read), barrier.
+  auto step = [&](int ks, auto stage) {
+    constexpr int u = decltype(stage)::value;  // ks mod D
+    gload(ks + D, stage);  // reuses register stage u: step ks is already in LDS
+    mma(ks & 1);
+    lstore((ks + 1) & 1, std::integral_constant<int, (u + 1) % D>{});
     __syncthreads();
+  };
+  const int nmain = nks - nks % D;
+  for (int ks = 0; ks < nmain; ks += D) {
+    step(ks, std::integral_constant<int, 0>{});
+    if constexpr (D > 1) step(ks + 1, std::integral_constant<int, 1 % D>{});
+    if constexpr (D > 2) step(ks + 2, std::integral_constant<int, 2 % D>{});
+    if constexpr (D > 3) step(ks + 3, std::integral_constant<int, 3 % D>{});
   }
+  // tail: the remaining nks % D steps (register stage of step ks is ks mod D)
+  if (nmain < nks) step(nmain, std::integral_constant<int, 0>{});
+  if constexpr (D > 1) if (nmain + 1 < nks) step(nmain + 1, std::integral_constant<int, 1 % D>{});
+  if constexpr (D > 2) if (nmain + 2 < nks) step(nmain + 2, std::integral_constant<int, 2 % D>{});
 
   // ---- epilogue: lane holds rows 8(r/4) + 4(lane/32) + r%4, column lane%32 --
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t n = n0 + wn * 64 + 32 * j + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m < M && n < N) store1<TY>(y, m * N + n, acc[i][j][r]);
       }
     }
@@ -206,7 +246,7 @@ static hipError_t gemm_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t
   }
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  k_w4a16_gemm<TS, TY><<<grid, 256, kGemmLds, st>>>(x, m, k, packed, scales, zeros, n, g, y,
+  k_w4a16_gemm<TS, TY><<<grid, 512, kGemmLds, st>>>(x, m, k, packed, scales, zeros, n, g, y,
                                                    tiles_m, tiles_n);
   return hipGetLastError();
 }
