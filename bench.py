@@ -53,10 +53,15 @@ def quant_bytes(n, k, g, w_bytes=2, sz_bytes=2):
     return n * k * w_bytes + n * k // 2 + 2 * n * (k // g) * sz_bytes
 
 
-def src_hash():
+# Sources that decide which kernel runs the [11008,4096] decode product and
+# what it does; stored byte counters are used only while these are unchanged.
+DECODE_SOURCES = ("api.cpp", "w4_common.h", "w4_internal.h", "gemv_dot2.hip")
+
+
+def src_hash(files=DECODE_SOURCES):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dequant_gemm_quantize_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -72,6 +77,12 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="skip the extra per-step measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
+    ap.add_argument("--kernel", choices=("decode_wb", "copy"), default=None,
+                    help="launch only this kernel --launches times, eagerly, for counter runs: "
+                         "decode_wb = the [11008,4096] decode product on rotated weights, "
+                         "copy = a plain device copy of --copy-mib MiB (calibrates byte counters)")
+    ap.add_argument("--launches", type=int, default=40)
+    ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -133,6 +144,9 @@ def main(argv=None):
         e1.synchronize()
         del graphs
         return e0.elapsed_time(e1) / 1e3 / iters
+
+    if args.kernel is not None:
+        return kernel_only(args, w4, WL, torch, dev, to_dev, log)
 
     g = 128
     log("generating Llama-7B decode weights")
@@ -308,6 +322,39 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
     sec = time_region(lambda i: w4.w4a16_matmul(x, p, s, z, 32, out=y), reps)
     out["single_layer_fp32_256"] = {"us": round(sec * 1e6, 2)}
     return out
+
+
+def kernel_only(args, w4, WL, torch, dev, to_dev, log):
+    """Eager launches of one kernel and nothing else of note, so a counter
+    run's per-dispatch records are easy to pick out."""
+    n_launch = max(1, args.launches)
+    if args.kernel == "copy":
+        nbytes = args.copy_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(n_launch):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": "copy", "launches": n_launch, "read_bytes": nbytes,
+                          "write_bytes": nbytes}), flush=True)
+        return 0
+    g, n, k = 128, 11008, 4096
+    wt = to_dev(WL.weight("Wb"))
+    q = w4.quantize_pack_int4(wt, g, torch.float16)
+    del wt
+    R = max(1, args.rotate)
+    copies = [tuple(a.clone() for a in q) for _ in range(R)]
+    x = to_dev(WL.activation(2, 1, k))
+    y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"decode_wb: {n_launch} launches over {R} weight copies")
+    for i in range(n_launch):
+        w4.w4a16_matmul(x, *copies[i % R], g, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "decode_wb", "launches": n_launch,
+                      "bytes_per_launch": w4a16_bytes(1, n, k, g)}), flush=True)
+    return 0
 
 
 def cpu_baseline(args, WL, np, log, wa, wb):
