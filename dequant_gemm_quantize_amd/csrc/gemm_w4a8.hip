@@ -1,0 +1,265 @@
+// Fused W4A8 GEMM for many tokens: INT8 activations (per-token scale) times
+// INT4 weights (per-group scale and zero-point) on the int8 MFMA units.
+//
+// Math ("Hands-on Build Guide: Group-wise INT4 Weight-only Quantization with
+// Per-channel Scales", Step 5, with the weight dequantization of "From
+// Scratch: Building a GPTQ INT4 Quantizer in Pure Python", Step 4):
+//   y[m, n] = s_a[m] * sum_g s[n, g] * sum_{k in g} xq[m, k] * (q[n, k] - zp[n, g]).
+// The inner sums are exact in int32 (|xq| <= 128, |q - zp| <= 15).  Each
+// K step of 128 columns lies inside one group (group sizes are multiples of
+// 128), so the int32 accumulators of a step are converted to fp32 and added
+// into the fp32 accumulators with that group's scale; the token scale is
+// applied once at the end.
+//
+// Tiling.  Workgroup tile 256 (M) x 128 (N), K steps of 128, eight waves in
+// a 4 x 2 arrangement, each a 64 x 64 output block (2 x 2 tiles of
+// v_mfma_i32_32x32x32_i8).  The weight tile is turned into int8 (q - zp) once
+// per workgroup while it is written to LDS; the activation tile is copied as
+// is.  Both are double-buffered in LDS; the global loads of x run one K step
+// ahead and those of the weights two, held in registers.
+#include <type_traits>
+
+#include "w4_common.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int ROW = BK + 16;            // bytes per LDS row (+16 bytes of padding)
+constexpr int A_STAGE = BM * ROW;       // bytes
+constexpr int B_STAGE = BN * ROW;       // bytes
+constexpr int S_STAGE = BN * 4;         // fp32 group scales of the tile's rows
+constexpr size_t kW4a8Lds = (size_t)2 * (A_STAGE + B_STAGE + S_STAGE);
+
+template <typename TS> struct G8;
+template <> struct G8<_Float16> {
+  typedef uint16_t T;
+  __device__ static float f(T v) { return (float)__builtin_bit_cast(_Float16, v); }
+};
+template <> struct G8<float> {
+  typedef uint32_t T;
+  __device__ static float f(T v) { return __uint_as_float(v); }
+};
+
+// 8 codes of a packed word -> 8 int8 values q - zp in column order, given
+// c = 0x80808080 - zp * 0x01010101: per byte q + 128 - zp lies in [113, 143],
+// so the add has no carries, and flipping bit 7 turns it into the two's
+// complement byte of q - zp.
+__device__ __forceinline__ u32x2 centre8(uint32_t p, uint32_t c) {
+  const uint32_t lo = (p & 0x0f0f0f0fu) + c;          // codes 0, 2, 4, 6
+  const uint32_t hi = ((p >> 4) & 0x0f0f0f0fu) + c;   // codes 1, 3, 5, 7
+  u32x2 r;
+  r.x = __builtin_amdgcn_perm(hi, lo, 0x05010400u) ^ 0x80808080u;  // 0 1 2 3
+  r.y = __builtin_amdgcn_perm(hi, lo, 0x07030602u) ^ 0x80808080u;  // 4 5 6 7
+  return r;
+}
+
+template <typename TY>
+__device__ __forceinline__ void store1(void* y, int64_t i, float v) {
+  if constexpr (sizeof(TY) == 4) {
+    ((float*)y)[i] = v;
+  } else {
+    ((uint16_t*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+}  // namespace
+
+template <typename TS, typename TY>
+__global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
+    const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, int64_t K,
+    const uint8_t* __restrict__ packed, const void* __restrict__ scales,
+    const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m) {
+  typedef typename G8<TS>::T R;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
+  uint8_t* sA = smem8;                          // [2][BM][ROW]
+  uint8_t* sB = smem8 + 2 * A_STAGE;            // [2][BN][ROW]
+  float* sS = (float*)(smem8 + 2 * (A_STAGE + B_STAGE));  // [2][BN]
+
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (tiles_m % 8 == 0) {  // XCD x (= bid mod 8) keeps M blocks x, x+8, ...
+    const int xcd = bid & 7, j = bid >> 3, per = tiles_m >> 3;
+    tm = xcd + 8 * (j % per);
+    tn = j / per;
+  } else {
+    tm = bid % tiles_m;
+    tn = bid / tiles_m;
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*64, cols wn*64
+
+  // x: 4 rounds of 64 rows; lane (t & 7) takes 16 bytes of a row's 128.
+  const int xr = tid >> 3, xc = tid & 7;
+  const int8_t* xt = xq + m0 * K + 16 * xc;
+  int xo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int64_t row = m0 + xr + 64 * r;
+    row = row < M ? row : M - 1;
+    xo[r] = (int)((row - m0) * K);  // bytes, + 128 * kstep
+  }
+  // W: 4 lanes per row, 16 bytes (32 codes) each.
+  const int wr = tid >> 2, wq4 = tid & 3;
+  int64_t wrow = n0 + wr;
+  wrow = wrow < N ? wrow : N - 1;
+  const uint8_t* wp = packed + wrow * (K / 2) + 16 * wq4;  // + 64 * kstep
+  const int64_t ng = K / g;
+  const int spg = g / BK;  // K steps per group
+  const R* sp = (const R*)scales + wrow * ng;
+  const R* zp = (const R*)zeros + wrow * ng;
+
+  // x runs one K step ahead of the MFMAs, the weights (HBM) two.  Loads past
+  // the last step are clamped to it, so the loop has no conditional loads.
+  const int nks = (int)(K / BK);
+  u32x4 xv[4];
+  u32x4 wv[2];
+  R sv[2], zv[2];
+  auto xload = [&](int ks) {
+    ks = ks < nks ? ks : nks - 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xv[r] = *(const u32x4*)(xt + xo[r] + (int64_t)BK * ks);
+  };
+  auto wload = [&](int ks, auto stage) {
+    constexpr int u = decltype(stage)::value;
+    ks = ks < nks ? ks : nks - 1;
+    wv[u] = *(const u32x4*)(wp + (int64_t)(BK / 2) * ks);
+    const int gi = spg == 1 ? ks : ks / spg;
+    sv[u] = sp[gi];
+    zv[u] = zp[gi];
+  };
+  auto lstore = [&](int lstage, auto stage) {
+    constexpr int u = decltype(stage)::value;
+    uint8_t* a = sA + lstage * A_STAGE;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *(u32x4*)(a + (xr + 64 * r) * ROW + 16 * xc) = xv[r];
+    const uint32_t zi = (uint32_t)G8<TS>::f(zv[u]);
+    const uint32_t c = 0x80808080u - zi * 0x01010101u;
+    const u32x2 b0 = centre8(wv[u].x, c), b1 = centre8(wv[u].y, c);
+    const u32x2 b2 = centre8(wv[u].z, c), b3 = centre8(wv[u].w, c);
+    uint8_t* bp = sB + lstage * B_STAGE + wr * ROW + 32 * wq4;
+    *(u32x4*)(bp + 0) = u32x4{b0.x, b0.y, b1.x, b1.y};
+    *(u32x4*)(bp + 16) = u32x4{b2.x, b2.y, b3.x, b3.y};
+    sS[lstage * BN + wr] = G8<TS>::f(sv[u]);  // the row's 4 lanes store the same value
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int l32 = lane & 31, lk = 16 * (lane >> 5);
+  // MFMAs of one K step into fresh int32 accumulators, then the group's
+  // scale folds them into the fp32 ones.
+  auto mma = [&](int lstage) {
+    const uint8_t* a = sA + lstage * A_STAGE + (wm * 64 + l32) * ROW + lk;
+    const uint8_t* b = sB + lstage * B_STAGE + (wn * 64 + l32) * ROW + lk;
+    const float* ss = sS + lstage * BN + wn * 64 + l32;
+    i32x16 ia[2][2];
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      i32x4 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = *(const i32x4*)(a + 32 * i * ROW + 32 * kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = *(const i32x4*)(b + 32 * j * ROW + 32 * kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          ia[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[j],
+                                                          kk == 0 ? i32x16{} : ia[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float s = ss[32 * j];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s, (float)ia[i][j][r], acc[i][j][r]);
+    }
+  };
+
+  xload(0);
+  wload(0, std::integral_constant<int, 0>{});
+  wload(1, std::integral_constant<int, 1>{});
+  lstore(0, std::integral_constant<int, 0>{});
+  xload(1);
+  __syncthreads();
+
+  // One K step: loads (x for ks + 2 would be too early for the one register
+  // stage, so x for ks + 1 was issued by the previous step), MFMAs on buffer
+  // ks & 1, step ks + 1 into the other buffer, barrier, then the next loads.
+  auto step = [&](int ks, auto stage) {
+    constexpr int u = decltype(stage)::value;  // ks mod 2
+    wload(ks + 2, stage);     // register stage u: step ks's weights are in LDS
+    mma(ks & 1);
+    lstore((ks + 1) & 1, std::integral_constant<int, 1 - u>{});
+    __syncthreads();
+    xload(ks + 2);
+  };
+  const int nmain = nks & ~1;
+  for (int ks = 0; ks < nmain; ks += 2) {
+    step(ks, std::integral_constant<int, 0>{});
+    step(ks + 1, std::integral_constant<int, 1>{});
+  }
+  if (nmain < nks) step(nmain, std::integral_constant<int, 0>{});
+
+  // ---- epilogue: lane holds rows 8(r/4) + 4(lane/32) + r%4, column lane%32 --
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (m >= M) continue;
+      const float sa = xs[m];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wn * 64 + 32 * j + l32;
+        if (n < N) store1<TY>(y, m * N + n, sa * acc[i][j][r]);
+      }
+    }
+  }
+}
+
+bool w4a8_gemm_fits(int64_t m, int64_t k, int g) { return m > 16 && g % BK == 0 && k % BK == 0; }
+
+template <typename TS, typename TY>
+static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t k,
+                          const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
+                          int g, void* y, hipStream_t st) {
+  static bool attr_set = false;  // LDS above the 64 KB default
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_w4a8_gemm<TS, TY>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4a8Lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  k_w4a8_gemm<TS, TY><<<grid, 512, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g, y,
+                                                   tiles_m);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_gemm(const int8_t* xq, const float* xs, int64_t m, int64_t k,
+                            const uint8_t* packed, const void* scales, const void* zeros,
+                            int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st) {
+  if (sz_dtype == W4_F16) {
+    if (y_dtype == W4_F32) return w4a8_go<_Float16, float>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+    return w4a8_go<_Float16, __bf16>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+  }
+  if (y_dtype == W4_F32) return w4a8_go<float, float>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+  return w4a8_go<float, __bf16>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+}
+
+}  // namespace w4

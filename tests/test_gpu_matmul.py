@@ -192,7 +192,30 @@ def test_w4a8(w4, m, n, k, g, ykind):
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 8192), (8, 48, 1024), (16, 64, 1024), (64, 256, 8192)])
+# Shapes for the int8-MFMA kernel (M > 16, group a multiple of 128): several
+# 256 x 128 tiles with ragged M and N, one K step only, groups of 256 (two K
+# steps per group), fp32 scales and zero-points.
+W8_GEMM = [(17, 130, 128, 128, "f16"), (257, 1000, 2048, 128, "f16"), (300, 200, 768, 256, "f16"),
+           (512, 384, 1024, 128, "f32"), (64, 129, 640, 640, "f16")]
+
+
+@pytest.mark.parametrize("m,n,k,g,sz", W8_GEMM)
+@pytest.mark.parametrize("ykind", ["bf16", "f32"])
+def test_w4a8_gemm(w4, m, n, k, g, sz, ykind):
+    P, S, Z = make_weights(n, k, g, sz, seed=5 * m + n + k, sigma=0.015)
+    rng = np.random.default_rng(m + 13)
+    x = rng.normal(0, 1, (m, k)).astype(np.float32)
+    x[:, rng.choice(k, max(1, k // 20), replace=False)] *= 20
+    xb = WL.bf16_round_bits(x)
+    y, xq, xs = run_w4a8(w4, xb, "bf16", dev_weights(P, S, Z, sz), g, ykind)
+    oq, os_ = O.act_quant_int8(O.widen_bf16(xb))
+    assert np.array_equal(xq, oq) and np.array_equal(bits(xs), bits(os_))
+    ref = O.matmul_w4a8_f64(oq, os_, P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 8192), (8, 48, 1024), (16, 64, 1024), (64, 256, 8192),
+                                   (300, 130, 256)])
 def test_w4a8_exact_integers(w4, m, n, k):
     """x integers with |x| <= 127 and 127 present (scale 1, xq = x); W integer
     codes with scale 1, zp 0: y is an exact integer below 2^24 and the bf16
