@@ -149,18 +149,30 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
   W4_TRY(check_ptr(fn, "scales", scales));
   W4_TRY(check_ptr(fn, "zeros", zeros));
   W4_TRY(check_ptr(fn, "y", y));
-  // Kernel choice: decode kernels (bf16 MFMA, 16-row tiles) for up to 16 bf16
-  // tokens with 128-aligned groups -- activations staged in LDS when they fit
-  // in 32 KB, read from memory otherwise; the general kernel for the rest.
+  // Kernel choice (bf16 activations): one or two tokens -> the dot2 GEMV;
+  // up to four tokens with the activations fitting in LDS -> the LDS decode
+  // kernel; up to 64 tokens, K a multiple of 512 -> the MFMA GEMV; other
+  // shapes up to 16 tokens -> the decode kernels; more tokens -> the MFMA
+  // GEMM; everything else (fp32 activations, odd group sizes) -> the
+  // general kernel.
   if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size))
     return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
                                             group_size, y, y_dtype, stream),
                       fn);
-  if (x_dtype == W4_BF16 && m <= 16 && group_size % 128 == 0 && w4::decode_lds_fits(m, k))
+  const bool dec = x_dtype == W4_BF16 && m <= 16 && group_size % 128 == 0;
+  if (dec && m <= 4 && w4::decode_lds_fits(m, k))
     return hip_status(w4::launch_w4a16_decode(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
                       fn);
-  if (x_dtype == W4_BF16 && m <= 16 && group_size % 128 == 0)
+  if (x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size))
+    return hip_status(w4::launch_w4a16_gemv(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                            group_size, y, y_dtype, stream),
+                      fn);
+  if (dec && w4::decode_lds_fits(m, k))
+    return hip_status(w4::launch_w4a16_decode(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                              group_size, y, y_dtype, stream),
+                      fn);
+  if (dec)
     return hip_status(w4::launch_w4a16_skinny(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
                       fn);

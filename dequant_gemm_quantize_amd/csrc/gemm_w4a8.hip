@@ -11,9 +11,11 @@
 // into the fp32 accumulators with that group's scale; the token scale is
 // applied once at the end.
 //
-// Tiling.  Workgroup tile 256 (M) x 128 (N), K steps of 128, eight waves in
-// a 4 x 2 arrangement, each a 64 x 64 output block (2 x 2 tiles of
-// v_mfma_i32_32x32x32_i8).  The weight tile is turned into int8 (q - zp) once
+// Tiling.  Workgroup tile BM (M) x 128 (N), K steps of 128, BM / 32 waves in
+// a (BM / 64) x 2 arrangement, each a 64 x 64 output block (2 x 2 tiles of
+// v_mfma_i32_32x32x32_i8).  With BM = 128 two workgroups share a CU, one
+// wave of each per SIMD; the two drift apart between their barriers, so one
+// workgroup's conversions overlap the other's MFMAs.  The weight tile is turned into int8 (q - zp) once
 // per workgroup while it is written to LDS; the activation tile is copied as
 // is.  Both are double-buffered in LDS; the global loads of x run one K step
 // ahead and those of the weights two, held in registers.
@@ -26,7 +28,13 @@ namespace w4 {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 128;
+#ifndef W4_W4A8_BM
+#define W4_W4A8_BM 256
+#endif
+constexpr int BM = W4_W4A8_BM, BN = 128, BK = 128;
+constexpr int NT = 2 * BM;            // threads: BM / 64 x 2 waves of 64 x 64 outputs
+constexpr int WB = BN * BK / 2 / NT;  // packed weight bytes per thread and K step
+constexpr int WL = BK / 2 / WB;       // lanes per weight row
 constexpr int ROW = BK + 16;            // bytes per LDS row (+16 bytes of padding)
 constexpr int A_STAGE = BM * ROW;       // bytes
 constexpr int B_STAGE = BN * ROW;       // bytes
@@ -67,8 +75,8 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v) {
 
 }  // namespace
 
-template <typename TS, typename TY>
-__global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
+template <typename TS, typename TY, bool G128>
+__global__ __launch_bounds__(NT, 512 / NT) void k_w4a8_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, int64_t K,
     const uint8_t* __restrict__ packed, const void* __restrict__ scales,
     const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m) {
@@ -95,21 +103,22 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*64, cols wn*64
 
-  // x: 4 rounds of 64 rows; lane (t & 7) takes 16 bytes of a row's 128.
+  // x: 4 rounds of NT/8 rows; lane (t & 7) takes 16 bytes of a row's 128.
+  constexpr int XRS = NT / 8;
   const int xr = tid >> 3, xc = tid & 7;
   const int8_t* xt = xq + m0 * K + 16 * xc;
   int xo[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    int64_t row = m0 + xr + 64 * r;
+    int64_t row = m0 + xr + XRS * r;
     row = row < M ? row : M - 1;
     xo[r] = (int)((row - m0) * K);  // bytes, + 128 * kstep
   }
-  // W: 4 lanes per row, 16 bytes (32 codes) each.
-  const int wr = tid >> 2, wq4 = tid & 3;
+  // W: WL lanes per row, WB bytes (2 WB codes) each.
+  const int wr = tid / WL, wql = tid % WL;
   int64_t wrow = n0 + wr;
   wrow = wrow < N ? wrow : N - 1;
-  const uint8_t* wp = packed + wrow * (K / 2) + 16 * wq4;  // + 64 * kstep
+  const uint8_t* wp = packed + wrow * (K / 2) + WB * wql;  // + 64 * kstep
   const int64_t ng = K / g;
   const int spg = g / BK;  // K steps per group
   const R* sp = (const R*)scales + wrow * ng;
@@ -117,9 +126,10 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
 
   // x runs one K step ahead of the MFMAs, the weights (HBM) two.  Loads past
   // the last step are clamped to it, so the loop has no conditional loads.
+  constexpr int WV = WB / 16;
   const int nks = (int)(K / BK);
   u32x4 xv[4];
-  u32x4 wv[2];
+  u32x4 wv[2][WV];
   R sv[2], zv[2];
   auto xload = [&](int ks) {
     ks = ks < nks ? ks : nks - 1;
@@ -129,8 +139,9 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
   auto wload = [&](int ks, auto stage) {
     constexpr int u = decltype(stage)::value;
     ks = ks < nks ? ks : nks - 1;
-    wv[u] = *(const u32x4*)(wp + (int64_t)(BK / 2) * ks);
-    const int gi = spg == 1 ? ks : ks / spg;
+#pragma unroll
+    for (int v = 0; v < WV; ++v) wv[u][v] = *(const u32x4*)(wp + (int64_t)(BK / 2) * ks + 16 * v);
+    const int gi = G128 ? ks : ks / spg;
     sv[u] = sp[gi];
     zv[u] = zp[gi];
   };
@@ -138,55 +149,72 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
     constexpr int u = decltype(stage)::value;
     uint8_t* a = sA + lstage * A_STAGE;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) *(u32x4*)(a + (xr + 64 * r) * ROW + 16 * xc) = xv[r];
+    for (int r = 0; r < 4; ++r) *(u32x4*)(a + (xr + XRS * r) * ROW + 16 * xc) = xv[r];
     const uint32_t zi = (uint32_t)G8<TS>::f(zv[u]);
     const uint32_t c = 0x80808080u - zi * 0x01010101u;
-    const u32x2 b0 = centre8(wv[u].x, c), b1 = centre8(wv[u].y, c);
-    const u32x2 b2 = centre8(wv[u].z, c), b3 = centre8(wv[u].w, c);
-    uint8_t* bp = sB + lstage * B_STAGE + wr * ROW + 32 * wq4;
-    *(u32x4*)(bp + 0) = u32x4{b0.x, b0.y, b1.x, b1.y};
-    *(u32x4*)(bp + 16) = u32x4{b2.x, b2.y, b3.x, b3.y};
-    sS[lstage * BN + wr] = G8<TS>::f(sv[u]);  // the row's 4 lanes store the same value
+    uint8_t* bp = sB + lstage * B_STAGE + wr * ROW + 2 * WB * wql;
+#pragma unroll
+    for (int v = 0; v < WV; ++v) {
+      const u32x2 b0 = centre8(wv[u][v].x, c), b1 = centre8(wv[u][v].y, c);
+      const u32x2 b2 = centre8(wv[u][v].z, c), b3 = centre8(wv[u][v].w, c);
+      *(u32x4*)(bp + 32 * v + 0) = u32x4{b0.x, b0.y, b1.x, b1.y};
+      *(u32x4*)(bp + 32 * v + 16) = u32x4{b2.x, b2.y, b3.x, b3.y};
+    }
+    sS[lstage * BN + wr] = G8<TS>::f(sv[u]);  // the row's lanes store the same value
   };
 
   f32x16 acc[2][2];
+  i32x16 ia[2][2];  // int32 sums of the current K step, one half (i) at a time
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        acc[i][j][r] = 0.0f;
+        ia[i][j][r] = 0;
+      }
+  float sc[2] = {0.0f, 0.0f};  // group scales of this lane's two columns
 
   const int l32 = lane & 31, lk = 16 * (lane >> 5);
-  // MFMAs of one K step into fresh int32 accumulators, then the group's
-  // scale folds them into the fp32 ones.
+  // Half i of a K step: the MFMAs of rows 32i..32i+31 of the wave block into
+  // ia[i], interleaved with the fp32 fold of the other half (1 - i), whose
+  // MFMAs finished one phase earlier (the previous step's, for i = 0).  The
+  // matrix cores and the vector ALU then work at the same time.
+  auto half = [&](int lstage, auto hi, const i32x4 (&bfr)[2][BK / 32]) {
+    constexpr int i = decltype(hi)::value;
+    const uint8_t* a = sA + lstage * A_STAGE + (wm * 64 + 32 * i + l32) * ROW + lk;
+    i32x4 af[BK / 32];
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) af[kk] = *(const i32x4*)(a + 32 * kk);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        ia[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk], bfr[j][kk],
+                                                        kk == 0 ? i32x16{} : ia[i][j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[1 - i][j][r] = fmaf(sc[j], (float)ia[1 - i][j][r], acc[1 - i][j][r]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
+    }
+  };
   auto mma = [&](int lstage) {
-    const uint8_t* a = sA + lstage * A_STAGE + (wm * 64 + l32) * ROW + lk;
     const uint8_t* b = sB + lstage * B_STAGE + (wn * 64 + l32) * ROW + lk;
+    i32x4 bfr[2][BK / 32];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kk = 0; kk < BK / 32; ++kk) bfr[j][kk] = *(const i32x4*)(b + 32 * j * ROW + 32 * kk);
+    half(lstage, std::integral_constant<int, 0>{}, bfr);  // folds half 1 of the previous step
     const float* ss = sS + lstage * BN + wn * 64 + l32;
-    i32x16 ia[2][2];
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      i32x4 af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *(const i32x4*)(a + 32 * i * ROW + 32 * kk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = *(const i32x4*)(b + 32 * j * ROW + 32 * kk);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          ia[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[j],
-                                                          kk == 0 ? i32x16{} : ia[i][j], 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float s = ss[32 * j];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(s, (float)ia[i][j][r], acc[i][j][r]);
-    }
+    sc[0] = ss[0];
+    sc[1] = ss[32];
+    half(lstage, std::integral_constant<int, 1>{}, bfr);  // folds half 0 of this step
   };
 
   xload(0);
@@ -196,9 +224,9 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
   xload(1);
   __syncthreads();
 
-  // One K step: loads (x for ks + 2 would be too early for the one register
-  // stage, so x for ks + 1 was issued by the previous step), MFMAs on buffer
-  // ks & 1, step ks + 1 into the other buffer, barrier, then the next loads.
+  // One K step: weights for ks + 2 in flight, MFMAs on buffer ks & 1, step
+  // ks + 1 (x loaded by the previous step) into the other buffer, barrier,
+  // then x for ks + 2.
   auto step = [&](int ks, auto stage) {
     constexpr int u = decltype(stage)::value;  // ks mod 2
     wload(ks + 2, stage);     // register stage u: step ks's weights are in LDS
@@ -213,6 +241,11 @@ __global__ __launch_bounds__(512, 1) void k_w4a8_gemm(
     step(ks + 1, std::integral_constant<int, 1>{});
   }
   if (nmain < nks) step(nmain, std::integral_constant<int, 0>{});
+  // fold half 1 of the last step
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[1][j][r] = fmaf(sc[j], (float)ia[1][j][r], acc[1][j][r]);
 
   // ---- epilogue: lane holds rows 8(r/4) + 4(lane/32) + r%4, column lane%32 --
 #pragma unroll
@@ -239,15 +272,20 @@ static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t 
                           int g, void* y, hipStream_t st) {
   static bool attr_set = false;  // LDS above the 64 KB default
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_w4a8_gemm<TS, TY>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4a8Lds);
-    if (e != hipSuccess) return e;
+    for (const void* f : {(const void*)k_w4a8_gemm<TS, TY, true>, (const void*)k_w4a8_gemm<TS, TY, false>}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4a8Lds);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  k_w4a8_gemm<TS, TY><<<grid, 512, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g, y,
-                                                   tiles_m);
+  if (g == BK)
+    k_w4a8_gemm<TS, TY, true><<<grid, NT, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g,
+                                                         y, tiles_m);
+  else
+    k_w4a8_gemm<TS, TY, false><<<grid, NT, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n,
+                                                          g, y, tiles_m);
   return hipGetLastError();
 }
 

@@ -31,20 +31,13 @@ namespace {
 #endif
 constexpr int kRowsWave = W4_DOT2_RW;    // weight rows per wave
 constexpr int kRowsWg = 4 * kRowsWave;   // weight rows per workgroup (4 waves)
-constexpr int kMaxCh = 4;      // 16-byte chunks per lane and row (K <= 64 * 4 * 32 = 8192)
-
-__device__ __forceinline__ uint32_t and_or2(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
 
 // 8 codes of a word -> 4 bf16 pairs (128 + q) in the order (0,4),(1,5),(2,6),(3,7).
-__device__ __forceinline__ void codes8(uint32_t p, uint32_t (&o)[4]) {
-  o[0] = and_or2(p, 0x000f000fu, 0x43004300u);
-  o[1] = and_or2(p >> 4, 0x000f000fu, 0x43004300u);
-  o[2] = and_or2(p >> 8, 0x000f000fu, 0x43004300u);
-  o[3] = and_or2(p >> 12, 0x000f000fu, 0x43004300u);
+__device__ __forceinline__ void codes8(uint32_t p, const NibConst& nk, uint32_t (&o)[4]) {
+  o[0] = nk(p);
+  o[1] = nk(p >> 4);
+  o[2] = nk(p >> 8);
+  o[3] = nk(p >> 12);
 }
 
 // 8 bf16 activations (4 pairs, natural order) -> pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7).
@@ -148,7 +141,7 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
     n = n < N ? n : N - 1;
     const u32x4* row = (const u32x4*)(packed + n * (K / 2));
 #pragma unroll
-    for (int c = 0; c < CH; ++c) wq[r][c] = row[lane + 64 * c];
+    for (int c = 0; c < CH; ++c) wq[r][c] = __builtin_nontemporal_load(row + lane + 64 * c);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -188,6 +181,7 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
     }
 
   // ---- rows: dot products, scale, zero-point correction, wave sums --------
+  const NibConst nk = NibConst::make();
   int gq[CH];  // group of the lane's chunk c
 #pragma unroll
   for (int c = 0; c < CH; ++c) gq[c] = (32 * (lane + 64 * c)) / g;
@@ -207,7 +201,7 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         uint32_t b[4];
-        codes8(w4[t], b);
+        codes8(w4[t], nk, b);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll

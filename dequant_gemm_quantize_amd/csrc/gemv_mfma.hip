@@ -1,0 +1,279 @@
+// Decode-time fused dequantize-matmul for 1 <= M <= 64 bf16 tokens, groups
+// that are multiples of 128 columns, K a multiple of 512 (up to 8192 for
+// M <= 16, 4096 above).
+// HBM-bound: the kernel exists to stream the packed codes at full bandwidth
+// with as little vector-ALU work per code as possible.
+//
+// Math.  For a 128-column block b of weight row n (one scale s and
+// zero-point zp) and token m:
+//   sum_k x[m,k] (q[n,k] - zp) s = s * ( sum_k x[m,k] (128 + q[n,k])
+//                                        - (128 + zp) * sum_k x[m,k] )
+// ("From Scratch: Building a GPTQ INT4 Quantizer in Pure Python", Step 4,
+// inside the product of "Building a From-Scratch Group-Wise INT4
+// Quantization Layer for LLaMA Weights", Step 2).  128 + q is an exact
+// bfloat16 whose low mantissa bits are the code: a byte permute and one
+// and-or turn two nibbles into an operand pair, and v_mfma_f32_16x16x32_bf16
+// does the multiply-adds (activations as the A operand, 16 token rows; codes
+// as B, 16 weight rows).  The block sums of x come from the same MFMA
+// against ones, once per wave.
+//
+// Work layout.  A workgroup owns 16 * RB weight rows over all of K and has
+// one wave per 512-column slice of K.  Each wave keeps the activations of
+// its slice in registers for the whole kernel and streams the codes of its
+// slice for all 16 * RB rows: lane l serves weight row l mod 16 and the
+// 32-column quarter l div 16 of each 128-column block, one 16-byte load per
+// block.  All loads of a wave are issued before any arithmetic and there is
+// no barrier until the waves add their partial sums through LDS at the end,
+// so each wave computes as soon as its own data arrives.
+#include "w4_common.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+namespace {
+
+#ifndef W4_GEMV_RB
+#define W4_GEMV_RB 2
+#endif
+constexpr int kSlice = 512;  // columns of K per wave
+constexpr int kBlocks = kSlice / 128;
+
+// Codes 2v, 2v+1 of a packed 8-code word as a bf16 pair (128 + q each).
+__device__ __forceinline__ uint32_t pair_of(uint32_t p, uint32_t p4, uint32_t v, const NibConst& nk) {
+  // byte v of p holds codes 2v (low nibble) and 2v+1; byte v of p >> 4 holds
+  // code 2v+1 in its low nibble.  Bytes 1 and 3 of the permute are zero.
+  const uint32_t sel = v | 0x0c00u | ((4u + v) << 16) | 0x0c000000u;
+  return nk(__builtin_amdgcn_perm(p4, p, sel));
+}
+
+__device__ __forceinline__ bf16x8 word_to_bf16(uint32_t p, const NibConst& nk) {
+  const uint32_t p4 = p >> 4;
+  const u32x4 r = {pair_of(p, p4, 0, nk), pair_of(p, p4, 1, nk), pair_of(p, p4, 2, nk),
+                   pair_of(p, p4, 3, nk)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <typename TS> struct GV;
+template <> struct GV<_Float16> {
+  typedef uint16_t T;
+  typedef u32x2 V4;  // four consecutive scales
+  __device__ static float f(T v) { return (float)__builtin_bit_cast(_Float16, v); }
+  __device__ static T at(const V4& v, int i) {
+    return (T)(((i < 2 ? v.x : v.y) >> (16 * (i & 1))) & 0xffffu);
+  }
+};
+template <> struct GV<float> {
+  typedef uint32_t T;
+  typedef u32x4 V4;
+  __device__ static float f(T v) { return __uint_as_float(v); }
+  __device__ static T at(const V4& v, int i) { return v[i]; }
+};
+
+template <typename TY>
+__device__ __forceinline__ void put1(void* y, int64_t i, float v) {
+  if constexpr (sizeof(TY) == 4) {
+    ((float*)y)[i] = v;
+  } else {
+    ((uint16_t*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+}  // namespace
+
+// MT: token blocks of 16 (1..4), or 0 for exactly one token (then only
+// accumulator element 0 is live).  The token blocks are processed one after
+// the other with the wave's codes held in registers, so the codes are read
+// from memory once whatever M is.
+// G128: group size 128 (the four scales of a slice are contiguous).
+template <typename TS, typename TY, int RB, int MT, bool G128>
+__global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
+    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g, int ng,
+    void* __restrict__ y) {
+  typedef typename GV<TS>::T R;
+  typedef typename GV<TS>::V4 V4;
+  constexpr bool M1 = MT == 0;
+  constexpr int T = M1 ? 1 : MT;
+  extern __shared__ float part[];  // [waves][RB][16 T tokens][16 rows]
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int l16 = lane & 15, h = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * (16 * RB);
+  const int64_t k0 = (int64_t)kSlice * w;
+
+  // activations of token block tb: token 16 tb + l16 (tokens past M repeat
+  // the last one and are never stored), columns k0 + 128 i + 32 h + 8 j .. + 7
+  u32x4 xf[kBlocks][4];
+  auto xload = [&](int tb) {
+    int tok = 16 * tb + l16;
+    tok = tok < M ? tok : M - 1;
+    const u32x4* xp = (const u32x4*)(x + (int64_t)tok * K + k0 + 32 * h);
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[i][j] = xp[16 * i + j];
+  };
+
+  // ---- every load of the wave, in the order the arithmetic needs them ----
+  xload(0);
+  // scales and zero-points of the lane's row for the slice's four blocks
+  int64_t rows[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t r = r0 + 16 * rb + l16;
+    rows[rb] = r < N ? r : N - 1;
+  }
+  R sv[RB][kBlocks], zv[RB][kBlocks];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (G128) {
+      const V4 s4 = *(const V4*)((const R*)scales + rows[rb] * ng + k0 / 128);
+      const V4 z4 = *(const V4*)((const R*)zeros + rows[rb] * ng + k0 / 128);
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        sv[rb][i] = GV<TS>::at(s4, i);
+        zv[rb][i] = GV<TS>::at(z4, i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        const int gi = (int)(k0 + 128 * i) / g;
+        sv[rb][i] = ((const R*)scales)[rows[rb] * ng + gi];
+        zv[rb][i] = ((const R*)zeros)[rows[rb] * ng + gi];
+      }
+    }
+  }
+  // packed codes: row, columns k0 + 128 i + 32 h .. + 31 (16 bytes)
+  u32x4 wq[RB][kBlocks];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const uint8_t* base = packed + rows[rb] * (K / 2) + k0 / 2 + 16 * h;
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) wq[rb][i] = __builtin_nontemporal_load((const u32x4*)(base + 64 * i));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  const NibConst nk = NibConst::make();
+  // lane holds tokens 16 tb + 4h + r (r = 0..3) of weight row l16
+  f32x4 acc[RB][T];
+#pragma unroll
+  for (int tb = 0; tb < T; ++tb) {
+    if (tb > 0) xload(tb);
+    // block sums of x for every token (MFMA against ones)
+    f32x4 xs[kBlocks];
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) {
+      xs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[i][j]), ones, xs[i], 0, 0, 0);
+    }
+    // row blocks: codes -> bf16 operands, MFMAs, scale and zero-point
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      acc[rb][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        const uint32_t wd[4] = {wq[rb][i].x, wq[rb][i].y, wq[rb][i].z, wq[rb][i].w};
+        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[i][j]),
+                                                      word_to_bf16(wd[j], nk), d, 0, 0, 0);
+        const float s = GV<TS>::f(sv[rb][i]);
+        const float nsz = -s * (128.0f + GV<TS>::f(zv[rb][i]));
+        if constexpr (M1) {
+          acc[rb][tb][0] = fmaf(s, d[0], fmaf(nsz, xs[i][0], acc[rb][tb][0]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[rb][tb][r] = fmaf(s, d[r], fmaf(nsz, xs[i][r], acc[rb][tb][r]));
+        }
+      }
+    }
+  }
+
+  // ---- partial sums of the waves' K slices -> LDS -> y --------------------
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float* p = part + (w * RB + rb) * (256 * T);
+    if constexpr (M1) {
+      if (h == 0) p[l16] = acc[rb][0][0];
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < T; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[(16 * tb + 4 * h + r) * 16 + l16] = acc[rb][tb][r];
+    }
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int mm = M1 ? 1 : M;
+  const int outs = RB * 16 * mm;
+  for (int o = tid; o < outs; o += blockDim.x) {
+    const int rb = o / (16 * mm);
+    const int rem = o - rb * 16 * mm;
+    const int t = rem >> 4, row = rem & 15;
+    float s = 0.0f;
+    for (int v = 0; v < nw; ++v) s += part[(v * RB + rb) * (256 * T) + t * 16 + row];
+    const int64_t n = r0 + 16 * rb + row;
+    if (n < N) put1<TY>(y, (int64_t)t * N + n, s);
+  }
+}
+
+bool gemv_mfma_fits(int64_t m, int64_t k, int g) {
+  if (k % kSlice != 0 || g % 128 != 0 || m < 1) return false;
+  if (m <= 16) return k <= 16 * kSlice;
+  return m <= 64 && k <= 8 * kSlice;
+}
+
+template <typename TS, typename TY, int MT, bool G128>
+static void gemv_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
+                    const void* scales, const void* zeros, int64_t n, int g, void* y,
+                    hipStream_t st) {
+  constexpr int RB = W4_GEMV_RB;
+  constexpr int T = MT == 0 ? 1 : MT;
+  const int nw = (int)(k / kSlice);
+  const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
+  const size_t lds = (size_t)nw * RB * 256 * T * sizeof(float);
+  k_w4a16_gemv<TS, TY, RB, MT, G128><<<grid, 64 * nw, lds, st>>>(x, (int)m, k, packed, scales,
+                                                                 zeros, n, g, (int)(k / g), y);
+}
+
+template <typename TS, typename TY, bool G128>
+static void gemv_pick(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
+                      const void* scales, const void* zeros, int64_t n, int g, void* y,
+                      hipStream_t st) {
+  if (m == 1) gemv_go<TS, TY, 0, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
+  else if (m <= 16) gemv_go<TS, TY, 1, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
+  else if (m <= 32) gemv_go<TS, TY, 2, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
+  else if (m <= 48) gemv_go<TS, TY, 3, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
+  else gemv_go<TS, TY, 4, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
+}
+
+template <typename TS, typename TY>
+static void gemv_pick(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
+                      const void* scales, const void* zeros, int64_t n, int g, void* y,
+                      hipStream_t st) {
+  if (g == 128) gemv_pick<TS, TY, true>(x, m, k, packed, scales, zeros, n, g, y, st);
+  else gemv_pick<TS, TY, false>(x, m, k, packed, scales, zeros, n, g, y, st);
+}
+
+hipError_t launch_w4a16_gemv(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                             const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                             int g, void* y, int y_dtype, hipStream_t st) {
+  const uint16_t* xb = (const uint16_t*)x;
+  if (sz_dtype == W4_F16) {
+    if (y_dtype == W4_F32) gemv_pick<_Float16, float>(xb, m, k, packed, scales, zeros, n, g, y, st);
+    else gemv_pick<_Float16, __bf16>(xb, m, k, packed, scales, zeros, n, g, y, st);
+  } else {
+    if (y_dtype == W4_F32) gemv_pick<float, float>(xb, m, k, packed, scales, zeros, n, g, y, st);
+    else gemv_pick<float, __bf16>(xb, m, k, packed, scales, zeros, n, g, y, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4

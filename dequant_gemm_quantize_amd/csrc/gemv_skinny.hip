@@ -43,12 +43,6 @@ constexpr int kWaves = W4_SKINNY_WAVES;  // waves per workgroup (K split)
 constexpr int kChunk = W4_SKINNY_CHUNK;  // 128-column blocks whose codes are loaded ahead
 constexpr int kXDist = W4_SKINNY_XDIST;  // activation prefetch distance (blocks)
 
-// (a & b) | c in one VALU instruction (v_and_or_b32).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
 
 // (q[2v], q[2v+1]) of a packed 8-code word as a bf16 pair (128 + q each).
 __device__ __forceinline__ uint32_t code_pair(uint32_t p, uint32_t p4, uint32_t v) {
@@ -56,7 +50,7 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t p, uint32_t p4, uint32_t 
   // code 2v+1 in its low nibble.  Bytes 1 and 3 of the result are zero.
   const uint32_t sel = v | 0x0c00u | ((4u + v) << 16) | 0x0c000000u;
   const uint32_t t = __builtin_amdgcn_perm(p4, p, sel);
-  return and_or(t, 0x000f000fu, 0x43004300u);
+  return NibConst::make()(t);
 }
 
 __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t p) {
@@ -255,10 +249,11 @@ constexpr int kDecodeLds = W4_DECODE_LDS_BYTES;
 // Codes 0..7 of a word as bf16 pairs (128+q) in the order (0,4),(1,5),(2,6),(3,7).
 __device__ __forceinline__ bf16x8 codes_to_bf16_interleaved(uint32_t p) {
   u32x4 r;
-  r.x = and_or(p, 0x000f000fu, 0x43004300u);
-  r.y = and_or(p >> 4, 0x000f000fu, 0x43004300u);
-  r.z = and_or(p >> 8, 0x000f000fu, 0x43004300u);
-  r.w = and_or(p >> 12, 0x000f000fu, 0x43004300u);
+  const NibConst nk = NibConst::make();
+  r.x = nk(p);
+  r.y = nk(p >> 4);
+  r.z = nk(p >> 8);
+  r.w = nk(p >> 12);
   return __builtin_bit_cast(bf16x8, r);
 }
 

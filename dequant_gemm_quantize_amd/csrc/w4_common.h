@@ -79,4 +79,23 @@ __device__ __forceinline__ T ldg_nt(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// The two constants of the nibble -> bf16 conversion (q & 0x000f000f) |
+// 0x43004300, held in registers.  VOP3 instructions on this target take no
+// literal operand, so with plain constants the compiler splits
+// v_and_or_b32 into v_and_b32 + v_or_b32.  The empty asm statement emits no
+// instruction; it only hides the values from constant folding, and being
+// free of side effects it is merged across calls, so the constants are
+// materialised once per kernel.  (The and-or itself stays plain C: an
+// inline-asm ALU instruction that feeds an MFMA is invisible to the
+// compiler's hazard tracking.)
+struct NibConst {
+  uint32_t mask, magic;
+  __device__ static NibConst make() {
+    NibConst k{0x000f000fu, 0x43004300u};
+    asm("" : "+v"(k.mask), "+v"(k.magic));
+    return k;
+  }
+  __device__ uint32_t operator()(uint32_t p) const { return (p & mask) | magic; }
+};
+
 }  // namespace w4

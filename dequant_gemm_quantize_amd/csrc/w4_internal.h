@@ -32,6 +32,10 @@ hipError_t launch_w4a16_dot2(const void* x, int64_t m, int64_t k, const uint8_t*
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
                              int g, void* y, int y_dtype, hipStream_t st);
 bool dot2_fits(int64_t m, int64_t k, int g);
+hipError_t launch_w4a16_gemv(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                             const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                             int g, void* y, int y_dtype, hipStream_t st);
+bool gemv_mfma_fits(int64_t m, int64_t k, int g);
 hipError_t launch_w4a16_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
                              int g, void* y, int y_dtype, hipStream_t st);

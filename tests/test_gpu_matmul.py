@@ -72,6 +72,29 @@ def test_w4a16_bf16(w4, m, n, k, g, sz):
     assert err <= TOL["bf16"], err
 
 
+# Decode shapes for the MFMA GEMV (M <= 64, K a multiple of 512, groups a
+# multiple of 128): one to sixteen 512-column slices, one to four blocks of
+# 16 tokens with ragged last blocks, ragged row counts (workgroups of 32
+# rows), groups spanning several blocks, both scale and output dtypes.
+DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
+          (2, 100, 1536, 128, "f32", "bf16"), (3, 77, 2048, 256, "f16", "bf16"),
+          (5, 64, 8192, 128, "f16", "bf16"), (8, 130, 4096, 512, "f32", "f32"),
+          (13, 31, 1024, 128, "f16", "f32"), (16, 300, 2560, 128, "f16", "bf16"),
+          (1, 17, 8192, 1024, "f16", "bf16"), (16, 1, 512, 512, "f32", "bf16"),
+          (17, 100, 1024, 128, "f16", "bf16"), (32, 300, 4096, 128, "f16", "bf16"),
+          (33, 65, 512, 256, "f32", "f32"), (48, 40, 1536, 128, "f16", "bf16"),
+          (64, 129, 2048, 128, "f16", "f32")]
+
+
+@pytest.mark.parametrize("m,n,k,g,sz,ykind", DECODE)
+def test_w4a16_decode_shapes(w4, m, n, k, g, sz, ykind):
+    P, S, Z = make_weights(n, k, g, sz, seed=7 * m + n + k)
+    x = WL.bf16_round_bits(np.random.default_rng(m + 17).normal(0, 1, (m, k)).astype(np.float32))
+    y = run_w4a16(w4, x, "bf16", dev_weights(P, S, Z, sz), g, ykind)
+    ref = O.matmul_w4a16_f64(O.widen_bf16(x), P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
+
+
 @pytest.mark.parametrize("m,n,k,g", [(1, 256, 256, 32), (3, 100, 384, 128), (19, 64, 640, 64)])
 @pytest.mark.parametrize("ykind", ["f32", "bf16"])
 def test_w4a16_f32_activations(w4, m, n, k, g, ykind):
@@ -82,7 +105,8 @@ def test_w4a16_f32_activations(w4, m, n, k, g, ykind):
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (8, 48, 512), (16, 64, 256), (40, 300, 1024), (256, 256, 2048)])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (1, 64, 4096), (8, 48, 512), (16, 64, 256), (40, 300, 1024),
+                                   (256, 256, 2048)])
 def test_w4a16_exact_integers(w4, m, n, k):
     """W integers 0..15 (each group holding 0 and 15 -> scale 1, zp 0), x
     integers in [-8, 8]: every partial sum is an exact integer below 2^24, so
