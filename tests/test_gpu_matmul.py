@@ -218,9 +218,12 @@ def test_w4a8(w4, m, n, k, g, ykind):
 
 # Shapes for the int8-MFMA kernel (M > 16, group a multiple of 128): several
 # 256 x 128 tiles with ragged M and N, one K step only, groups of 256 (two K
-# steps per group), fp32 scales and zero-points.
+# steps per group), fp32 scales and zero-points; then the one-token GEMV.
 W8_GEMM = [(17, 130, 128, 128, "f16"), (257, 1000, 2048, 128, "f16"), (300, 200, 768, 256, "f16"),
-           (512, 384, 1024, 128, "f32"), (64, 129, 640, 640, "f16")]
+           (512, 384, 1024, 128, "f32"), (64, 129, 640, 640, "f16"),
+           # one token, group 128, K = 2048 .. 8192: the dot4 GEMV (ragged row counts)
+           (1, 1, 2048, 128, "f16"), (1, 300, 4096, 128, "f32"), (1, 17, 6144, 128, "f16"),
+           (1, 1000, 8192, 128, "f16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz", W8_GEMM)
