@@ -235,7 +235,7 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
 
     # small-batch sweep on the Llama-7B shapes (rotated weights)
     sweep = {}
-    for m in (1, 2, 4, 8, 16, 32):
+    for m in (1, 2, 4, 8, 16, 32, 64):
         x = to_dev(WL.activation(2 if m == 1 else 3, m, 4096))
         row = {}
         for name, (n, k) in (("Wa", (4096, 4096)), ("Wb", (11008, 4096))):
