@@ -77,9 +77,12 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="skip the extra per-step measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
-    ap.add_argument("--kernel", choices=("decode_wb", "copy"), default=None,
+    ap.add_argument("--kernel", choices=("decode_wb", "prefill_wb", "w4a8_m1", "w4a8_m512", "copy"),
+                    default=None,
                     help="launch only this kernel --launches times, eagerly, for counter runs: "
                          "decode_wb = the [11008,4096] decode product on rotated weights, "
+                         "prefill_wb = the M=2048 product on [11008,4096], "
+                         "w4a8_m1 / w4a8_m512 = the W4A8 product on [28672,8192], "
                          "copy = a plain device copy of --copy-mib MiB (calibrates byte counters)")
     ap.add_argument("--launches", type=int, default=40)
     ap.add_argument("--copy-mib", type=int, default=256)
@@ -338,6 +341,37 @@ def kernel_only(args, w4, WL, torch, dev, to_dev, log):
         torch.cuda.synchronize()
         print(json.dumps({"kernel": "copy", "launches": n_launch, "read_bytes": nbytes,
                           "write_bytes": nbytes}), flush=True)
+        return 0
+    if args.kernel == "prefill_wb":
+        g, n, k = 128, 11008, 4096
+        wt = to_dev(WL.weight("Wb"))
+        p, s, z = w4.quantize_pack_int4(wt, g, torch.float16)
+        del wt
+        x = to_dev(WL.activation(4, 2048, k))
+        y = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for i in range(n_launch):
+            w4.w4a16_matmul(x, p, s, z, g, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": "prefill_wb", "launches": n_launch,
+                          "flops_per_launch": 2 * 2048 * n * k}), flush=True)
+        return 0
+    if args.kernel in ("w4a8_m1", "w4a8_m512"):
+        g, n, k = 128, 28672, 8192
+        m = 1 if args.kernel == "w4a8_m1" else 512
+        wt = to_dev(WL.weight("We"))
+        q = w4.quantize_pack_int4(wt, g, torch.float16)
+        del wt
+        copies = [q] + [tuple(a.clone() for a in q) for _ in range(3)]
+        xq, xs = w4.quantize_act_int8(to_dev(WL.activation(5, m, k)))
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for i in range(n_launch):
+            w4.w4a8_matmul(xq, xs, *copies[i % 4], g, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": args.kernel, "launches": n_launch,
+                          "bytes_per_launch": w4a8_bytes(m, n, k, g),
+                          "ops_per_launch": 2 * m * n * k}), flush=True)
         return 0
     g, n, k = 128, 11008, 4096
     wt = to_dev(WL.weight("Wb"))
