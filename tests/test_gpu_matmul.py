@@ -276,3 +276,23 @@ def test_workload_w4a8(w4, m):
     rows = np.arange(m) if m == 1 else np.unique(np.concatenate([[0, m - 1], np.random.default_rng(5).choice(m, 48, replace=False)]))
     ref = O.matmul_w4a8_f64(oq[rows], os_[rows], P, S, Z, 128)
     assert O.max_rel_err(y_as_f64(y)[rows], ref) <= TOL["bf16"]
+
+
+def test_empty_inputs(w4):
+    """Zero tokens or zero weight rows: valid calls that launch nothing and
+    return correctly shaped empty outputs."""
+    dev = torch.device("cuda")
+    p0, s0, z0 = w4.quantize_pack_int4(torch.zeros((0, 256), dtype=torch.bfloat16, device=dev), 128,
+                                       torch.float16)
+    assert tuple(p0.shape) == (0, 128) and tuple(s0.shape) == (0, 2)
+    P, S, Z = make_weights(64, 256, 128, "f16", seed=1)
+    dw = dev_weights(P, S, Z, "f16")
+    x0 = torch.zeros((0, 256), dtype=torch.bfloat16, device=dev)
+    assert tuple(w4.w4a16_matmul(x0, *dw, 128).shape) == (0, 64)
+    xq, xs = w4.quantize_act_int8(x0)
+    assert tuple(xq.shape) == (0, 256) and tuple(xs.shape) == (0,)
+    assert tuple(w4.w4a8_matmul(xq, xs, *dw, 128).shape) == (0, 64)
+    x3 = torch.ones((3, 256), dtype=torch.bfloat16, device=dev)
+    y = w4.w4a16_matmul(x3, p0, s0, z0, 128)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (3, 0)
