@@ -12,7 +12,7 @@
 // with a shift and one and-or; v_dot2_f32_bf16 multiplies two such codes by
 // two activations and accumulates in fp32.
 //
-// Work layout.  A 256-lane workgroup owns 4 * RW weight rows; wave w owns
+// Work layout.  A workgroup of W waves owns W * RW weight rows; wave w owns
 // rows RW*w .. RW*w + RW-1 over all of K.  Lane l covers the 16-byte chunks l, l+64, ...
 // of a row (32 columns each), so every load instruction reads 1 KB of one
 // row contiguously.  The activations of the lane's columns are read once
@@ -29,8 +29,13 @@ namespace {
 #ifndef W4_DOT2_RW
 #define W4_DOT2_RW 4
 #endif
-constexpr int kRowsWave = W4_DOT2_RW;    // weight rows per wave
-constexpr int kRowsWg = 4 * kRowsWave;   // weight rows per workgroup (4 waves)
+#ifndef W4_DOT2_WAVES
+#define W4_DOT2_WAVES 4
+#endif
+constexpr int kWavesWg = W4_DOT2_WAVES;         // waves per workgroup
+constexpr int kThreads = 64 * kWavesWg;
+constexpr int kRowsWave = W4_DOT2_RW;           // weight rows per wave
+constexpr int kRowsWg = kWavesWg * kRowsWave;   // weight rows per workgroup
 
 // 8 codes of a word -> 4 bf16 pairs (128 + q) in the order (0,4),(1,5),(2,6),(3,7).
 __device__ __forceinline__ void codes8(uint32_t p, const NibConst& nk, uint32_t (&o)[4]) {
@@ -90,7 +95,7 @@ template <> struct SZ<float> {
 
 // CH: 16-byte chunks per lane and row (K = 64 * 32 * CH).
 template <typename TS, typename TY, int MT, int CH>
-__global__ __launch_bounds__(256) void k_w4a16_dot2(
+__global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
     void* __restrict__ y) {
@@ -98,10 +103,10 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
   // staging lanes), scale tile [16][ng] as (s, -s*(128+zp)) float pairs
   // (region of 1024 pairs).
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  constexpr int XPER_ = (MT * CH * 2048 / 8 + 255) / 256;
+  constexpr int XPER_ = (MT * CH * 2048 / 8 + kThreads - 1) / kThreads;
   const int ng = (int)(K / g);
   u32x4* x_l = (u32x4*)lds;
-  float2* sz_l = (float2*)(lds + XPER_ * 256 * 16);
+  float2* sz_l = (float2*)(lds + XPER_ * kThreads * 16);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,22 +115,22 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
 
   // ---- 1. staging loads (activations, scale / zero-point tile), straight
   //         line: XPER / SPER per thread, indices clamped into range -------
-  constexpr int XPER = (MT * CH * 2048 / 8 + 255) / 256;  // 16-byte activation groups
+  constexpr int XPER = XPER_;  // 16-byte activation groups per thread
   const int xgroups = MT * (int)(K / 8);
   const u32x4* xg = (const u32x4*)x;
   u32x4 xv[XPER];
 #pragma unroll
   for (int r = 0; r < XPER; ++r) {
-    const int i = tid + 256 * r;
+    const int i = tid + kThreads * r;
     xv[r] = xg[i < xgroups ? i : xgroups - 1];
   }
   const int tile = kRowsWg * ng;  // <= 16 * 64 elements for K <= 8192, g >= 128
-  constexpr int SPER = (kRowsWg * 64 + 255) / 256;
+  constexpr int SPER = (kRowsWg * 64 + kThreads - 1) / kThreads;
   typedef typename SZ<TS>::T R;
   R sv[SPER], zv[SPER];
 #pragma unroll
   for (int r = 0; r < SPER; ++r) {
-    const int e = tid + 256 * r;
+    const int e = tid + kThreads * r;
     const int ee = e < tile ? e : tile - 1;
     const int rr = ee / ng, q = ee - rr * ng;
     const int64_t row = (n0 + rr) < N ? (n0 + rr) : (N - 1);
@@ -148,11 +153,11 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
   // ---- 3. LDS stores (wait for the staging loads only) ---------------------
   // unconditional: the LDS regions have room for every staging lane
 #pragma unroll
-  for (int r = 0; r < XPER; ++r) x_l[tid + 256 * r] = xv[r];
+  for (int r = 0; r < XPER; ++r) x_l[tid + kThreads * r] = xv[r];
 #pragma unroll
   for (int r = 0; r < SPER; ++r) {
     const float sf = SZ<TS>::f(sv[r]);
-    sz_l[tid + 256 * r] = float2{sf, -sf * (128.0f + SZ<TS>::f(zv[r]))};
+    sz_l[tid + kThreads * r] = float2{sf, -sf * (128.0f + SZ<TS>::f(zv[r]))};
   }
   __syncthreads();
 
@@ -220,8 +225,8 @@ __global__ __launch_bounds__(256) void k_w4a16_dot2(
 }
 
 size_t dot2_lds_bytes(int64_t m, int64_t k, int g) {
-  const int64_t xper = (m * k / 8 + 255) / 256;
-  return (size_t)(xper * 256 * 16 + ((kRowsWg * 64 + 255) / 256) * 256 * 8);
+  const int64_t xper = (m * k / 8 + kThreads - 1) / kThreads;
+  return (size_t)(xper * kThreads * 16 + ((kRowsWg * 64 + kThreads - 1) / kThreads) * kThreads * 8);
 }
 
 bool dot2_fits(int64_t m, int64_t k, int g) {
@@ -234,10 +239,10 @@ static void dot2_go(dim3 grid, hipStream_t st, const uint16_t* x, int64_t k, con
   const size_t lds = dot2_lds_bytes(MT, k, g);
   const int ch = (int)(k / 2048);
   switch (ch) {
-    case 1: k_w4a16_dot2<TS, TY, MT, 1><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    case 2: k_w4a16_dot2<TS, TY, MT, 2><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    case 3: k_w4a16_dot2<TS, TY, MT, 3><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    default: k_w4a16_dot2<TS, TY, MT, 4><<<grid, 256, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 1: k_w4a16_dot2<TS, TY, MT, 1><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 2: k_w4a16_dot2<TS, TY, MT, 2><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 3: k_w4a16_dot2<TS, TY, MT, 3><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    default: k_w4a16_dot2<TS, TY, MT, 4><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
   }
 }
 

@@ -58,10 +58,37 @@ __device__ __forceinline__ uint32_t code_of(float w, float s, float zpf) {
 // Eight codes -> one 32-bit word; element i sits in nibble i, so byte j holds
 // the even column in its low nibble ("Build a GPTQ INT4 Quantization Engine in
 // Python/NumPy", Step 4).
+//
+// The division is the costly part, so it is skipped where it cannot change
+// a code.  t = w * (1/s) + zp differs from the defined fl32(fl32(w/s) + zp)
+// by less than 2^-16 whenever |t| < 32 (|w/s| <= |t| + 15; the hardware
+// reciprocal (v_rcp_f32, within 1 ulp) and the product add at most 2 ulp of
+// w/s, the sum one rounding), and a
+// code only depends on which side of a half-integer t lies (the clamp
+// bounds -0.5 and 15.5 are half-integers too; for |t| >= 32 both values
+// clamp alike).  So unless some t of the word lies within 2^-12 of a
+// half-integer -- or 1/s overflows -- the codes from t are the defined ones;
+// otherwise the word is recomputed with the correctly rounded division.
 __device__ __forceinline__ uint32_t pack8(const float (&v)[8], float s, float zpf) {
-  uint32_t word = 0;
+  const float r = __builtin_amdgcn_rcpf(s);
+  float t[8];
+  bool near = !(r < 3.0e38f);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= code_of(v[i], s, zpf) << (4 * i);
+  for (int i = 0; i < 8; ++i) {
+    t[i] = v[i] * r + zpf;
+    near |= fabsf(fabsf(t[i] - rintf(t[i])) - 0.5f) < 0x1p-12f;
+  }
+  uint32_t word = 0;
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= code_of(v[i], s, zpf) << (4 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float c = fminf(fmaxf(rintf(t[i]), 0.0f), 15.0f);
+      word |= (uint32_t)c << (4 * i);
+    }
+  }
   return word;
 }
 
