@@ -237,13 +237,12 @@ template <typename TS, typename TY>
 static hipError_t gemm_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
                           const void* scales, const void* zeros, int64_t n, int g, void* y,
                           hipStream_t st) {
-  static bool attr_set = false;  // LDS above the 64 KB default
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_w4a16_gemm<TS, TY>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
+  hipError_t e = once_per_device(attr_done, [] {
+    return hipFuncSetAttribute((const void*)k_w4a16_gemm<TS, TY>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+  });
+  if (e != hipSuccess) return e;
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   k_w4a16_gemm<TS, TY><<<grid, 512, kGemmLds, st>>>(x, m, k, packed, scales, zeros, n, g, y,

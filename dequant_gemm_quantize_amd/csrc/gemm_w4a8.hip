@@ -270,14 +270,15 @@ template <typename TS, typename TY>
 static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                           const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
                           int g, void* y, hipStream_t st) {
-  static bool attr_set = false;  // LDS above the 64 KB default
-  if (!attr_set) {
+  static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
+  hipError_t e = once_per_device(attr_done, [] {
     for (const void* f : {(const void*)k_w4a8_gemm<TS, TY, true>, (const void*)k_w4a8_gemm<TS, TY, false>}) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4a8Lds);
-      if (e != hipSuccess) return e;
+      hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4a8Lds);
+      if (r != hipSuccess) return r;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (e != hipSuccess) return e;
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (g == BK)

@@ -5,9 +5,27 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/w4.h"
 
 namespace w4 {
+
+// Runs set() (an idempotent per-device setting such as a kernel's dynamic-LDS
+// limit) once for the current device and remembers success in `done`, one bit
+// per device.  Concurrent first calls may both run set(); that is harmless.
+// Devices past 63 are set on every call.
+template <typename F>
+hipError_t once_per_device(std::atomic<uint64_t>& done, F set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = set();
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
                                 uint8_t* packed, void* scales, void* zeros, int sz_dtype,
