@@ -60,86 +60,133 @@ __device__ __forceinline__ uint32_t code_of(float w, float s, float zpf) {
 // Python/NumPy", Step 4).
 //
 // The division is the costly part, so it is skipped where it cannot change
-// a code.  t = w * (1/s) + zp differs from the defined fl32(fl32(w/s) + zp)
+// a code.  t = fma(w, 1/s, zp) differs from the defined fl32(fl32(w/s) + zp)
 // by less than 2^-16 whenever |t| < 32 (|w/s| <= |t| + 15; the hardware
-// reciprocal (v_rcp_f32, within 1 ulp) and the product add at most 2 ulp of
-// w/s, the sum one rounding), and a
-// code only depends on which side of a half-integer t lies (the clamp
-// bounds -0.5 and 15.5 are half-integers too; for |t| >= 32 both values
-// clamp alike).  So unless some t of the word lies within 2^-12 of a
-// half-integer -- or 1/s overflows -- the codes from t are the defined ones;
-// otherwise the word is recomputed with the correctly rounded division.
-__device__ __forceinline__ uint32_t pack8(const float (&v)[8], float s, float zpf) {
-  const float r = __builtin_amdgcn_rcpf(s);
-  float t[8];
-  bool near = !(r < 3.0e38f);
+// reciprocal (v_rcp_f32, within 1 ulp) and the product add at most 1.5 ulp of
+// w/s, the two sums one rounding each).  A code only depends on which side
+// of a half-integer in 0.5 .. 14.5 t lies once it is clamped to [0, 15]
+// (clamping first changes no code: every t that clamps gives 0 or 15 either
+// way).  So unless some clamped t of the word lies within 2^-12 of a
+// half-integer -- or 1/s overflows -- rint of the clamped t is the defined
+// code; otherwise the word is recomputed with the correctly rounded division.
+// r = 1/s from v_rcp_f32.
+__device__ __forceinline__ uint32_t pack8(const float* v, float s, float r, float zpf) {
+  float c[8];
+  float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    t[i] = v[i] * r + zpf;
-    near |= fabsf(fabsf(t[i] - rintf(t[i])) - 0.5f) < 0x1p-12f;
+    const float t = fminf(fmaxf(fmaf(v[i], r, zpf), 0.0f), 15.0f);
+    c[i] = rintf(t);
+    dmax = fmaxf(dmax, fabsf(t - c[i]));  // exact difference, at most 0.5
   }
-  uint32_t word = 0;
-  if (near) {
+  if (!(dmax < 0.5f - 0x1p-12f) || !(r < 3.0e38f)) {
+    uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) word |= code_of(v[i], s, zpf) << (4 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float c = fminf(fmaxf(rintf(t[i]), 0.0f), 15.0f);
-      word |= (uint32_t)c << (4 * i);
-    }
+    return word;
   }
-  return word;
+  // even codes to the bytes of lo, odd codes to the bytes of hi (c is an
+  // integer in 0 .. 15, so the byte conversion is exact)
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * j], j, lo);
+    hi = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * j + 1], j, hi);
+  }
+  return lo | (hi << 4);
 }
 
 // ---------------------------------------------------------------------------
-// Quantize + pack, power-of-two groups of 32..512 elements.
+// Quantize + pack, groups of g = 32 L elements, L = 1, 2, 4, 8, 16.
 // The tensor is treated as a flat run of N*K elements: with K % g == 0 a
 // group never crosses a row, and flat group index == row * (K/g) + group.
-// Each lane owns one 8-element chunk; L = g/8 neighbouring lanes share a
-// group and reduce its min/max with xor butterflies.  U chunks per lane are
-// loaded up front (U*16 bytes of bf16 in flight per lane).
+// Each lane owns pieces of 32 consecutive elements (4 packed words); L
+// neighbouring lanes share a group and reduce its min/max with xor
+// butterflies, so the per-group work (scale, zero-point, reciprocal) is
+// shared by 4 words.  U pieces per lane are loaded up front.
 // ---------------------------------------------------------------------------
 template <typename TIn, typename TS, int L, int U>
 __global__ __launch_bounds__(256) void k_quantize_pack_sub(const void* __restrict__ w,
-                                                          int64_t nchunks,
+                                                          int64_t npieces,
                                                           uint32_t* __restrict__ packed,
                                                           TS* __restrict__ scales,
                                                           TS* __restrict__ zeros) {
   const int64_t base = (int64_t)blockIdx.x * (256 * U) + threadIdx.x;
-  float v[U][8];
+  float v[U][4][8];
+  if constexpr (sizeof(TIn) == 2 && U == 1) {
+    // bf16: the wave's 4 KB are loaded with consecutive lanes on consecutive
+    // 16-byte chunks (fully coalesced), then regrouped through LDS so that
+    // lane l holds chunks 4l .. 4l+3.  LDS slots are XOR-swizzled (slot
+    // c ^ ((c / 16) mod 4)) so both the stores and the strided reads are free
+    // of bank conflicts.
+    __shared__ u32x4 stg[4][256];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t c0 = 4 * ((int64_t)blockIdx.x * 256 + 64 * wv);
+    const int64_t nchunks = 4 * npieces;
+    u32x4 a[4];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t c = base + (int64_t)u * 256;
-    if (c < nchunks) {
-      Load8<TIn>::run(w, c, v[u]);
-    } else {
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = c0 + 64 * j + lane;
+      a[j] = c < nchunks ? ((const u32x4*)w)[c] : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const int cl = 64 * j + lane;
+      stg[wv][cl ^ ((cl >> 4) & 3)] = a[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = 4 * lane + j;
+      const u32x4 b = stg[wv][cl ^ ((cl >> 4) & 3)];
+      v[0][j][0] = bf16_lo(b.x); v[0][j][1] = bf16_hi(b.x); v[0][j][2] = bf16_lo(b.y); v[0][j][3] = bf16_hi(b.y);
+      v[0][j][4] = bf16_lo(b.z); v[0][j][5] = bf16_hi(b.z); v[0][j][6] = bf16_lo(b.w); v[0][j][7] = bf16_hi(b.w);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = base + (int64_t)u * 256;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (p < npieces) {
+          Load8<TIn>::run(w, 4 * p + j, v[u][j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[u][j][i] = 0.0f;
+        }
+      }
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t c = base + (int64_t)u * 256;
-    float mn = v[u][0], mx = v[u][0];
+    const int64_t p = base + (int64_t)u * 256;
+    float mn = v[u][0][0], mx = v[u][0][0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
-      mn = fminf(mn, v[u][i]);
-      mx = fmaxf(mx, v[u][i]);
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mn = fminf(mn, v[u][j][i]);
+        mx = fmaxf(mx, v[u][j][i]);
+      }
     mn = group_min<L>(mn);
     mx = group_max<L>(mx);
     TS st;
     float s;
     int zp;
     scale_zero<TS>(mn, mx, st, s, zp);
-    const uint32_t word = pack8(v[u], s, (float)zp);
-    if (c < nchunks) {
-      packed[c] = word;
+    const float r = __builtin_amdgcn_rcpf(s);
+    const float zpf = (float)zp;
+    u32x4 words;
+    words.x = pack8(v[u][0], s, r, zpf);
+    words.y = pack8(v[u][1], s, r, zpf);
+    words.z = pack8(v[u][2], s, r, zpf);
+    words.w = pack8(v[u][3], s, r, zpf);
+    if (p < npieces) {
+      ((u32x4*)packed)[p] = words;
       if ((threadIdx.x & (L - 1)) == 0) {
-        const int64_t gi = c / L;
+        const int64_t gi = p / L;
         scales[gi] = st;
-        zeros[gi] = (TS)(float)zp;
+        zeros[gi] = (TS)zpf;
       }
     }
   }
@@ -175,10 +222,11 @@ __global__ __launch_bounds__(256) void k_quantize_pack_wave(const void* __restri
   float s;
   int zp;
   scale_zero<TS>(mn, mx, st, s, zp);
+  const float r = __builtin_amdgcn_rcpf(s);
   for (int c = lane; c < cpg; c += kWave) {
     float v[8];
     Load8<TIn>::run(w, c0 + c, v);
-    packed[c0 + c] = pack8(v, s, (float)zp);
+    packed[c0 + c] = pack8(v, s, r, (float)zp);
   }
   if (lane == 0) {
     scales[grp] = st;
@@ -189,28 +237,31 @@ __global__ __launch_bounds__(256) void k_quantize_pack_wave(const void* __restri
 template <typename TIn, typename TS>
 static hipError_t launch_qp(const void* w, int64_t n, int64_t k, int g, uint8_t* packed, void* scales,
                             void* zeros, hipStream_t st) {
-  const int64_t nchunks = n * k / 8;
+  const int64_t npieces = n * k / 32;
   uint32_t* pk = (uint32_t*)packed;
   TS* sc = (TS*)scales;
   TS* zr = (TS*)zeros;
-  constexpr int U = sizeof(TIn) == 2 ? 4 : 2;
+#ifndef W4_QUANT_PIECES
+#define W4_QUANT_PIECES 1
+#endif
+  constexpr int U = sizeof(TIn) == 2 ? W4_QUANT_PIECES : 1;  // pieces per lane
   const int64_t per_block = 256 * U;
-  const dim3 grid((unsigned)((nchunks + per_block - 1) / per_block));
+  const dim3 grid((unsigned)((npieces + per_block - 1) / per_block));
   switch (g) {
     case 32:
-      k_quantize_pack_sub<TIn, TS, 4, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 1, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 64:
-      k_quantize_pack_sub<TIn, TS, 8, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 2, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 128:
-      k_quantize_pack_sub<TIn, TS, 16, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 4, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 256:
-      k_quantize_pack_sub<TIn, TS, 32, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 8, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 512:
-      k_quantize_pack_sub<TIn, TS, 64, U><<<grid, 256, 0, st>>>(w, nchunks, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 16, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     default: {
       const int64_t ngroups = n * (k / g);
