@@ -94,7 +94,9 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
   typedef typename GV<TS>::V4 V4;
   constexpr bool M1 = MT == 0;
   constexpr int T = M1 ? 1 : MT;
-  extern __shared__ float part[];  // [waves][RB][16 T tokens][16 rows]
+  // [waves][RB][16 T tokens][16 rows] partial sums; before them, 4 KB per wave
+  // for regrouping activations
+  extern __shared__ __attribute__((aligned(16))) float part[];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -103,17 +105,50 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
   const int64_t r0 = (int64_t)blockIdx.x * (16 * RB);
   const int64_t k0 = (int64_t)kSlice * w;
 
-  // activations of token block tb: token 16 tb + l16 (tokens past M repeat
-  // the last one and are never stored), columns k0 + 128 i + 32 h + 8 j .. + 7
+  // activations of token block tb: the MFMA operand of lane (l16, h) is token
+  // 16 tb + l16 (tokens past M repeat the last one and are never stored),
+  // columns k0 + 128 i + 32 h + 8 j .. + 7.
   u32x4 xf[kBlocks][4];
+  // Several tokens: the block's 16 x 128 activations are loaded with 16
+  // consecutive lanes on one token's 256 contiguous bytes (xr), then regrouped
+  // into operand order through the wave's own 4 KB of LDS, one 128-column
+  // block at a time.  LDS holds token t's 16-byte chunk c at slot c ^ t, so
+  // the stores and the operand reads (16 tokens, one chunk) are free of bank
+  // conflicts.  LDS operations of a wave complete in order, so the region is
+  // reused block after block without a wait.
+  u32x4 xr[kBlocks][4];
   auto xload = [&](int tb) {
-    int tok = 16 * tb + l16;
-    tok = tok < M ? tok : M - 1;
-    const u32x4* xp = (const u32x4*)(x + (int64_t)tok * K + k0 + 32 * h);
+    if constexpr (M1) {
+      const u32x4* xp = (const u32x4*)(x + k0 + 32 * h);
 #pragma unroll
-    for (int i = 0; i < kBlocks; ++i)
+      for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xf[i][j] = xp[16 * i + j];
+        for (int j = 0; j < 4; ++j) xf[i][j] = xp[16 * i + j];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int tok = 16 * tb + 4 * q + h;
+        tok = tok < M ? tok : M - 1;
+        const u32x4* xp = (const u32x4*)(x + (int64_t)tok * K + k0) + l16;
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i) xr[i][q] = xp[16 * i];
+      }
+    }
+  };
+  auto xstage = [&]() {
+    if constexpr (!M1) {
+      u32x4* st = (u32x4*)part + 256 * w;
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = 4 * q + h;
+          st[16 * t + (l16 ^ t)] = xr[i][q];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xf[i][j] = st[16 * l16 + ((4 * h + j) ^ l16)];
+      }
+    }
   };
 
   // ---- every load of the wave, in the order the arithmetic needs them ----
@@ -162,6 +197,7 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
 #pragma unroll
   for (int tb = 0; tb < T; ++tb) {
     if (tb > 0) xload(tb);
+    xstage();
     // block sums of x for every token (MFMA against ones)
     f32x4 xs[kBlocks];
 #pragma unroll
@@ -197,6 +233,7 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
   }
 
   // ---- partial sums of the waves' K slices -> LDS -> y --------------------
+  if constexpr (!M1) __syncthreads();  // every wave is done with its activation region
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float* p = part + (w * RB + rb) * (256 * T);
@@ -238,7 +275,9 @@ static void gemv_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* pack
   constexpr int T = MT == 0 ? 1 : MT;
   const int nw = (int)(k / kSlice);
   const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
-  const size_t lds = (size_t)nw * RB * 256 * T * sizeof(float);
+  const size_t part = (size_t)nw * RB * 256 * T * sizeof(float);
+  const size_t stage = MT == 0 ? 0 : (size_t)nw * 4096;  // activation regrouping
+  const size_t lds = part > stage ? part : stage;
   k_w4a16_gemv<TS, TY, RB, MT, G128><<<grid, 64 * nw, lds, st>>>(x, (int)m, k, packed, scales,
                                                                  zeros, n, g, (int)(k / g), y);
 }
