@@ -359,11 +359,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode(
   const int b0 = (wave * nblk) / WAVES;
   const int b1 = ((wave + 1) * nblk) / WAVES;
   const int nwb = b1 - b0;                                  // this wave's blocks
-  const int nw = (int)decode_wave_blocks(K, WAVES);         // region stride
   unsigned char* base = lds + (int64_t)wave * decode_wave_bytes(M, K, WAVES);
   float* sc_l = (float*)base;                               // [16][nblk]
   uint32_t* zb_l = (uint32_t*)(base + 16 * nblk * 4);       // [16][nblk]
-  u32x4* xs_l = (u32x4*)(base + 16 * nblk * 8);             // [M][nw*16]
+  // [M][nwb*16]; the region is sized for the largest wave share,
+  // decode_wave_blocks(K, WAVES) blocks
+  u32x4* xs_l = (u32x4*)(base + 16 * nblk * 8);
   f32x4* part = (f32x4*)(lds + (int64_t)WAVES * decode_wave_bytes(M, K, WAVES));
 
   const R* sg = (const R*)scales;
