@@ -288,33 +288,70 @@ hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k
 // Step 4): w = fl32((q - zp) * scale), rounded to the output type.
 // One lane per 32-bit word (8 codes); grid-stride over the flat tensor.
 // ---------------------------------------------------------------------------
-template <typename TS, int OUT>
+// The group of word c is c >> cpg_log2 when the words per group are a power
+// of two (every group size from 32 to 512), else c / cpg.
+// fp16 scales: q*s and zp*s are exact in fp32 (4 + 11 significant bits), so
+// fma(q, s, -zp*s) rounds the exact (q - zp)*s once, like the definition.
+// fp32 scales: the integer q - zp times s, one rounding.
+template <typename TS, int OUT, bool POW2>
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ packed,
                                                 const void* __restrict__ scales,
                                                 const void* __restrict__ zeros, int64_t nchunks,
-                                                int cpg, void* __restrict__ out) {
+                                                int cpg, int cpg_log2, void* __restrict__ out) {
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
        c += (int64_t)gridDim.x * 256) {
     const uint32_t word = packed[c];
-    const int64_t gi = c / cpg;
+    const int64_t gi = POW2 ? (c >> cpg_log2) : c / cpg;
     const float s = ScaleT<TS>::load(scales, gi);
-    const int zp = (int)ScaleT<TS>::load(zeros, gi);
+    const float zf = ScaleT<TS>::load(zeros, gi);
     float v[8];
+    if constexpr (sizeof(TS) == 2) {
+      const float b = -zf * s;  // exact
+      uint32_t lo = word & 0x0f0f0f0fu, hi = (word >> 4) & 0x0f0f0f0fu;
+      // opaque to the optimizer, so each byte converts with v_cvt_f32_ubyteN
+      // instead of an extract plus a conversion
+      asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)((int)((word >> (4 * i)) & 15u) - zp) * s;
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = fmaf((float)((lo >> (8 * i)) & 0xffu), s, b);
+        v[2 * i + 1] = fmaf((float)((hi >> (8 * i)) & 0xffu), s, b);
+      }
+    } else {
+      const int zp = (int)zf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (float)((int)((word >> (4 * i)) & 15u) - zp) * s;
+    }
     if constexpr (OUT == W4_F32) {
       f32x4* o = (f32x4*)out + 2 * c;
       o[0] = f32x4{v[0], v[1], v[2], v[3]};
       o[1] = f32x4{v[4], v[5], v[6], v[7]};
+    } else if constexpr (OUT == W4_BF16) {
+      // hardware round-to-nearest-even pairs
+      u32x4 r;
+      r.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[0], (__bf16)v[1]});
+      r.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2], (__bf16)v[3]});
+      r.z = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[4], (__bf16)v[5]});
+      r.w = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[6], (__bf16)v[7]});
+      ((u32x4*)out)[c] = r;
     } else {
       uint32_t h[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        h[i] = (OUT == W4_F16) ? f32_to_f16_bits(v[i]) : f32_to_bf16_bits(v[i]);
+      for (int i = 0; i < 8; ++i) h[i] = f32_to_f16_bits(v[i]);
       ((u32x4*)out)[c] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                                h[6] | (h[7] << 16)};
     }
   }
+}
+
+template <typename TS, bool POW2>
+static void launch_dq2(const uint32_t* pk, const void* scales, const void* zeros, int64_t nchunks,
+                       int cpg, int lg, void* out, int out_dtype, dim3 grid, hipStream_t st) {
+  if (out_dtype == W4_F32)
+    k_dequant<TS, W4_F32, POW2><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, cpg, lg, out);
+  else if (out_dtype == W4_F16)
+    k_dequant<TS, W4_F16, POW2><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, cpg, lg, out);
+  else
+    k_dequant<TS, W4_BF16, POW2><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, cpg, lg, out);
 }
 
 template <typename TS>
@@ -325,12 +362,14 @@ static hipError_t launch_dq(const uint8_t* packed, const void* scales, const voi
   if (blocks > 65536) blocks = 65536;
   const dim3 grid((unsigned)blocks);
   const uint32_t* pk = (const uint32_t*)packed;
-  if (out_dtype == W4_F32)
-    k_dequant<TS, W4_F32><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, g / 8, out);
-  else if (out_dtype == W4_F16)
-    k_dequant<TS, W4_F16><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, g / 8, out);
-  else
-    k_dequant<TS, W4_BF16><<<grid, 256, 0, st>>>(pk, scales, zeros, nchunks, g / 8, out);
+  const int cpg = g / 8;
+  if ((cpg & (cpg - 1)) == 0) {
+    int lg = 0;
+    while ((1 << lg) < cpg) ++lg;
+    launch_dq2<TS, true>(pk, scales, zeros, nchunks, cpg, lg, out, out_dtype, grid, st);
+  } else {
+    launch_dq2<TS, false>(pk, scales, zeros, nchunks, cpg, 0, out, out_dtype, grid, st);
+  }
   return hipGetLastError();
 }
 
