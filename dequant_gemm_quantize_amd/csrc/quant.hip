@@ -424,13 +424,89 @@ __global__ __launch_bounds__(256) void k_act_quant(const void* __restrict__ x, i
   if (threadIdx.x == 0) x_scale[row] = s;
 }
 
+// Eight activations -> eight int8 codes clamp(rint(x / s), -128, 127), packed
+// little-endian.  As in pack8, the division is skipped where it cannot
+// change a code: t = x * (1/s) is within 2^-15 of fl32(x / s) because
+// |x / s| <= 128 (the hardware reciprocal is within 1 ulp, the product and
+// the quotient round once each), and a code only depends on which side of a
+// half-integer t lies.  Words with a t within 2^-12 of a half-integer use the
+// correctly rounded division.
+__device__ __forceinline__ u32x2 act8(const float* v, float s, float r) {
+  float c[8];
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = v[i] * r;
+    c[i] = rintf(t);
+    dmax = fmaxf(dmax, fabsf(t - c[i]));
+  }
+  if (!(dmax < 0.5f - 0x1p-12f)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = rintf(v[i] / s);
+  }
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = (uint32_t)((int)fminf(fmaxf(c[i], -128.0f), 127.0f)) & 0xffu;
+  return u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+               b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+}
+
+// Rows of up to 8 NT R activations: one NT-lane block per token, the row held
+// in registers (R 8-element chunks per lane) between finding max|x| and
+// writing the codes, so it is read once.
+template <typename TX, int NT, int R>
+__global__ __launch_bounds__(NT) void k_act_quant_reg(const void* __restrict__ x, int64_t k,
+                                                     int8_t* __restrict__ xq,
+                                                     float* __restrict__ x_scale) {
+  __shared__ float red[NT / 64];
+  const int64_t row = blockIdx.x;
+  const int nch = (int)(k / 8);
+  const int64_t c0 = row * nch;
+  const int tid = threadIdx.x;
+  float v[R][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = tid + NT * r;
+    if (c < nch) {
+      Load8<TX>::run(x, c0 + c, v[r]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[r][i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[r][i]));
+  }
+  amax = group_max<kWave>(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
+  const float s = fmaxf(amax, 1e-8f) / 127.0f;
+  const float rs = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = tid + NT * r;
+    if (c < nch) ((u32x2*)xq)[c0 + c] = act8(v[r], s, rs);
+  }
+  if (tid == 0) x_scale[row] = s;
+}
+
 hipError_t launch_act_quant(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* xq,
                             float* x_scale, hipStream_t st) {
   const dim3 grid((unsigned)m);
-  if (x_dtype == W4_BF16)
-    k_act_quant<__bf16><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
-  else
-    k_act_quant<float><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+  const bool bf = x_dtype == W4_BF16;
+  if (m < 64 && k <= 8 * 1024) {  // few tokens: a wide block per token
+    if (bf) k_act_quant_reg<__bf16, 1024, 1><<<grid, 1024, 0, st>>>(x, k, xq, x_scale);
+    else k_act_quant_reg<float, 1024, 1><<<grid, 1024, 0, st>>>(x, k, xq, x_scale);
+  } else if (k <= 8 * 256 * 4) {
+    if (bf) k_act_quant_reg<__bf16, 256, 4><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+    else k_act_quant_reg<float, 256, 4><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+  } else {
+    if (bf) k_act_quant<__bf16><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+    else k_act_quant<float><<<grid, 256, 0, st>>>(x, k, xq, x_scale);
+  }
   return hipGetLastError();
 }
 

@@ -141,7 +141,11 @@ def test_dequant_workload(w4):
     assert np.array_equal(got, O.dequant(P, S, Z, 128, "bf16"))
 
 
-@pytest.mark.parametrize("m,k", [(1, 8192), (5, 640), (64, 4096), (3, 8), (2, 2056)])
+# shapes cover the three kernel paths: one wide block per token (m < 64,
+# k <= 8192), 256 lanes with the row in registers (k <= 8192), and the
+# two-pass kernel for longer rows
+@pytest.mark.parametrize("m,k", [(1, 8192), (5, 640), (64, 4096), (3, 8), (2, 2056), (70, 8192),
+                                 (3, 16400), (65, 8200)])
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 def test_act_quant(w4, m, k, kind):
     rng = np.random.default_rng(m * 31 + k)
