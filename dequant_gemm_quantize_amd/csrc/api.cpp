@@ -33,6 +33,9 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr int64_t kMaxK = (int64_t)1 << 23;      // columns
+constexpr int64_t kMaxElems = (int64_t)1 << 36;  // n*k, m*k, m*n
+
 // Shared checks of the weight-side arguments (shape, group, scale dtype).
 int check_weights(const char* fn, int64_t n, int64_t k, int32_t g, int sz_dtype) {
   if (n < 0) return fail(W4_EINVAL, "%s: n = %lld < 0", fn, (long long)n);
@@ -43,9 +46,22 @@ int check_weights(const char* fn, int64_t n, int64_t k, int32_t g, int sz_dtype)
     return fail(W4_EINVAL, "%s: k = %lld is not a multiple of group_size = %d", fn, (long long)k, g);
   if (sz_dtype != W4_F32 && sz_dtype != W4_F16)
     return fail(W4_EINVAL, "%s: scale dtype %d must be W4_F32 or W4_F16", fn, sz_dtype);
-  // keep flat element counts far from int64 overflow
-  if (n > ((int64_t)1 << 40) / k)
+  // Size limits that keep every kernel's 32-bit tile offsets (up to 256 rows
+  // of K elements) and launch sizes (under 2^32 work-items) in range.
+  if (k > kMaxK)
+    return fail(W4_EINVAL, "%s: k = %lld is too large (at most %lld)", fn, (long long)k,
+                (long long)kMaxK);
+  if (n > kMaxElems / k)
     return fail(W4_EINVAL, "%s: n * k = %lld * %lld is too large", fn, (long long)n, (long long)k);
+  return W4_OK;
+}
+
+// Shared checks of the token count against K and N (matmuls).
+int check_tokens(const char* fn, int64_t m, int64_t k, int64_t n) {
+  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
+  if (m > 0x7fffffffLL) return fail(W4_EINVAL, "%s: m = %lld is too large", fn, (long long)m);
+  if (m > kMaxElems / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  if (n > 0 && m > kMaxElems / n) return fail(W4_EINVAL, "%s: m * n is too large", fn);
   return W4_OK;
 }
 
@@ -118,11 +134,12 @@ int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
   static const char* fn = "quantize_act_int8";
   if (x_dtype != W4_F32 && x_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: x dtype %d must be W4_F32 or W4_BF16", fn, x_dtype);
-  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
   if (k <= 0 || k % 8 != 0)
     return fail(W4_EINVAL, "%s: k = %lld must be a positive multiple of 8", fn, (long long)k);
-  if (m > 0x7fffffffLL) return fail(W4_EINVAL, "%s: m = %lld is too large", fn, (long long)m);
-  if (m > ((int64_t)1 << 40) / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  if (k > kMaxK)
+    return fail(W4_EINVAL, "%s: k = %lld is too large (at most %lld)", fn, (long long)k,
+                (long long)kMaxK);
+  W4_TRY(check_tokens(fn, m, k, 0));
   if (m == 0) return ok();
   W4_TRY(check_ptr(fn, "x", x));
   W4_TRY(check_ptr(fn, "xq", xq));
@@ -141,8 +158,7 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
     return fail(W4_EINVAL, "%s: x dtype %d must be W4_F32 or W4_BF16", fn, x_dtype);
   if (y_dtype != W4_F32 && y_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: y dtype %d must be W4_F32 or W4_BF16", fn, y_dtype);
-  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
-  if (m > ((int64_t)1 << 40) / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  W4_TRY(check_tokens(fn, m, k, n));
   if (m == 0 || n == 0) return ok();
   W4_TRY(check_ptr(fn, "x", x));
   W4_TRY(check_ptr(fn, "packed", packed));
@@ -192,8 +208,7 @@ int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
   W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
   if (y_dtype != W4_F32 && y_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: y dtype %d must be W4_F32 or W4_BF16", fn, y_dtype);
-  if (m < 0) return fail(W4_EINVAL, "%s: m = %lld < 0", fn, (long long)m);
-  if (m > ((int64_t)1 << 40) / k) return fail(W4_EINVAL, "%s: m * k is too large", fn);
+  W4_TRY(check_tokens(fn, m, k, n));
   if (m == 0 || n == 0) return ok();
   W4_TRY(check_ptr(fn, "xq", xq));
   W4_TRY(check_ptr(fn, "packed", packed));

@@ -35,6 +35,8 @@
  *    thread.  No C++ exception crosses this interface.
  *  - M == 0 or N == 0 is a valid empty call: it returns W4_OK and enqueues
  *    nothing.  K must be > 0.
+ *  - Size limits (W4_EINVAL beyond them): K <= 2^23; N*K, M*K and M*N each
+ *    <= 2^36 elements; M < 2^31.
  *  - Inputs must be finite; NaN or Inf inputs, and group ranges that overflow
  *    the scale dtype (fp16 scales: (max - min) / 15 > 65504), give unspecified
  *    (but memory-safe) results.

@@ -78,6 +78,8 @@ def _err(lib):
     ((A, 2, 4, 128, 32, A, U, A, 1, None), "scales is not 16-byte aligned"),
     ((A, 2, 4, 128, 32, A, A, None, 1, None), "zeros is NULL"),
     ((A, 2, 1 << 30, 1 << 20, 32, A, A, A, 1, None), "too large"),
+    ((A, 2, 1 << 14, 1 << 23, 32, A, A, A, 1, None), "n * k"),
+    ((A, 2, 4, (1 << 23) + 32, 32, A, A, A, 1, None), "k = 8388640 is too large"),
 ])
 def test_quantize_pack_rejects(lib, args, msg):
     assert lib.quantize_pack_int4(*args) == -1
@@ -102,6 +104,8 @@ def test_empty_calls_are_noops(lib):
     ((A, 2, 1, 128, None, A, A, 1, 64, 32, A, 2, None), "packed is NULL"),
     ((A, 2, 1, 128, A, A, A, 1, 64, 32, U, 2, None), "y is not 16-byte aligned"),
     ((A, 2, 1, 128, A, A, A, 5, 64, 32, A, 2, None), "scale dtype"),
+    ((A, 2, 1 << 30, 32, A, A, A, 1, 128, 32, A, 2, None), "m * n is too large"),
+    ((A, 2, 1 << 29, 1 << 8, A, A, A, 1, 64, 32, A, 2, None), "m * k is too large"),
 ])
 def test_w4a16_rejects(lib, args, msg):
     assert lib.w4a16_matmul(*args) == -1
