@@ -1,6 +1,5 @@
-// Decode-time fused dequantize-matmul for 1 <= M <= 64 bf16 tokens, groups
-// that are multiples of 128 columns, K a multiple of 512 (up to 8192 for
-// M <= 16, 4096 above).
+// Decode-time fused dequantize-matmul for 1 <= M <= 64 bf16 tokens and
+// groups that are multiples of 128 columns, any K.
 // HBM-bound: the kernel exists to stream the packed codes at full bandwidth
 // with as little vector-ALU work per code as possible.
 //
@@ -25,6 +24,10 @@
 // block.  All loads of a wave are issued before any arithmetic and there is
 // no barrier until the waves add their partial sums through LDS at the end,
 // so each wave computes as soon as its own data arrives.
+// When K is not nw whole slices for at most 16 waves (8 with several token
+// blocks) -- the Llama-7B down projection, K = 11008, is one case -- a
+// workgroup owns 16 rows and up to 8 waves, and each wave loops over an
+// equal share of the slices, the last of which may be partial.
 #include "w4_common.h"
 #include "w4_internal.h"
 
@@ -85,8 +88,8 @@ __device__ __forceinline__ void put1(void* y, int64_t i, float v) {
 // the other with the wave's codes held in registers, so the codes are read
 // from memory once whatever M is.
 // G128: group size 128 (the four scales of a slice are contiguous).
-template <typename TS, typename TY, int RB, int MT, bool G128>
-__global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
+template <typename TS, typename TY, int RB, int MT, bool G128, bool SL>
+__global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g, int ng,
     void* __restrict__ y) {
@@ -103,7 +106,13 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
   const int nw = blockDim.x >> 6;
   const int l16 = lane & 15, h = lane >> 4;
   const int64_t r0 = (int64_t)blockIdx.x * (16 * RB);
-  const int64_t k0 = (int64_t)kSlice * w;
+  // SL: K is not nw whole slices, so the waves loop over slices w, w + nw,
+  // ... and the last slice may hold fewer than kBlocks blocks (nb): its
+  // missing blocks reuse the last block's addresses and contribute nothing
+  // (zero scale).  Otherwise wave w takes exactly slice w.
+  int64_t k0 = (int64_t)kSlice * w;
+  int nb = kBlocks;
+  auto blk = [&](int i) { return SL ? (i < nb ? i : nb - 1) : i; };
 
   // activations of token block tb: the MFMA operand of lane (l16, h) is token
   // 16 tb + l16 (tokens past M repeat the last one and are never stored),
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
 #pragma unroll
       for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xf[i][j] = xp[16 * i + j];
+        for (int j = 0; j < 4; ++j) xf[i][j] = xp[16 * blk(i) + j];
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
         tok = tok < M ? tok : M - 1;
         const u32x4* xp = (const u32x4*)(x + (int64_t)tok * K + k0) + l16;
 #pragma unroll
-        for (int i = 0; i < kBlocks; ++i) xr[i][q] = xp[16 * i];
+        for (int i = 0; i < kBlocks; ++i) xr[i][q] = xp[16 * blk(i)];
       }
     }
   };
@@ -151,85 +160,104 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
     }
   };
 
-  // ---- every load of the wave, in the order the arithmetic needs them ----
-  xload(0);
-  // scales and zero-points of the lane's row for the slice's four blocks
   int64_t rows[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int64_t r = r0 + 16 * rb + l16;
     rows[rb] = r < N ? r : N - 1;
   }
-  R sv[RB][kBlocks], zv[RB][kBlocks];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if constexpr (G128) {
-      const V4 s4 = *(const V4*)((const R*)scales + rows[rb] * ng + k0 / 128);
-      const V4 z4 = *(const V4*)((const R*)zeros + rows[rb] * ng + k0 / 128);
-#pragma unroll
-      for (int i = 0; i < kBlocks; ++i) {
-        sv[rb][i] = GV<TS>::at(s4, i);
-        zv[rb][i] = GV<TS>::at(z4, i);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kBlocks; ++i) {
-        const int gi = (int)(k0 + 128 * i) / g;
-        sv[rb][i] = ((const R*)scales)[rows[rb] * ng + gi];
-        zv[rb][i] = ((const R*)zeros)[rows[rb] * ng + gi];
-      }
-    }
-  }
-  // packed codes: row, columns k0 + 128 i + 32 h .. + 31 (16 bytes)
-  u32x4 wq[RB][kBlocks];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const uint8_t* base = packed + rows[rb] * (K / 2) + k0 / 2 + 16 * h;
-#pragma unroll
-    for (int i = 0; i < kBlocks; ++i) wq[rb][i] = __builtin_nontemporal_load((const u32x4*)(base + 64 * i));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const NibConst nk = NibConst::make();
   // lane holds tokens 16 tb + 4h + r (r = 0..3) of weight row l16
   f32x4 acc[RB][T];
 #pragma unroll
-  for (int tb = 0; tb < T; ++tb) {
-    if (tb > 0) xload(tb);
-    xstage();
-    // block sums of x for every token (MFMA against ones)
-    f32x4 xs[kBlocks];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int i = 0; i < kBlocks; ++i) {
-      xs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[i][j]), ones, xs[i], 0, 0, 0);
-    }
-    // row blocks: codes -> bf16 operands, MFMAs, scale and zero-point
+    for (int tb = 0; tb < T; ++tb) acc[rb][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // one slice: loads, then the products of every token block into acc
+  auto slice = [&]() {
+    // ---- every load of the wave, in the order the arithmetic needs them ----
+    xload(0);
+    // scales and zero-points of the lane's row for the slice's four blocks
+    R sv[RB][kBlocks], zv[RB][kBlocks];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      acc[rb][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (G128 && (!SL || (ng % kBlocks == 0 && nb == kBlocks))) {  // 4 aligned, in-range scales
+        const V4 s4 = *(const V4*)((const R*)scales + rows[rb] * ng + k0 / 128);
+        const V4 z4 = *(const V4*)((const R*)zeros + rows[rb] * ng + k0 / 128);
 #pragma unroll
-      for (int i = 0; i < kBlocks; ++i) {
-        const uint32_t wd[4] = {wq[rb][i].x, wq[rb][i].y, wq[rb][i].z, wq[rb][i].w};
-        f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < kBlocks; ++i) {
+          sv[rb][i] = GV<TS>::at(s4, i);
+          zv[rb][i] = GV<TS>::at(z4, i);
+        }
+      } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[i][j]),
-                                                      word_to_bf16(wd[j], nk), d, 0, 0, 0);
-        const float s = GV<TS>::f(sv[rb][i]);
-        const float nsz = -s * (128.0f + GV<TS>::f(zv[rb][i]));
-        if constexpr (M1) {
-          acc[rb][tb][0] = fmaf(s, d[0], fmaf(nsz, xs[i][0], acc[rb][tb][0]));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[rb][tb][r] = fmaf(s, d[r], fmaf(nsz, xs[i][r], acc[rb][tb][r]));
+        for (int i = 0; i < kBlocks; ++i) {
+          const int gi = (int)((k0 + 128 * blk(i)) / g);
+          sv[rb][i] = ((const R*)scales)[rows[rb] * ng + gi];
+          zv[rb][i] = ((const R*)zeros)[rows[rb] * ng + gi];
         }
       }
     }
+    // packed codes: row, columns k0 + 128 i + 32 h .. + 31 (16 bytes)
+    u32x4 wq[RB][kBlocks];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint8_t* base = packed + rows[rb] * (K / 2) + k0 / 2 + 16 * h;
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i)
+        wq[rb][i] = __builtin_nontemporal_load((const u32x4*)(base + 64 * blk(i)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int tb = 0; tb < T; ++tb) {
+      if (tb > 0) xload(tb);
+      xstage();
+      // block sums of x for every token (MFMA against ones)
+      f32x4 xs[kBlocks];
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        xs[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[i][j]), ones, xs[i], 0, 0, 0);
+      }
+      // row blocks: codes -> bf16 operands, MFMAs, scale and zero-point
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i) {
+          const uint32_t wd[4] = {wq[rb][i].x, wq[rb][i].y, wq[rb][i].z, wq[rb][i].w};
+          f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf[i][j]),
+                                                        word_to_bf16(wd[j], nk), d, 0, 0, 0);
+          const float s = (!SL || i < nb) ? GV<TS>::f(sv[rb][i]) : 0.0f;
+          const float nsz = -s * (128.0f + GV<TS>::f(zv[rb][i]));
+          if constexpr (M1) {
+            acc[rb][tb][0] = fmaf(s, d[0], fmaf(nsz, xs[i][0], acc[rb][tb][0]));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[rb][tb][r] = fmaf(s, d[r], fmaf(nsz, xs[i][r], acc[rb][tb][r]));
+          }
+        }
+      }
+    }
+  };
+  if constexpr (SL) {
+    const int nblk = (int)(K / 128);
+    const int nsl = (nblk + kBlocks - 1) / kBlocks;
+    for (int sl = w; sl < nsl; sl += nw) {
+      k0 = (int64_t)kSlice * sl;
+      nb = nblk - kBlocks * sl < kBlocks ? nblk - kBlocks * sl : kBlocks;
+      slice();
+    }
+  } else {
+    slice();
   }
 
   // ---- partial sums of the waves' K slices -> LDS -> y --------------------
@@ -262,24 +290,45 @@ __global__ __launch_bounds__(MT >= 2 ? 512 : 1024) void k_w4a16_gemv(
 }
 
 bool gemv_mfma_fits(int64_t m, int64_t k, int g) {
-  if (k % kSlice != 0 || g % 128 != 0 || m < 1) return false;
-  if (m <= 16) return k <= 16 * kSlice;
-  return m <= 64 && k <= 8 * kSlice;
+  (void)k;  // any K: K % g == 0, so K % 128 == 0
+  return g % 128 == 0 && m >= 1 && m <= 64;
+}
+
+// Waves per workgroup of the slice-loop form: at most 8, each taking the
+// same number of slices of K.
+static int gemv_waves(int64_t k) {
+  const int nsl = (int)((k / 128 + kBlocks - 1) / kBlocks);
+  const int per = (nsl + 7) / 8;
+  return (nsl + per - 1) / per;
+}
+// One whole slice per wave: the form without the slice loop.
+static bool gemv_one_slice(int64_t k, int mt) {
+  return k % kSlice == 0 && k / kSlice <= (mt >= 2 ? 8 : 16);
 }
 
 template <typename TS, typename TY, int MT, bool G128>
 static void gemv_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
                     const void* scales, const void* zeros, int64_t n, int g, void* y,
                     hipStream_t st) {
-  constexpr int RB = W4_GEMV_RB;
   constexpr int T = MT == 0 ? 1 : MT;
-  const int nw = (int)(k / kSlice);
-  const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
-  const size_t part = (size_t)nw * RB * 256 * T * sizeof(float);
-  const size_t stage = MT == 0 ? 0 : (size_t)nw * 4096;  // activation regrouping
-  const size_t lds = part > stage ? part : stage;
-  k_w4a16_gemv<TS, TY, RB, MT, G128><<<grid, 64 * nw, lds, st>>>(x, (int)m, k, packed, scales,
-                                                                 zeros, n, g, (int)(k / g), y);
+  const size_t stage_per_wave = MT == 0 ? 0 : 4096;  // activation regrouping
+  if (gemv_one_slice(k, MT)) {
+    constexpr int RB = W4_GEMV_RB;
+    const int nw = (int)(k / kSlice);
+    const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
+    const size_t part = (size_t)nw * RB * 256 * T * sizeof(float), stage = nw * stage_per_wave;
+    k_w4a16_gemv<TS, TY, RB, MT, G128, false><<<grid, 64 * nw, part > stage ? part : stage, st>>>(
+        x, (int)m, k, packed, scales, zeros, n, g, (int)(k / g), y);
+  } else {
+    // slice loop: one row block per workgroup (more workgroups, fewer
+    // registers per wave)
+    constexpr int RB = 1;
+    const int nw = gemv_waves(k);
+    const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
+    const size_t part = (size_t)nw * RB * 256 * T * sizeof(float), stage = nw * stage_per_wave;
+    k_w4a16_gemv<TS, TY, RB, MT, G128, true><<<grid, 64 * nw, part > stage ? part : stage, st>>>(
+        x, (int)m, k, packed, scales, zeros, n, g, (int)(k / g), y);
+  }
 }
 
 template <typename TS, typename TY, bool G128>
@@ -290,7 +339,13 @@ static void gemv_pick(const uint16_t* x, int64_t m, int64_t k, const uint8_t* pa
   else if (m <= 16) gemv_go<TS, TY, 1, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
   else if (m <= 32) gemv_go<TS, TY, 2, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
   else if (m <= 48) gemv_go<TS, TY, 3, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
-  else gemv_go<TS, TY, 4, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
+  else if (!gemv_one_slice(k, 4)) {
+    // The slice-loop form with four token blocks runs out of registers; two
+    // launches of up to 32 tokens each are faster.
+    gemv_go<TS, TY, 2, G128>(x, 32, k, packed, scales, zeros, n, g, y, st);
+    gemv_go<TS, TY, 2, G128>(x + 32 * k, m - 32, k, packed, scales, zeros, n, g,
+                             (char*)y + 32 * n * (int64_t)sizeof(TY), st);
+  } else gemv_go<TS, TY, 4, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
 }
 
 template <typename TS, typename TY>

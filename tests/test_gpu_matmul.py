@@ -83,7 +83,13 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           (1, 17, 8192, 1024, "f16", "bf16"), (16, 1, 512, 512, "f32", "bf16"),
           (17, 100, 1024, 128, "f16", "bf16"), (32, 300, 4096, 128, "f16", "bf16"),
           (33, 65, 512, 256, "f32", "f32"), (48, 40, 1536, 128, "f16", "bf16"),
-          (64, 129, 2048, 128, "f16", "f32")]
+          (64, 129, 2048, 128, "f16", "f32"),
+          # K not a whole number of 512-column slices per wave (the slice loop,
+          # with a partial last slice): Llama-7B down-projection K and others
+          (5, 70, 640, 128, "f16", "bf16"), (12, 33, 11008, 128, "f16", "f32"),
+          (24, 130, 1152, 128, "f32", "bf16"), (40, 64, 11008, 128, "f16", "bf16"),
+          (64, 96, 2688, 128, "f16", "bf16"), (20, 50, 1280, 256, "f16", "bf16"),
+          (6, 40, 9216, 128, "f16", "bf16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz,ykind", DECODE)
