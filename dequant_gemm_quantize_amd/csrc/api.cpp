@@ -167,10 +167,11 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
   W4_TRY(check_ptr(fn, "y", y));
   // Kernel choice (bf16 activations): one or two tokens -> the dot2 GEMV;
   // up to four tokens with the activations fitting in LDS -> the LDS decode
-  // kernel; up to 64 tokens, K a multiple of 512 -> the MFMA GEMV; other
-  // shapes up to 16 tokens -> the decode kernels; more tokens -> the MFMA
-  // GEMM; everything else (fp32 activations, odd group sizes) -> the
-  // general kernel.
+  // kernel; up to 128 tokens, groups of a multiple of 128 -> the MFMA GEMV
+  // (in launches of up to 64 tokens); other shapes up to 16 tokens -> the
+  // decode kernels; more tokens -> the MFMA GEMM; everything else (fp32
+  // activations, group sizes that are not a multiple of 128) -> the general
+  // kernel.
   if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size))
     return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
                                             group_size, y, y_dtype, stream),

@@ -1,5 +1,6 @@
-// Decode-time fused dequantize-matmul for 1 <= M <= 64 bf16 tokens and
-// groups that are multiples of 128 columns, any K.
+// Decode-time fused dequantize-matmul for 1 <= M <= 64 bf16 tokens per
+// launch (up to 128 in launches of 64) and groups that are multiples of 128
+// columns, any K.
 // HBM-bound: the kernel exists to stream the packed codes at full bandwidth
 // with as little vector-ALU work per code as possible.
 //
@@ -291,7 +292,7 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
 
 bool gemv_mfma_fits(int64_t m, int64_t k, int g) {
   (void)k;  // any K: K % g == 0, so K % 128 == 0
-  return g % 128 == 0 && m >= 1 && m <= 64;
+  return g % 128 == 0 && m >= 1 && m <= 128;
 }
 
 // Waves per workgroup of the slice-loop form: at most 8, each taking the
@@ -348,12 +349,20 @@ static void gemv_pick(const uint16_t* x, int64_t m, int64_t k, const uint8_t* pa
   } else gemv_go<TS, TY, 4, G128>(x, m, k, packed, scales, zeros, n, g, y, st);
 }
 
+// More than 64 tokens: launches of up to 64 tokens each, every one reading
+// the codes again.  Up to 128 tokens this beats the prefill GEMM, whose
+// 256 x 128 tiles then cover few CUs (N / 128 workgroups).
 template <typename TS, typename TY>
 static void gemv_pick(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
                       const void* scales, const void* zeros, int64_t n, int g, void* y,
                       hipStream_t st) {
-  if (g == 128) gemv_pick<TS, TY, true>(x, m, k, packed, scales, zeros, n, g, y, st);
-  else gemv_pick<TS, TY, false>(x, m, k, packed, scales, zeros, n, g, y, st);
+  for (int64_t t0 = 0; t0 < m; t0 += 64) {
+    const int64_t mc = m - t0 < 64 ? m - t0 : 64;
+    const uint16_t* xc = x + t0 * k;
+    void* yc = (char*)y + t0 * n * (int64_t)sizeof(TY);
+    if (g == 128) gemv_pick<TS, TY, true>(xc, mc, k, packed, scales, zeros, n, g, yc, st);
+    else gemv_pick<TS, TY, false>(xc, mc, k, packed, scales, zeros, n, g, yc, st);
+  }
 }
 
 hipError_t launch_w4a16_gemv(const void* x, int64_t m, int64_t k, const uint8_t* packed,

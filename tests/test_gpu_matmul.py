@@ -72,10 +72,10 @@ def test_w4a16_bf16(w4, m, n, k, g, sz):
     assert err <= TOL["bf16"], err
 
 
-# Decode shapes for the MFMA GEMV (M <= 64, K a multiple of 512, groups a
-# multiple of 128): one to sixteen 512-column slices, one to four blocks of
-# 16 tokens with ragged last blocks, ragged row counts (workgroups of 32
-# rows), groups spanning several blocks, both scale and output dtypes.
+# Decode shapes for the MFMA GEMV (M <= 128, groups a multiple of 128): one to
+# sixteen 512-column slices, one to four blocks of 16 tokens with ragged last
+# blocks, ragged row counts (workgroups of 32 or 16 rows), groups spanning
+# several blocks, both scale and output dtypes.
 DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           (2, 100, 1536, 128, "f32", "bf16"), (3, 77, 2048, 256, "f16", "bf16"),
           (5, 64, 8192, 128, "f16", "bf16"), (8, 130, 4096, 512, "f32", "f32"),
@@ -89,7 +89,10 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           (5, 70, 640, 128, "f16", "bf16"), (12, 33, 11008, 128, "f16", "f32"),
           (24, 130, 1152, 128, "f32", "bf16"), (40, 64, 11008, 128, "f16", "bf16"),
           (64, 96, 2688, 128, "f16", "bf16"), (20, 50, 1280, 256, "f16", "bf16"),
-          (6, 40, 9216, 128, "f16", "bf16")]
+          (6, 40, 9216, 128, "f16", "bf16"),
+          # 65..128 tokens: launches of up to 64 tokens
+          (65, 48, 1024, 128, "f16", "bf16"), (100, 70, 11008, 128, "f16", "f32"),
+          (128, 33, 2048, 256, "f32", "bf16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz,ykind", DECODE)
