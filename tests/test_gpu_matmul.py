@@ -92,7 +92,9 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           (6, 40, 9216, 128, "f16", "bf16"),
           # 65..128 tokens: launches of up to 64 tokens
           (65, 48, 1024, 128, "f16", "bf16"), (100, 70, 11008, 128, "f16", "f32"),
-          (128, 33, 2048, 256, "f32", "bf16")]
+          (128, 33, 2048, 256, "f32", "bf16"),
+          # three tokens at K = 4096: the fast LDS decode kernel
+          (3, 70, 4096, 128, "f16", "bf16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz,ykind", DECODE)
