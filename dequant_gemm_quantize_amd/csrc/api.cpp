@@ -165,7 +165,7 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
   W4_TRY(check_ptr(fn, "scales", scales));
   W4_TRY(check_ptr(fn, "zeros", zeros));
   W4_TRY(check_ptr(fn, "y", y));
-  // Kernel choice (bf16 activations): one or two tokens -> the dot2 GEMV;
+  // Kernel choice (bf16 activations): one token -> the dot2 GEMV;
   // up to four tokens with the activations fitting in LDS -> the LDS decode
   // kernel; up to 128 tokens, groups of a multiple of 128 -> the MFMA GEMV
   // (in launches of up to 64 tokens); other shapes up to 16 tokens -> the

@@ -173,11 +173,22 @@ def test_workload_single_layer_fp32(w4):
 
 
 @pytest.mark.parametrize("name", ["Wa", "Wb"])
-@pytest.mark.parametrize("m", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 16, 32])
 def test_workload_llama_decode(w4, name, m):
-    """Llama-7B shapes at M = 1 (decode) and 4..32 (small batch)."""
+    """Llama-7B shapes at M = 1 (decode) and 2..32 (small batch)."""
     t, (P, S, Z) = quantized(name, 128, "f16")
     x = WL.activation(2 if m == 1 else 3, m, 4096)
+    y = run_w4a16(w4, x.data, "bf16", dev_weights(P, S, Z, "f16"), 128, "bf16")
+    ref = O.matmul_w4a16_f64(x.as_f32(), P, S, Z, 128)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("m", [1, 3, 17, 64, 100])
+def test_workload_llama_down_decode(w4, m):
+    """The Llama-7B down projection [4096, 11008] at decode and small-batch
+    sizes (K is not a whole number of 512-column slices per wave)."""
+    t, (P, S, Z) = quantized("Wd", 128, "f16")
+    x = WL.activation(3, m, 11008)
     y = run_w4a16(w4, x.data, "bf16", dev_weights(P, S, Z, "f16"), 128, "bf16")
     ref = O.matmul_w4a16_f64(x.as_f32(), P, S, Z, 128)
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL["bf16"]
