@@ -94,7 +94,9 @@ template <> struct SZ<float> {
 
 }  // namespace
 
-// CH: 16-byte chunks per lane and row (K = 64 * 32 * CH).
+// CH: 16-byte chunks (32 columns) per lane and row, K <= 2048 CH.  Lane l
+// takes chunks l, l + 64, ...; chunks past the row's K / 32 reuse its last
+// chunk's addresses and contribute nothing (zero scale pair).
 template <typename TS, typename TY, int MT, int CH>
 __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     const int i = tid + kThreads * r;
     xv[r] = xg[i < xgroups ? i : xgroups - 1];
   }
-  const int tile = kRowsWg * ng;  // <= 16 * 64 elements for K <= 8192, g >= 128
-  constexpr int SPER = (kRowsWg * 64 + kThreads - 1) / kThreads;
+  const int tile = kRowsWg * ng;  // <= 16 * 16 CH elements for g >= 128
+  constexpr int SPER = (kRowsWg * 16 * CH + kThreads - 1) / kThreads;
   typedef typename SZ<TS>::T R;
   R sv[SPER], zv[SPER];
 #pragma unroll
@@ -140,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   }
 
   // ---- 2. codes of the wave's rows: kRowsWave x CH 16-byte loads per lane --
+  const int nchunk = (int)(K / 32);
   u32x4 wq[kRowsWave][CH];
 #pragma unroll
   for (int r = 0; r < kRowsWave; ++r) {
@@ -147,7 +150,10 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     n = n < N ? n : N - 1;
     const u32x4* row = (const u32x4*)(packed + n * (K / 2));
 #pragma unroll
-    for (int c = 0; c < CH; ++c) wq[r][c] = __builtin_nontemporal_load(row + lane + 64 * c);
+    for (int c = 0; c < CH; ++c) {
+      const int ci = lane + 64 * c;
+      wq[r][c] = __builtin_nontemporal_load(row + (ci < nchunk ? ci : nchunk - 1));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -170,7 +176,9 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       // columns 32*(lane + 64c) .. +31 = 16-byte groups 4*(lane + 64c) .. +3
-      const u32x4* src = x_l + (int64_t)m * (K / 8) + 4 * (lane + 64 * c);
+      // (past K: the staged copies of the last group, never used)
+      const int ci = lane + 64 * c < nchunk ? lane + 64 * c : nchunk - 1;
+      const u32x4* src = x_l + (int64_t)m * (K / 8) + 4 * ci;
       float s = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -188,9 +196,9 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
 
   // ---- rows: dot products, scale, zero-point correction, wave sums --------
   const NibConst nk = NibConst::make();
-  int gq[CH];  // group of the lane's chunk c
+  int gq[CH];  // group of the lane's chunk c, or -1 past the row's end
 #pragma unroll
-  for (int c = 0; c < CH; ++c) gq[c] = (32 * (lane + 64 * c)) / g;
+  for (int c = 0; c < CH; ++c) gq[c] = lane + 64 * c < nchunk ? (32 * (lane + 64 * c)) / g : -1;
 #pragma unroll
   for (int r = 0; r < kRowsWave; ++r) {
     const int rr = wave * kRowsWave + r;
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const float2 sc = sz_l[rr * ng + gq[c]];
+      const float2 sc = gq[c] >= 0 ? sz_l[rr * ng + gq[c]] : float2{0.0f, 0.0f};
       const uint32_t w4[4] = {wq[r][c].x, wq[r][c].y, wq[r][c].z, wq[r][c].w};
       float d[MT];
 #pragma unroll
@@ -225,27 +233,33 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   }
 }
 
+static int dot2_ch(int64_t k) { return (int)((k + 2047) / 2048); }
+
 size_t dot2_lds_bytes(int64_t m, int64_t k, int g) {
-  const int64_t xper = (m * k / 8 + kThreads - 1) / kThreads;
-  return (size_t)(xper * kThreads * 16 + ((kRowsWg * 64 + kThreads - 1) / kThreads) * kThreads * 8);
+  (void)g;
+  const int ch = dot2_ch(k);
+  const int64_t xper = (m * ch * 2048 / 8 + kThreads - 1) / kThreads;
+  return (size_t)(xper * kThreads * 16 + ((kRowsWg * 16 * ch + kThreads - 1) / kThreads) * kThreads * 8);
 }
 
 bool dot2_fits(int64_t m, int64_t k, int g) {
   // One token: two already run faster in the LDS decode kernel (8.3 against
-  // 9.5 us on [11008,4096]).
-  return k % 2048 == 0 && g >= 128 && m == 1 && k <= 8192;
+  // 9.5 us on [11008,4096]).  Groups of at least 128 keep the scale tile
+  // within 16 CH pairs per row.
+  return m == 1 && g >= 128 && k % 32 == 0 && k <= 6 * 2048;
 }
 
 template <typename TS, typename TY, int MT>
 static void dot2_go(dim3 grid, hipStream_t st, const uint16_t* x, int64_t k, const uint8_t* packed,
                     const void* scales, const void* zeros, int64_t n, int g, void* y) {
   const size_t lds = dot2_lds_bytes(MT, k, g);
-  const int ch = (int)(k / 2048);
-  switch (ch) {
+  switch (dot2_ch(k)) {
     case 1: k_w4a16_dot2<TS, TY, MT, 1><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
     case 2: k_w4a16_dot2<TS, TY, MT, 2><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
     case 3: k_w4a16_dot2<TS, TY, MT, 3><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    default: k_w4a16_dot2<TS, TY, MT, 4><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 4: k_w4a16_dot2<TS, TY, MT, 4><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 5: k_w4a16_dot2<TS, TY, MT, 5><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    default: k_w4a16_dot2<TS, TY, MT, 6><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
   }
 }
 

@@ -94,7 +94,11 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           (65, 48, 1024, 128, "f16", "bf16"), (100, 70, 11008, 128, "f16", "f32"),
           (128, 33, 2048, 256, "f32", "bf16"),
           # three tokens at K = 4096: the fast LDS decode kernel
-          (3, 70, 4096, 128, "f16", "bf16")]
+          (3, 70, 4096, 128, "f16", "bf16"),
+          # one token, K not a multiple of 2048 (the dot2 kernel's partial
+          # last chunk round), up to its K = 12288 limit
+          (1, 50, 11008, 128, "f16", "bf16"), (1, 33, 2560, 256, "f32", "f32"),
+          (1, 20, 12288, 128, "f16", "bf16"), (1, 7, 640, 128, "f16", "bf16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz,ykind", DECODE)
