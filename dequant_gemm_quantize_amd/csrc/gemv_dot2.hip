@@ -35,8 +35,10 @@ namespace {
 #endif
 constexpr int kWavesWg = W4_DOT2_WAVES;         // waves per workgroup
 constexpr int kThreads = 64 * kWavesWg;
-constexpr int kRowsWave = W4_DOT2_RW;           // weight rows per wave
-constexpr int kRowsWg = kWavesWg * kRowsWave;   // weight rows per workgroup
+// Weight rows per wave: W4_DOT2_RW up to K = 8192; two above, where the
+// codes and activations of six chunk rounds leave registers for no more
+// (measured on [4096,11008]: 9.0 us with two rows, 10.0 with four).
+constexpr int rows_wave(int ch) { return ch <= 4 ? W4_DOT2_RW : 2; }
 
 // 8 codes of a word -> 4 bf16 pairs (128 + q) in the order (0,4),(1,5),(2,6),(3,7).
 __device__ __forceinline__ void codes8(uint32_t p, const NibConst& nk, uint32_t (&o)[4]) {
@@ -106,6 +108,8 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   // staging lanes), scale tile [16][ng] as (s, -s*(128+zp)) float pairs
   // (region of 1024 pairs).
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  constexpr int kRowsWave = rows_wave(CH);
+  constexpr int kRowsWg = kWavesWg * kRowsWave;
   constexpr int XPER_ = (MT * CH * 2048 / 8 + kThreads - 1) / kThreads;
   const int ng = (int)(K / g);
   u32x4* x_l = (u32x4*)lds;
@@ -238,8 +242,9 @@ static int dot2_ch(int64_t k) { return (int)((k + 2047) / 2048); }
 size_t dot2_lds_bytes(int64_t m, int64_t k, int g) {
   (void)g;
   const int ch = dot2_ch(k);
+  const int rows_wg = kWavesWg * rows_wave(ch);
   const int64_t xper = (m * ch * 2048 / 8 + kThreads - 1) / kThreads;
-  return (size_t)(xper * kThreads * 16 + ((kRowsWg * 16 * ch + kThreads - 1) / kThreads) * kThreads * 8);
+  return (size_t)(xper * kThreads * 16 + ((rows_wg * 16 * ch + kThreads - 1) / kThreads) * kThreads * 8);
 }
 
 bool dot2_fits(int64_t m, int64_t k, int g) {
@@ -266,7 +271,8 @@ static void dot2_go(dim3 grid, hipStream_t st, const uint16_t* x, int64_t k, con
 hipError_t launch_w4a16_dot2(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
                              int g, void* y, int y_dtype, hipStream_t st) {
-  const dim3 grid((unsigned)((n + kRowsWg - 1) / kRowsWg));
+  const int rows_wg = kWavesWg * rows_wave(dot2_ch(k));
+  const dim3 grid((unsigned)((n + rows_wg - 1) / rows_wg));
   const uint16_t* xb = (const uint16_t*)x;
   const bool sh = sz_dtype == W4_F16, yf = y_dtype == W4_F32;
   (void)m;  // one token (dot2_fits)
