@@ -62,6 +62,11 @@ hipError_t launch_w4a8_gemv(const int8_t* xq, const float* xs, int64_t m, int64_
                             const uint8_t* packed, const void* scales, const void* zeros,
                             int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st);
 bool w4a8_gemv_fits(int64_t m, int64_t k, int g);
+hipError_t launch_w4a8_gemv_mfma(const int8_t* xq, const float* xs, int64_t m, int64_t k,
+                                 const uint8_t* packed, const void* scales, const void* zeros,
+                                 int sz_dtype, int64_t n, int g, void* y, int y_dtype,
+                                 hipStream_t st);
+bool w4a8_gemv_mfma_fits(int64_t m, int64_t k, int g);
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                             const uint8_t* packed, const void* scales, const void* zeros,
                             int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st);

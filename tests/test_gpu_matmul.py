@@ -242,14 +242,18 @@ def test_w4a8(w4, m, n, k, g, ykind):
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
 
 
-# Shapes for the int8-MFMA kernel (M > 16, group a multiple of 128): several
+# Shapes for the int8-MFMA GEMM (M > 16, group a multiple of 128): several
 # 256 x 128 tiles with ragged M and N, one K step only, groups of 256 (two K
 # steps per group), fp32 scales and zero-points; then the one-token GEMV.
 W8_GEMM = [(17, 130, 128, 128, "f16"), (257, 1000, 2048, 128, "f16"), (300, 200, 768, 256, "f16"),
            (512, 384, 1024, 128, "f32"), (64, 129, 640, 640, "f16"),
            # one token, group 128, K = 2048 .. 8192: the dot4 GEMV (ragged row counts)
            (1, 1, 2048, 128, "f16"), (1, 300, 4096, 128, "f32"), (1, 17, 6144, 128, "f16"),
-           (1, 1000, 8192, 128, "f16")]
+           (1, 1000, 8192, 128, "f16"),
+           # up to 16 tokens, groups a multiple of 128, any K: the int8 MFMA GEMV
+           # (slices shared by up to 8 waves, partial last slice)
+           (1, 50, 28672, 128, "f16"), (7, 33, 1280, 256, "f16"), (12, 40, 11008, 128, "f32"),
+           (2, 17, 8192, 128, "f16"), (16, 64, 128, 128, "f16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz", W8_GEMM)
