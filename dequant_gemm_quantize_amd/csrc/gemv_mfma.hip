@@ -201,16 +201,39 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
         }
       }
     }
-    // packed codes: row, columns k0 + 128 i + 32 h .. + 31 (16 bytes)
-    u32x4 wq[RB][kBlocks];
+    // packed codes, in 256-byte row runs: row 16 rb + 4 j + h of the
+    // workgroup, 16-byte chunk l16 of the slice's run (chunks past the
+    // slice's blocks repeat its last chunk)
+    u32x4 cr[RB][4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint8_t* base = packed + rows[rb] * (K / 2) + k0 / 2 + 16 * h;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < kBlocks; ++i)
-        wq[rb][i] = __builtin_nontemporal_load((const u32x4*)(base + 64 * blk(i)));
-    }
+      for (int j = 0; j < 4; ++j) {
+        int64_t rj = r0 + 16 * rb + 4 * j + h;
+        rj = rj < N ? rj : N - 1;
+        const int c = l16 < 4 * nb ? l16 : 4 * nb - 1;
+        cr[rb][j] = __builtin_nontemporal_load((const u32x4*)(packed + rj * (K / 2) + k0 / 2) + c);
+      }
     __builtin_amdgcn_sched_barrier(0);
+    // regroup through the wave's LDS region into operand order: lane (l16,
+    // h) takes row l16, chunk 4 i + h of block i (row t's chunk c at slot
+    // c ^ t, free of bank conflicts; LDS operations of a wave complete in
+    // order, so the region is reused row block after row block and then by
+    // the activations)
+    u32x4 wq[RB][kBlocks];
+    {
+      u32x4* st = (u32x4*)part + 256 * w;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 4 * j + h;
+          st[16 * t + (l16 ^ t)] = cr[rb][j];
+        }
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i) wq[rb][i] = st[16 * l16 + ((4 * blk(i) + h) ^ l16)];
+      }
+    }
 
 #pragma unroll
     for (int tb = 0; tb < T; ++tb) {
@@ -262,7 +285,7 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
   }
 
   // ---- partial sums of the waves' K slices -> LDS -> y --------------------
-  if constexpr (!M1) __syncthreads();  // every wave is done with its activation region
+  __syncthreads();  // every wave is done with its regrouping region
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float* p = part + (w * RB + rb) * (256 * T);
@@ -312,7 +335,7 @@ static void gemv_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* pack
                     const void* scales, const void* zeros, int64_t n, int g, void* y,
                     hipStream_t st) {
   constexpr int T = MT == 0 ? 1 : MT;
-  const size_t stage_per_wave = MT == 0 ? 0 : 4096;  // activation regrouping
+  const size_t stage_per_wave = 4096;  // code and activation regrouping
   if (gemv_one_slice(k, MT)) {
     constexpr int RB = W4_GEMV_RB;
     const int nw = (int)(k / kSlice);
