@@ -20,9 +20,11 @@
 // Work layout.  A workgroup owns 16 * RB weight rows over all of K and has
 // one wave per 512-column slice of K.  Each wave keeps the activations of
 // its slice in registers for the whole kernel and streams the codes of its
-// slice for all 16 * RB rows: lane l serves weight row l mod 16 and the
-// 32-column quarter l div 16 of each 128-column block, one 16-byte load per
-// block.  All loads of a wave are issued before any arithmetic and there is
+// slice for all 16 * RB rows.  In the MFMA operands lane l serves weight row
+// l mod 16 and the 32-column quarter l div 16 of each 128-column block; the
+// codes are loaded instead as 256-byte runs of one row per 16 lanes (HBM
+// serves long runs better) and regrouped through the wave's own 4 KB of
+// LDS.  All loads of a wave are issued before any arithmetic and there is
 // no barrier until the waves add their partial sums through LDS at the end,
 // so each wave computes as soon as its own data arrives.
 // When K is not nw whole slices for at most 16 waves (8 with several token
