@@ -272,6 +272,24 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
                                         "GB/s": round((n * k // 2 + 4 * n * (k // g) + 2 * n * k) / dsec / 1e9, 1)}
             del dq
         del wt
+        if name == "Wd":
+            # the down projection [4096,11008] at decode and small-batch sizes
+            # (K = 11008 is not a whole number of 512-column slices per wave)
+            cpd = [(p, s, z)] + [tuple(a.clone() for a in (p, s, z)) for _ in range(R - 1)]
+            down = {}
+            for m in (1, 16, 64, 128):
+                xd = to_dev(WL.activation(2 if m == 1 else 3, m, k))
+                yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                fn = lambda i, xd=xd, yd=yd: w4.w4a16_matmul(xd, *cpd[i % R], g, out=yd)
+                for i in range(3):
+                    fn(i)
+                sec = time_region(fn, reps)
+                down[f"M={m}"] = {"us": round(sec * 1e6, 3),
+                                  "GB/s": round(w4a16_bytes(m, n, k, g) / sec / 1e9, 1),
+                                  "TFLOP/s": round(2 * m * n * k / sec / 1e12, 3)}
+            out["w4a16_down_proj_4096x11008"] = down
+            log(f"down projection: {json.dumps(down)}")
+            del cpd
         x = to_dev(WL.activation(4, 2048, k))
         y = torch.empty((2048, n), dtype=torch.bfloat16, device=dev)
         fn = lambda i: w4.w4a16_matmul(x, p, s, z, g, out=y)
@@ -297,7 +315,7 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
     del wt, qo
     cp8 = [(p, s, z)] + [tuple(a.clone() for a in (p, s, z)) for _ in range(3)]
     w8 = {}
-    for m in (1, 512):
+    for m in (1, 2, 8, 16, 512):
         xb = to_dev(WL.activation(5, m, 8192))
         xq = torch.empty((m, k), dtype=torch.int8, device=dev)
         xs = torch.empty((m,), dtype=torch.float32, device=dev)
