@@ -247,9 +247,11 @@ def test_w4a8(w4, m, n, k, g, ykind):
 # steps per group), fp32 scales and zero-points; then the one-token GEMV.
 W8_GEMM = [(17, 130, 128, 128, "f16"), (257, 1000, 2048, 128, "f16"), (300, 200, 768, 256, "f16"),
            (512, 384, 1024, 128, "f32"), (64, 129, 640, 640, "f16"),
-           # one token, group 128, K = 2048 .. 8192: the dot4 GEMV (ragged row counts)
+           # one to four tokens, group 128, K = 2048 .. 8192: the dot4 GEMV (ragged
+           # row counts)
            (1, 1, 2048, 128, "f16"), (1, 300, 4096, 128, "f32"), (1, 17, 6144, 128, "f16"),
-           (1, 1000, 8192, 128, "f16"),
+           (1, 1000, 8192, 128, "f16"), (3, 300, 4096, 128, "f32"), (4, 100, 2048, 128, "f16"),
+           (4, 33, 8192, 128, "f16"),
            # up to 16 tokens, groups a multiple of 128, any K: the int8 MFMA GEMV
            # (slices shared by up to 8 waves, partial last slice)
            (1, 50, 28672, 128, "f16"), (7, 33, 1280, 256, "f16"), (12, 40, 11008, 128, "f32"),
@@ -271,8 +273,8 @@ def test_w4a8_gemm(w4, m, n, k, g, sz, ykind):
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 8192), (8, 48, 1024), (16, 64, 1024), (64, 256, 8192),
-                                   (300, 130, 256)])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 8192), (3, 48, 4096), (8, 48, 1024), (16, 64, 1024),
+                                   (64, 256, 8192), (300, 130, 256)])
 def test_w4a8_exact_integers(w4, m, n, k):
     """x integers with |x| <= 127 and 127 present (scale 1, xq = x); W integer
     codes with scale 1, zp 0: y is an exact integer below 2^24 and the bf16
