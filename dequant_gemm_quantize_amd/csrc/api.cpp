@@ -219,9 +219,9 @@ int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
   if (x_scale == nullptr) return fail(W4_EINVAL, "%s: x_scale is NULL", fn);
   if ((reinterpret_cast<uintptr_t>(x_scale) & 3u) != 0)
     return fail(W4_EINVAL, "%s: x_scale is not 4-byte aligned", fn);
-  // Kernel choice: one token, group 128, K a multiple of 2048 up to 8192 ->
-  // the dot4 GEMV; up to 16 tokens, groups of a multiple of 128 -> the int8
-  // MFMA GEMV; more tokens -> the int8 MFMA GEMM; everything else -> the
+  // Kernel choice: one to four tokens, group 128, K a multiple of 2048 up to
+  // 8192 -> the dot4 GEMV; up to 16 tokens, groups of a multiple of 128 ->
+  // the int8 MFMA GEMV; more tokens -> the int8 MFMA GEMM; everything else -> the
   // general kernel.
   if (w4::w4a8_gemv_fits(m, k, group_size))
     return hip_status(w4::launch_w4a8_gemv(xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n,
