@@ -165,33 +165,24 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
   W4_TRY(check_ptr(fn, "scales", scales));
   W4_TRY(check_ptr(fn, "zeros", zeros));
   W4_TRY(check_ptr(fn, "y", y));
-  // Kernel choice (bf16 activations): one token -> the dot2 GEMV;
-  // up to four tokens with the activations fitting in LDS -> the LDS decode
-  // kernel; up to 128 tokens, groups of a multiple of 128 -> the MFMA GEMV
-  // (in launches of up to 64 tokens); other shapes up to 16 tokens -> the
-  // decode kernels; more tokens -> the MFMA GEMM; everything else (fp32
-  // activations, group sizes that are not a multiple of 128) -> the general
-  // kernel.
+  // Kernel choice (bf16 activations): one token, groups of at least 128, K up
+  // to 12288 -> the dot2 GEMV; up to four tokens with the activations fitting
+  // in LDS, groups of a multiple of 128 -> the LDS decode kernel; up to 128
+  // tokens, groups of a multiple of 128 -> the MFMA GEMV (in launches of up
+  // to 64 tokens); more tokens -> the MFMA GEMM; everything else (fp32
+  // activations, smaller group sizes at few tokens) -> the general kernel.
   if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size))
     return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
                                             group_size, y, y_dtype, stream),
                       fn);
-  const bool dec = x_dtype == W4_BF16 && m <= 16 && group_size % 128 == 0;
-  if (dec && m <= 4 && w4::decode_lds_fits(m, k))
+  const bool dec = x_dtype == W4_BF16 && m <= 4 && group_size % 128 == 0;
+  if (dec && w4::decode_lds_fits(m, k))
     return hip_status(w4::launch_w4a16_decode(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
                       fn);
   if (x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size))
     return hip_status(w4::launch_w4a16_gemv(x, m, k, packed, scales, zeros, sz_dtype, n,
                                             group_size, y, y_dtype, stream),
-                      fn);
-  if (dec && w4::decode_lds_fits(m, k))
-    return hip_status(w4::launch_w4a16_decode(x, m, k, packed, scales, zeros, sz_dtype, n,
-                                              group_size, y, y_dtype, stream),
-                      fn);
-  if (dec)
-    return hip_status(w4::launch_w4a16_skinny(x, m, k, packed, scales, zeros, sz_dtype, n,
-                                              group_size, y, y_dtype, stream),
                       fn);
   if (x_dtype == W4_BF16 && w4::gemm_fits(m, k, group_size))
     return hip_status(w4::launch_w4a16_gemm(x, m, k, packed, scales, zeros, sz_dtype, n,

@@ -1,6 +1,6 @@
-// Decode-time fused dequantize-matmul for 1 <= M <= 16 tokens (bf16 x),
-// groups that are multiples of 128 columns.  HBM-bound: the kernel exists to
-// stream the packed codes at full bandwidth.
+// Decode-time fused dequantize-matmul for 1 <= M <= 4 tokens (bf16 x) whose
+// activations fit in LDS, groups that are multiples of 128 columns.
+// HBM-bound: the kernels exist to stream the packed codes at full bandwidth.
 //
 // Math.  For a 128-column block b of weight row n (inside one group, scale s,
 // zero-point zp) and token m:
@@ -9,19 +9,19 @@
 // ("From Scratch: Building a GPTQ INT4 Quantizer in Pure Python", Step 4,
 // inside the product of "Building a From-Scratch Group-Wise INT4 Quantization
 // Layer for LLaMA Weights", Step 2).  128 + q is an exact bfloat16 whose low
-// mantissa bits are the code, so a nibble becomes an MFMA operand with one
-// byte permute and one and-or per pair of codes.  Both sums run on the bf16
-// MFMA unit (v_mfma_f32_16x16x32_bf16): the first against the codes, the
-// second against the constant -(128 + zp) of the row, into the same fp32
+// mantissa bits are the code, so a nibble becomes an MFMA operand with a
+// shift and one and-or per pair of codes.  Both sums run on the bf16 MFMA
+// unit (v_mfma_f32_16x16x32_bf16): the first against the codes, the second
+// against the constant -(128 + zp) of the row, into the same fp32
 // accumulator.  The block result is scaled by s with one FMA per output.
 //
 // Work layout.  A 256-lane workgroup owns 16 weight rows (one MFMA column
 // each) over all of K; its four waves split K into contiguous ranges and add
 // their 16x16 partial tiles through LDS at the end.  Lane l serves weight row
 // (l mod 16) and k-group (l div 16): per block it loads 16 bytes of packed
-// codes (32 consecutive columns), and, when token (l mod 16) < M, the 32
-// matching activations (64 bytes).  Packed loads for up to 8 blocks are in
-// flight per lane before the first MFMA.
+// codes (32 consecutive columns).  Each wave stages its activations, scales
+// and zero-points in its own LDS region (no workgroup barrier), and packed
+// loads for up to 8 blocks are in flight per lane before the first MFMA.
 #include "w4_common.h"
 #include "w4_internal.h"
 
@@ -29,39 +29,12 @@ namespace w4 {
 
 namespace {
 
-#ifndef W4_SKINNY_WAVES
-#define W4_SKINNY_WAVES 4
-#endif
-#ifndef W4_SKINNY_XDIST
-#define W4_SKINNY_XDIST 2
-#endif
-#ifndef W4_SKINNY_CHUNK
-#define W4_SKINNY_CHUNK 8
+#ifndef W4_DECODE_CHUNK
+#define W4_DECODE_CHUNK 8
 #endif
 constexpr int kRows = 16;                // weight rows per workgroup
-constexpr int kWaves = W4_SKINNY_WAVES;  // waves per workgroup (K split)
-constexpr int kChunk = W4_SKINNY_CHUNK;  // 128-column blocks whose codes are loaded ahead
-constexpr int kXDist = W4_SKINNY_XDIST;  // activation prefetch distance (blocks)
+constexpr int kChunk = W4_DECODE_CHUNK;  // 128-column blocks whose codes are loaded ahead
 
-
-// (q[2v], q[2v+1]) of a packed 8-code word as a bf16 pair (128 + q each).
-__device__ __forceinline__ uint32_t code_pair(uint32_t p, uint32_t p4, uint32_t v) {
-  // byte v of p holds codes 2v (low nibble) and 2v+1; byte v of p >> 4 holds
-  // code 2v+1 in its low nibble.  Bytes 1 and 3 of the result are zero.
-  const uint32_t sel = v | 0x0c00u | ((4u + v) << 16) | 0x0c000000u;
-  const uint32_t t = __builtin_amdgcn_perm(p4, p, sel);
-  return NibConst::make()(t);
-}
-
-__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t p) {
-  const uint32_t p4 = p >> 4;
-  u32x4 r;
-  r.x = code_pair(p, p4, 0);
-  r.y = code_pair(p, p4, 1);
-  r.z = code_pair(p, p4, 2);
-  r.w = code_pair(p, p4, 3);
-  return __builtin_bit_cast(bf16x8, r);
-}
 
 template <typename TY>
 __device__ __forceinline__ void store_out(void* y, int64_t i, float v) {
@@ -87,153 +60,10 @@ template <> struct RawSZ<float> {
   __device__ static uint32_t zero(T v) { return (uint32_t)__uint_as_float(v); }
 };
 
-// CH consecutive 128-column blocks starting at block c0, no branches: all
-// packed-code, scale and zero-point loads are issued first; activations are
-// prefetched two blocks ahead of the MFMAs that consume them.  Each block
-// accumulates into its own MFMA accumulator, so the block chains are
-// independent; the scales are applied after the last MFMA of the chunk.
-// gi(i) = group index of block c0 + i (precomputed by the caller).
-template <int CH, typename TS>
-__device__ __forceinline__ void skinny_chunk(const u32x4* __restrict__ wrow,
-                                             const u32x4* __restrict__ xrow,
-                                             const typename RawSZ<TS>::T* __restrict__ srow,
-                                             const typename RawSZ<TS>::T* __restrict__ zrow,
-                                             const int (&gi)[CH], int c0, f32x4& acc) {
-  typedef typename RawSZ<TS>::T R;
-  u32x4 wq[CH];
-  R sr[CH], zr[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) wq[i] = __builtin_nontemporal_load(wrow + 4 * (c0 + i));
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    sr[i] = srow[gi[i]];
-    zr[i] = zrow[gi[i]];
-  }
-  constexpr int D = CH < kXDist ? CH : kXDist;
-  u32x4 xa[D + 1][4];
-#pragma unroll
-  for (int i = 0; i < D; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) xa[i][t] = xrow[16 * (c0 + i) + t];
-  // keep every load above in flight before any arithmetic (the scheduler
-  // would otherwise sink them next to their uses and serialize the latency)
-  __builtin_amdgcn_sched_barrier(0);
-  f32x4 gacc[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    if (i + D < CH) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) xa[(i + D) % (D + 1)][t] = xrow[16 * (c0 + i + D) + t];
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const uint32_t zb = (0xc300u | RawSZ<TS>::zero(zr[i])) * 0x00010001u;  // bf16 pair -(128+zp)
-    const bf16x8 bz = __builtin_bit_cast(bf16x8, u32x4{zb, zb, zb, zb});
-    const uint32_t w4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
-    gacc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, xa[i % (D + 1)][t]);
-      gacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, codes_to_bf16(w4[t]), gacc[i], 0, 0, 0);
-      gacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bz, gacc[i], 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const float sc = RawSZ<TS>::scale(sr[i]);
-    acc.x = fmaf(sc, gacc[i].x, acc.x);
-    acc.y = fmaf(sc, gacc[i].y, acc.y);
-    acc.z = fmaf(sc, gacc[i].z, acc.z);
-    acc.w = fmaf(sc, gacc[i].w, acc.w);
-  }
-}
-
-// Group index of each block of a chunk: blocks per group is 1 for g = 128
-// (the common case, no arithmetic) and bpg otherwise.
-template <int CH, bool BPG1>
-__device__ __forceinline__ void chunk_groups(int c0, int bpg, int (&gi)[CH]) {
-  if (BPG1) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) gi[i] = c0 + i;
-  } else {
-    int q = c0 / bpg, r = c0 - q * bpg;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      gi[i] = q;
-      if (++r == bpg) { r = 0; ++q; }
-    }
-  }
-}
-
-template <int CH, typename TS, bool BPG1>
-__device__ __forceinline__ void run_chunk(const u32x4* wrow, const u32x4* xrow,
-                                          const typename RawSZ<TS>::T* srow,
-                                          const typename RawSZ<TS>::T* zrow, int bpg, int c0,
-                                          f32x4& acc) {
-  int gi[CH];
-  chunk_groups<CH, BPG1>(c0, bpg, gi);
-  skinny_chunk<CH, TS>(wrow, xrow, srow, zrow, gi, c0, acc);
-}
-
-template <typename TS, typename TY, bool BPG1>
-__global__ __launch_bounds__(64 * kWaves) void k_w4a16_skinny(
-    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
-    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
-    void* __restrict__ y) {
-  typedef typename RawSZ<TS>::T R;
-  __shared__ f32x4 part[kWaves][64];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int j = lane & 15;     // weight row in the tile; token row of the x operand
-  const int kg = lane >> 4;    // 32-column group inside a 128-column block
-  const int64_t n0 = (int64_t)blockIdx.x * kRows;
-  const int64_t n = (n0 + j < N) ? (n0 + j) : (N - 1);  // ragged tail: read a valid row
-
-  const int nblk = (int)(K / 128);
-  const int b0 = (wave * nblk) / kWaves;
-  const int b1 = ((wave + 1) * nblk) / kWaves;
-  const int64_t ng = K / g;
-  const int bpg = g / 128;  // 128-column blocks per group
-
-  const u32x4* wrow = (const u32x4*)(packed + n * (K / 2)) + kg;  // block b at + 4*b
-  // Operand rows m >= M read token 0 again: their results are never stored.
-  const int jx = j < M ? j : 0;
-  const u32x4* xrow = (const u32x4*)(x + (int64_t)jx * K) + kg * 4;  // block b at + 16*b
-  const R* srow = (const R*)scales + n * ng;
-  const R* zrow = (const R*)zeros + n * ng;
-
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int c0 = b0;
-  for (; c0 + kChunk <= b1; c0 += kChunk) run_chunk<kChunk, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc);
-  if (kChunk > 4 && c0 + 4 <= b1) { run_chunk<4, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc); c0 += 4; }
-  if (kChunk > 2 && c0 + 2 <= b1) { run_chunk<2, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc); c0 += 2; }
-  if (c0 < b1) run_chunk<1, TS, BPG1>(wrow, xrow, srow, zrow, bpg, c0, acc);
-
-  // lane holds D[i][j] for token i = 4*kg + r, weight row j = lane mod 16
-  part[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    f32x4 s = part[0][lane];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      const f32x4 o = part[w][lane];
-      s.x += o.x; s.y += o.y; s.z += o.z; s.w += o.w;
-    }
-    if (n0 + j < N) {
-      const float v[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (m < M) store_out<TY>(y, (int64_t)m * N + n0 + j, v[r]);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Decode kernel with the activations staged in LDS (used when M * K * 2 bytes
-// fits the LDS budget of 64 KB: M <= 4 at K = 4096, M = 1 at K = 8192).  Same math and work layout as
-// above, with two differences that cut registers and VALU work:
+// The decode kernels (used when the activations fit the LDS budget of
+// 64 KB: M <= 4 at K = 4096, M = 1 at K = 8192).  Two details cut registers
+// and VALU work:
 //  * the block's codes are expanded in the order (0,4), (1,5), (2,6), (3,7)
 //    of each 8-code word -- seven instructions per word (shift + and-or) --
 //    and the activations are stored in LDS in that same order, so the MFMA
@@ -267,9 +97,6 @@ __device__ __forceinline__ u32x4 interleave8(u32x4 v) {
   return r;
 }
 
-// One chunk of CH blocks.  Loads are issued in the order scale/zero-point,
-// then codes, so that (vmcnt retires in order) block i waits only for its own
-// codes: the MFMAs of block i overlap the arrival of blocks i+1 .. CH-1.
 // MFMAs of CH consecutive blocks whose codes are already loaded (wq); block
 // i waits only for its own codes (vmcnt retires in order).  Scale and
 // zero-point of every block come from the LDS tile.
@@ -628,32 +455,6 @@ hipError_t launch_w4a16_decode(const void* x, int64_t m, int64_t k, const uint8_
   } else {
     if (y_dtype == W4_F32) decode_go<float, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
     else decode_go<float, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
-  }
-  return hipGetLastError();
-}
-
-template <typename TS, typename TY>
-static void skinny_go(dim3 grid, hipStream_t st, const uint16_t* x, int M, int64_t k,
-                      const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
-                      int g, void* y) {
-  if (g == 128)
-    k_w4a16_skinny<TS, TY, true><<<grid, 64 * kWaves, 0, st>>>(x, M, k, packed, scales, zeros, n, g, y);
-  else
-    k_w4a16_skinny<TS, TY, false><<<grid, 64 * kWaves, 0, st>>>(x, M, k, packed, scales, zeros, n, g, y);
-}
-
-hipError_t launch_w4a16_skinny(const void* x, int64_t m, int64_t k, const uint8_t* packed,
-                               const void* scales, const void* zeros, int sz_dtype, int64_t n,
-                               int g, void* y, int y_dtype, hipStream_t st) {
-  const dim3 grid((unsigned)((n + kRows - 1) / kRows));
-  const uint16_t* xb = (const uint16_t*)x;
-  const int M = (int)m;
-  if (sz_dtype == W4_F16) {
-    if (y_dtype == W4_F32) skinny_go<_Float16, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
-    else skinny_go<_Float16, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
-  } else {
-    if (y_dtype == W4_F32) skinny_go<float, float>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
-    else skinny_go<float, __bf16>(grid, st, xb, M, k, packed, scales, zeros, n, g, y);
   }
   return hipGetLastError();
 }

@@ -39,9 +39,6 @@ hipError_t launch_w4a16_generic(const void* x, int x_dtype, int64_t m, int64_t k
                                 const uint8_t* packed, const void* scales, const void* zeros,
                                 int sz_dtype, int64_t n, int g, void* y, int y_dtype,
                                 hipStream_t st);
-hipError_t launch_w4a16_skinny(const void* x, int64_t m, int64_t k, const uint8_t* packed,
-                               const void* scales, const void* zeros, int sz_dtype, int64_t n,
-                               int g, void* y, int y_dtype, hipStream_t st);
 hipError_t launch_w4a16_decode(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                                const void* scales, const void* zeros, int sz_dtype, int64_t n,
                                int g, void* y, int y_dtype, hipStream_t st);
