@@ -432,12 +432,10 @@ static void decode_go(dim3 grid, hipStream_t st, const uint16_t* x, int M, int64
 #define W4_DEC_FAST(XP, SP, NWB) \
   k_w4a16_decode_fast<TS, TY, W, XP, SP, NWB><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, y)
   const int64_t nwb = nblk / W;
-  if (xper == 2 && sper == 1 && nwb == 8) W4_DEC_FAST(2, 1, 8);        // M = 1, K = 4096, fp16 s/z
-  else if (xper == 4 && sper == 2 && nwb == 16) W4_DEC_FAST(4, 2, 16); // M = 1, K = 8192, fp16 s/z
-  else if (xper == 4 && sper == 1 && nwb == 8) W4_DEC_FAST(4, 1, 8);   // M = 2, K = 4096
-  else if (xper == 6 && sper == 1 && nwb == 8) W4_DEC_FAST(6, 1, 8);   // M = 3, K = 4096
-  else if (xper == 8 && sper == 1 && nwb == 8) W4_DEC_FAST(8, 1, 8);   // M = 4, K = 4096
-  else if (xper == 2 && sper == 2 && nwb == 8) W4_DEC_FAST(2, 2, 8);   // M = 1, K = 4096, fp32 s/z
+  // (one token never gets here: it goes to the dot2 GEMV)
+  if (xper == 4 && sper == 1 && nwb == 8) W4_DEC_FAST(4, 1, 8);        // M = 2, K = 4096, fp16 s/z
+  else if (xper == 6 && sper == 1 && nwb == 8) W4_DEC_FAST(6, 1, 8);   // M = 3, K = 4096, fp16 s/z
+  else if (xper == 8 && sper == 1 && nwb == 8) W4_DEC_FAST(8, 1, 8);   // M = 4, K = 4096, fp16 s/z
   else W4_DEC(0, 0);
 #undef W4_DEC_FAST
 #undef W4_DEC
