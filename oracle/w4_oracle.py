@@ -31,6 +31,9 @@ test in tests/test_oracle_pins.py):
     even; dequantized weight (q - zp) * scale ([P5] Step 4);
   * two codes per byte, the even column in the low nibble ([P4] Step 4;
     [P3] Step 1);
+  * symmetric variant: scale = absmax/7 and code clamp(round(w/scale), -8, 7)
+    ([P4] Step 2), stored with the +8 offset of [P4] Step 4, i.e. a fixed
+    zero-point of 8; same stored-scale and zero-guard readings as above;
   * per-token activation scale max(max|x|, 1e-8)/127 and
     clamp(round(x/s), -128, 127) ([P1] Step 3);
   * matmul y = x . dequant(W)^T ([P3] Step 2; [P4] Step 5), and for the
@@ -153,6 +156,52 @@ def quantize_pack_int4(w: np.ndarray, kind: str, g: int, sz: str):
     s_st, zp = scale_zero(mn, mx, sz)
     q = quantize_codes(w32, s_st, zp, g)
     return pack_nibbles(q), s_st, zp.astype(SZ_DTYPES[sz])
+
+
+# --------------------------------------------------------------------------
+# Symmetric variant ([P4] Step 2 for scale and codes, Step 4 for the +8
+# offset).  The codes and scales it stores feed the same dequantization and
+# matmuls as the asymmetric ones, with every zero-point equal to 8.
+# --------------------------------------------------------------------------
+SYM_OFFSET = 8
+
+
+def group_absmax(w32: np.ndarray, g: int) -> np.ndarray:
+    """Per-group maximum of |w| ([P4] Step 2)."""
+    return np.abs(split_groups(w32, g)).max(axis=2)
+
+
+def scale_sym(amax: np.ndarray, sz: str) -> np.ndarray:
+    """scale = fl32(absmax / 7), rounded to the storage dtype; a stored scale
+    of zero becomes 1 ([P4] Step 2).  Like the asymmetric scale, the guard is
+    applied to the stored value."""
+    sd = SZ_DTYPES[sz]
+    s_st = (amax.astype(F32) / F32(7.0)).astype(sd)
+    return np.where(s_st == 0, sd(1.0), s_st).astype(sd)
+
+
+def quantize_codes_sym(w32: np.ndarray, s_st: np.ndarray, g: int) -> np.ndarray:
+    """Signed code clamp(rint(fl32(w / scale)), -8, 7) ([P4] Step 2), stored
+    unsigned as code + 8 ([P4] Step 4).  The offset is added to the rounded
+    integer, not before rounding."""
+    wg = split_groups(w32, g)
+    s = s_st.astype(F32)[..., None]
+    q = np.clip(np.rint(wg / s), -8, 7).astype(np.int32)
+    return (q + SYM_OFFSET).astype(np.uint8).reshape(w32.shape)
+
+
+def quantize_pack_int4_sym(w: np.ndarray, kind: str, g: int, sz: str):
+    """Symmetric quantize + pack of W [N, K].
+
+    Returns (packed uint8 [N, K/2], scales [N, K/g] in sz dtype, zeros
+    [N, K/g] in sz dtype, all equal to 8), so that (q - zp) * scale is the
+    symmetric dequantization.
+    """
+    w32 = as_f32(w, kind)
+    s_st = scale_sym(group_absmax(w32, g), sz)
+    q = quantize_codes_sym(w32, s_st, g)
+    zeros = np.full(s_st.shape, SYM_OFFSET, SZ_DTYPES[sz])
+    return pack_nibbles(q), s_st, zeros
 
 
 # --------------------------------------------------------------------------

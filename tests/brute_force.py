@@ -67,6 +67,42 @@ def quantize_pack(w32: np.ndarray, g: int, sz: str):
     return packed, scales, zeros
 
 
+def quantize_group_sym(vals, sz: str):
+    """One group, symmetric: list of float32 values -> (stored scale, codes
+    0..15 holding the signed code + 8)."""
+    amax = f32(0.0)
+    for v in vals:
+        a = f32(abs(v))
+        if a > amax:
+            amax = a
+    s32 = f32(amax / f32(7.0))
+    stored = np.float16(s32) if sz == "f16" else f32(s32)
+    if float(stored) == 0.0:
+        stored = np.float16(1.0) if sz == "f16" else f32(1.0)
+    s = f32(stored)
+    return stored, [_clamp(_rint(f32(v / s)), -8, 7) + 8 for v in vals]
+
+
+def quantize_pack_sym(w32: np.ndarray, g: int, sz: str):
+    """Symmetric W [N,K] float32 -> (packed bytes, scales, zeros = 8)."""
+    n, k = w32.shape
+    ng = k // g
+    sdt = np.float16 if sz == "f16" else np.float32
+    packed = np.zeros((n, k // 2), np.uint8)
+    scales = np.zeros((n, ng), sdt)
+    zeros = np.zeros((n, ng), sdt)
+    for r in range(n):
+        codes_row = []
+        for gi in range(ng):
+            st, codes = quantize_group_sym([f32(w32[r, gi * g + t]) for t in range(g)], sz)
+            scales[r, gi] = st
+            zeros[r, gi] = 8
+            codes_row.extend(codes)
+        for j in range(k // 2):
+            packed[r, j] = codes_row[2 * j] + 16 * codes_row[2 * j + 1]
+    return packed, scales, zeros
+
+
 def dequant(packed, scales, zeros, g: int) -> np.ndarray:
     """w_hat[r, c] = fl32((code - zp) * scale), element by element."""
     n, half = packed.shape

@@ -393,6 +393,166 @@ def check_invariants_small_config():
 
 
 # ---------------------------------------------------------------------------
+# Symmetric variant ("Build a GPTQ INT4 Quantization Engine in Python/NumPy",
+# Step 2: scale = absmax/7, code clamp(round(w/scale), -8, 7); Step 4: +8)
+# ---------------------------------------------------------------------------
+def worked_example_sym_group(kind: str):
+    """The 32 values of the symmetric worked example and their stored codes
+    (tests/golden/worked_example_sym_g32.json).  The near-tie value is exact
+    in fp32 only; the bf16 case has 0 (code 8) in its place."""
+    gv = _golden("worked_example_sym_g32.json")
+    u = 2.0 ** -6
+    vals = [j * u for j in gv["levels_j"]]
+    codes = [j + 8 for j in gv["levels_j"]]
+    vals += [(j + 0.5) * u for j in gv["midpoints_j"]]
+    codes += gv["expected"]["midpoint_codes"]
+    vals += [j * u for j in gv["repeated_levels_j"]]
+    codes += [j + 8 for j in gv["repeated_levels_j"]]
+    if kind == "f32":
+        vals.append(float(np.frombuffer(bytes.fromhex(gv["near_tie_value_f32_hex"])[::-1], f32)[0]))
+        codes.append(gv["expected"]["near_tie_code"])
+    else:
+        vals.append(0.0)
+        codes.append(8)
+    assert len(vals) == 32
+    return np.array(vals, f32), np.array(codes, np.uint8)
+
+
+def check_sym_worked_example():
+    gv = _golden("worked_example_sym_g32.json")
+    u = 2.0 ** -6
+    for sz in ("f32", "f16"):
+        for kind in ("f32", "bf16"):
+            vals, codes = worked_example_sym_group(kind)
+            w = vals.reshape(1, 32) if kind == "f32" else O.to_bf16(vals).reshape(1, 32)
+            assert np.array_equal(O.as_f32(w, kind)[0], vals)  # every value exact in the input type
+            p, s, z = O.quantize_pack_int4_sym(w, kind, 32, sz)
+            assert float(s[0, 0]) == u, (sz, kind, float(s[0, 0]))
+            assert float(z[0, 0]) == gv["expected"]["zero_point"]
+            assert np.array_equal(O.unpack_nibbles(p)[0], codes), (O.unpack_nibbles(p)[0], codes)
+            wh = O.dequant_f32(p, s, z, 32)[0]
+            assert np.array_equal(wh, ((codes.astype(np.float64) - 8) * u).astype(np.float32))
+            lv = np.r_[0:15, 29:31]  # the levels reproduce exactly
+            assert np.array_equal(wh[lv], vals[lv])
+
+
+def check_sym_special_groups():
+    """Zero and signed-zero groups, a scale that underflows fp16, and an
+    fp16-subnormal scale coarse enough that the -8 code is reached."""
+    g = 32
+    t = np.float32(2.0 ** -24)
+    w = np.zeros((4, 2 * g), np.float32)
+    w[0, g:] = -3.0                                   # constant negative group
+    w[1, :5] = np.array([-10, 10, 7.5, -8.5, -7.5], np.float32) * t
+    w[1, g:g + 15] = np.arange(-7, 8) * np.float32(2.0 ** -27)
+    w[2, ::2] = -0.0
+    w[3, :g] = np.arange(-16, 16) * np.float32(1e-30)  # tiny fp32 range
+    p16, s16, z16 = O.quantize_pack_int4_sym(w, "f32", g, "f16")
+    q16 = O.unpack_nibbles(p16).astype(int)
+    assert (np.asarray(z16, np.float32) == 8).all()
+    # all-zero and signed-zero groups: scale 1, code 8 (signed 0)
+    assert float(s16[0, 0]) == 1.0 and (q16[0, :g] == 8).all()
+    assert float(s16[2, 0]) == 1.0 and (q16[2] == 8).all()
+    # constant -3: scale fp16(3/7), code -7
+    assert float(s16[0, 1]) == float(np.float16(np.float32(3.0) / np.float32(7.0)))
+    assert (q16[0, g:] == 1).all()
+    # absmax 10 * 2^-24: fp32 scale 10/7 * 2^-24 rounds to the fp16 subnormal
+    # 2^-24, so w/s = -10, 10, 7.5, -8.5, -7.5 -> -8, 7, 7, -8, -8 (stored +8)
+    assert float(s16[1, 0]) == 2.0 ** -24
+    assert q16[1, :5].tolist() == [0, 15, 15, 0, 0]
+    # absmax 7 * 2^-27: the scale 2^-27 underflows fp16 -> 1, every code 8
+    assert float(s16[1, 1]) == 1.0 and (q16[1, g:] == 8).all()
+    assert float(s16[3, 0]) == 1.0 and (q16[3, :g] == 8).all()
+    # fp32 scales keep all of these
+    p32, s32, z32 = O.quantize_pack_int4_sym(w, "f32", g, "f32")
+    q32 = O.unpack_nibbles(p32).astype(int)
+    assert float(s32[1, 1]) == 2.0 ** -27
+    assert q32[1, g:g + 15].tolist() == list(range(1, 16))
+    assert q32[1, :5].tolist() == [1, 15, 13, 2, 3]  # w/s = -7, 7, 5.25, -5.95, -5.25
+    assert float(s32[3, 0]) == float(np.float32(np.float32(16e-30) / np.float32(7.0)))
+
+
+def check_sym_brute_force():
+    rng = np.random.default_rng(15)
+    for (n, k, g) in ((4, 64, 32), (3, 128, 64), (2, 256, 128)):
+        w = rng.normal(0, 0.05, (n, k)).astype(np.float32)
+        w[0, 5] = -0.6
+        w[-1, :g] = np.abs(w[-1, :g])
+        for sz in ("f32", "f16"):
+            for kind in ("f32", "bf16"):
+                src = w if kind == "f32" else O.to_bf16(w)
+                w32 = w if kind == "f32" else O.widen_bf16(src)
+                p, s, z = O.quantize_pack_int4_sym(src, kind, g, sz)
+                bp, bs, bz = BF.quantize_pack_sym(w32, g, sz)
+                assert np.array_equal(p, bp), (n, k, g, sz, kind)
+                assert np.array_equal(s.view(np.uint8), bs.view(np.uint8))
+                assert np.array_equal(z.view(np.uint8), bz.view(np.uint8))
+                d = O.dequant_f32(p, s, z, g)
+                assert np.array_equal(d.view(np.uint32), BF.dequant(p, s, z, g).view(np.uint32))
+
+
+def check_sym_exact_scaled_matmul():
+    """W[r, group] = 2^e * Q with Q in -7..7 and |Q| = 7 in every group:
+    quantization returns (2^e, Q + 8) exactly, and the matmuls equal the
+    exact rational results."""
+    rng = np.random.default_rng(16)
+    n, k, g, m = 5, 128, 32, 3
+    ng = k // g
+    Q = rng.integers(-7, 8, (n, k))
+    for r in range(n):
+        for gi in range(ng):
+            Q[r, gi * g + rng.integers(0, g)] = 7 * (1 if rng.integers(0, 2) else -1)
+    E = rng.integers(-9, -3, (n, ng))
+    w = np.repeat(2.0 ** E, g, axis=1) * Q
+    w32 = w.astype(np.float32)
+    xi = rng.integers(-127, 128, (m, k))
+    for sz in ("f32", "f16"):
+        p, s, z = O.quantize_pack_int4_sym(w32, "f32", g, sz)
+        assert np.array_equal(np.asarray(s, np.float64), 2.0 ** E)
+        assert np.array_equal(O.unpack_nibbles(p).astype(np.int64), Q + 8)
+        assert np.array_equal(O.dequant_f32(p, s, z, g), w32)
+        y = O.matmul_w4a16_f64(xi.astype(np.float32), p, s, z, g)
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(int(xi[i, c])) * Fraction(float(w[j, c])) for c in range(k))
+                assert y[i, j] == float(exact)
+        xq, sa = O.act_quant_int8(xi.astype(np.float32))
+        y8 = O.matmul_w4a8_f64(xq, sa, p, s, z, g)
+        assert np.allclose(y8, (xq.astype(np.float64) * sa[:, None].astype(np.float64)) @ w.T,
+                           rtol=1e-15, atol=0)
+
+
+def check_sym_invariants():
+    """Codes 1..15 (the -8 code needs a subnormal scale); the element of
+    largest magnitude of each group takes code 1 or 15; every error within
+    half a step; each code a nearest level of the stored grid; MSE near
+    s^2/12 (one exact element per group lowers it by about 1/g)."""
+    from workloads import weight
+    rng = np.random.default_rng(17)
+    cases = [(weight("W1").as_f32(), 32, "f32"), (weight("W1").as_f32(), 32, "f16"),
+             (O.widen_bf16(O.to_bf16(rng.normal(0, 0.02, (64, 1024)).astype(np.float32))), 128, "f16")]
+    for w, g, sz in cases:
+        n, k = w.shape
+        p, s, z = O.quantize_pack_int4_sym(w, "f32", g, sz)
+        q = O.unpack_nibbles(p).astype(np.int64).reshape(n, k // g, g)
+        assert q.min() >= 1 and q.max() <= 15
+        wg = w.astype(np.float64).reshape(n, k // g, g)
+        top = np.take_along_axis(q, np.abs(wg).argmax(axis=2)[..., None], 2)[..., 0]
+        assert np.isin(top, (1, 15)).all()
+        sv = np.asarray(s, np.float64)[..., None]
+        err = np.abs(wg - (q - 8) * sv)
+        slack = 2.0 ** -6 if sz == "f16" else 2.0 ** -16
+        assert (err <= sv / 2 * (1 + slack)).all()
+        for d in (-1, 1):
+            qn = q + d
+            ok = (qn >= 0) & (qn <= 15)
+            errn = np.abs(wg - (qn - 8) * sv)
+            assert (err[ok] <= errn[ok] + np.broadcast_to(sv, err.shape)[ok] * 2.0 ** -20).all()
+        mse_ratio = float((err ** 2).mean() / (sv ** 2 / 12).mean())
+        assert (1 - 2.0 / g) < mse_ratio < 1.05, (g, sz, mse_ratio)
+
+
+# ---------------------------------------------------------------------------
 # bf16 rounding of the oracle against the library routine (torch)
 # ---------------------------------------------------------------------------
 def check_bf16_rounding_vs_torch():
@@ -422,4 +582,6 @@ ALL_CHECKS = [
     check_exact_scaled_matmul,
     check_act_quant_closed_forms, check_act_quant_invariants, check_invariants_small_config,
     check_bf16_rounding_vs_torch, check_max_rel_err,
+    check_sym_worked_example, check_sym_special_groups, check_sym_brute_force,
+    check_sym_exact_scaled_matmul, check_sym_invariants,
 ]

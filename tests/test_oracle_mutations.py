@@ -148,6 +148,58 @@ def _dequant64_wrong_group(packed, scales, zeros, g, rows=None):
     return _orig["dequant_f64"](packed, s, z, g, rows)
 
 
+def _sym_scale_over_8(amax, sz):
+    sd = O.SZ_DTYPES[sz]
+    s_st = (amax.astype(F32) / F32(8.0)).astype(sd)
+    return np.where(s_st == 0, sd(1.0), s_st).astype(sd)
+
+
+def _sym_scale_guard_first(amax, sz):
+    sd = O.SZ_DTYPES[sz]
+    s32 = amax.astype(F32) / F32(7.0)
+    with np.errstate(all="ignore"):
+        return np.where(s32 == 0, F32(1.0), s32).astype(sd)
+
+
+def _sym_offset_before_rounding(w32, s_st, g):
+    wg = O.split_groups(w32, g)
+    t = np.rint(wg / s_st.astype(F32)[..., None] + F32(8.0))
+    return np.clip(t, 0, 15).astype(np.uint8).reshape(w32.shape)
+
+
+def _sym_codes_of_magnitude(w32, s_st, g):
+    # quantizes |w| instead of w
+    return _orig["quantize_codes_sym"](np.abs(w32), s_st, g)
+
+
+def _sym_clamp_7(w32, s_st, g):
+    wg = O.split_groups(w32, g)
+    q = np.clip(np.rint(wg / s_st.astype(F32)[..., None]), -7, 7).astype(np.int32)
+    return (q + 8).astype(np.uint8).reshape(w32.shape)
+
+
+def _sym_round_half_away(w32, s_st, g):
+    wg = O.split_groups(w32, g)
+    v = wg / s_st.astype(F32)[..., None]
+    q = np.clip(np.sign(v) * np.floor(np.abs(v) + F32(0.5)), -8, 7).astype(np.int32)
+    return (q + 8).astype(np.uint8).reshape(w32.shape)
+
+
+def _sym_quantize_with_unrounded_scale(w, kind, g, sz):
+    w32 = O.as_f32(w, kind)
+    s32 = O.group_absmax(w32, g).astype(F32) / F32(7.0)
+    s32 = np.where(s32 == 0, F32(1.0), s32).astype(F32)
+    s_st = s32.astype(O.SZ_DTYPES[sz])
+    s_st = np.where(s_st == 0, O.SZ_DTYPES[sz](1.0), s_st)
+    q = O.quantize_codes_sym(w32, s32, g)
+    return O.pack_nibbles(q), s_st, np.full(s_st.shape, 8, O.SZ_DTYPES[sz])
+
+
+def _sym_zero_point_7(w, kind, g, sz):
+    p, s, z = _orig["quantize_pack_int4_sym"](w, kind, g, sz)
+    return p, s, np.full(z.shape, 7, z.dtype)
+
+
 _uq_sz, _uq_codes = _codes_with_unrounded_scale_factory()
 
 MUTATIONS = {
@@ -168,6 +220,14 @@ MUTATIONS = {
     "w4a8_drops_act_scale": {"matmul_w4a8_f64": _w4a8_no_act_scale},
     "bf16_truncates": {"to_bf16": _to_bf16_truncate},
     "dequant_shifted_group_index": {"dequant_f64": _dequant64_wrong_group},
+    "sym_scale_over_8": {"scale_sym": _sym_scale_over_8},
+    "sym_guard_before_fp16_rounding": {"scale_sym": _sym_scale_guard_first},
+    "sym_offset_before_rounding": {"quantize_codes_sym": _sym_offset_before_rounding},
+    "sym_quantizes_magnitude": {"quantize_codes_sym": _sym_codes_of_magnitude},
+    "sym_clamp_to_plus_minus_7": {"quantize_codes_sym": _sym_clamp_7},
+    "sym_round_half_away": {"quantize_codes_sym": _sym_round_half_away},
+    "sym_quantize_with_unrounded_scale": {"quantize_pack_int4_sym": _sym_quantize_with_unrounded_scale},
+    "sym_zero_point_7": {"quantize_pack_int4_sym": _sym_zero_point_7},
 }
 
 
