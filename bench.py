@@ -265,6 +265,11 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
         qsec = time_region(lambda i: w4.quantize_pack_int4(wt, g, torch.float16, out=qo), reps)
         out.setdefault("quantize_pack", {})[name] = {
             "us": round(qsec * 1e6, 2), "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}
+        # the symmetric variant moves the same bytes
+        qsec = time_region(lambda i: w4.quantize_pack_int4_sym(wt, g, torch.float16, out=qo), reps)
+        out.setdefault("quantize_pack_sym", {})[name] = {
+            "us": round(qsec * 1e6, 2), "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}
+        del qo
         if name == "Wb":
             dq = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
             dsec = time_region(lambda i: w4.dequant_int4(p, s, z, g, out=dq), reps)

@@ -25,6 +25,7 @@ _DT = {torch.float32: W4_F32, torch.float16: W4_F16, torch.bfloat16: W4_BF16}
 _VP, _I, _I64, _I32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32
 SIGNATURES = [
     ("quantize_pack_int4", _I, [_VP, _I, _I64, _I64, _I32, _VP, _VP, _VP, _I, _VP]),
+    ("quantize_pack_int4_sym", _I, [_VP, _I, _I64, _I64, _I32, _VP, _VP, _VP, _I, _VP]),
     ("dequant_int4", _I, [_VP, _VP, _VP, _I, _I64, _I64, _I32, _VP, _I, _VP]),
     ("quantize_act_int8", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP]),
     ("w4a16_matmul", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
@@ -104,7 +105,16 @@ def _dtype_code(dt: torch.dtype) -> int:
 def quantize_pack_int4(w: torch.Tensor, group_size: int, sz_dtype: torch.dtype = torch.float16,
                        out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """W [N, K] (fp32 or bf16) -> (packed uint8 [N, K/2], scales [N, K/g], zeros [N, K/g])."""
-    lib = load()
+    return _quantize_pack(load().quantize_pack_int4, w, group_size, sz_dtype, out)
+
+
+def quantize_pack_int4_sym(w: torch.Tensor, group_size: int, sz_dtype: torch.dtype = torch.float16,
+                           out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Symmetric variant: same arguments and outputs; every zero-point is 8."""
+    return _quantize_pack(load().quantize_pack_int4_sym, w, group_size, sz_dtype, out)
+
+
+def _quantize_pack(fn, w, group_size, sz_dtype, out):
     n, k = w.shape
     dev = _gpu(w)
     if out is None:
@@ -114,8 +124,8 @@ def quantize_pack_int4(w: torch.Tensor, group_size: int, sz_dtype: torch.dtype =
     else:
         packed, scales, zeros = out
         _gpu(packed, scales, zeros)
-    _check(lib.quantize_pack_int4(_ptr(w), _dtype_code(w.dtype), n, k, group_size, _ptr(packed),
-                                  _ptr(scales), _ptr(zeros), _dtype_code(scales.dtype), _stream(dev)))
+    _check(fn(_ptr(w), _dtype_code(w.dtype), n, k, group_size, _ptr(packed), _ptr(scales),
+              _ptr(zeros), _dtype_code(scales.dtype), _stream(dev)))
     return packed, scales, zeros
 
 

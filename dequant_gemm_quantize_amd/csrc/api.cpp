@@ -95,10 +95,9 @@ const char* w4_last_error(void) { return g_last_error; }
 
 const char* w4_version(void) { return "w4 0.1.0 gfx950"; }
 
-int quantize_pack_int4(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
-                       uint8_t* packed, void* scales, void* zeros, int sz_dtype,
-                       hipStream_t stream) {
-  static const char* fn = "quantize_pack_int4";
+static int quantize_pack_common(const char* fn, bool symmetric, const void* w, int w_dtype,
+                                int64_t n, int64_t k, int32_t group_size, uint8_t* packed,
+                                void* scales, void* zeros, int sz_dtype, hipStream_t stream) {
   W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
   if (w_dtype != W4_F32 && w_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: w dtype %d must be W4_F32 or W4_BF16", fn, w_dtype);
@@ -108,8 +107,22 @@ int quantize_pack_int4(const void* w, int w_dtype, int64_t n, int64_t k, int32_t
   W4_TRY(check_ptr(fn, "scales", scales));
   W4_TRY(check_ptr(fn, "zeros", zeros));
   return hip_status(w4::launch_quantize_pack(w, w_dtype, n, k, group_size, packed, scales, zeros,
-                                             sz_dtype, stream),
+                                             sz_dtype, symmetric, stream),
                     fn);
+}
+
+int quantize_pack_int4(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                       uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                       hipStream_t stream) {
+  return quantize_pack_common("quantize_pack_int4", false, w, w_dtype, n, k, group_size, packed,
+                              scales, zeros, sz_dtype, stream);
+}
+
+int quantize_pack_int4_sym(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                           uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                           hipStream_t stream) {
+  return quantize_pack_common("quantize_pack_int4_sym", true, w, w_dtype, n, k, group_size, packed,
+                              scales, zeros, sz_dtype, stream);
 }
 
 int dequant_int4(const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,

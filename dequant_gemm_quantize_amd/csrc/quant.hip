@@ -96,6 +96,78 @@ __device__ __forceinline__ uint32_t pack8(const float* v, float s, float r, floa
   return lo | (hi << 4);
 }
 
+// Symmetric variant ("Build a GPTQ INT4 Quantization Engine in
+// Python/NumPy", Step 2): scale = absmax / 7 rounded to the storage type,
+// 0 -> 1; signed code clamp(rint(w/scale), -8, 7), stored as code + 8
+// (Step 4), i.e. a fixed zero-point of 8.  The offset goes onto the rounded
+// integer.
+template <typename TS>
+__device__ __forceinline__ void scale_sym(float amax, TS& s_store, float& s) {
+  float s32 = amax / 7.0f;
+  TS st = (TS)s32;
+  if (st == (TS)0.0f) st = (TS)1.0f;
+  s_store = st;
+  s = (float)st;
+}
+
+__device__ __forceinline__ uint32_t code_sym(float w, float s) {
+  float t = rintf(w / s);
+  t = fminf(fmaxf(t, -8.0f), 7.0f);
+  return (uint32_t)(t + 8.0f);
+}
+
+// As pack8, for the symmetric codes.  t = w * (1/s) differs from fl32(w/s)
+// by less than 2^-19 wherever |t| <= 8 (1.5 ulp of the product plus the
+// division's half ulp), and only the half-integers -7.5 .. 6.5 decide a code
+// once t is clamped to [-8, 7] (every t that clamps gives -8 or 7 either
+// way).  Words with a clamped t within 2^-12 of a half-integer, or with an
+// infinite 1/s, take the correctly rounded division.
+__device__ __forceinline__ uint32_t pack8_sym(const float* v, float s, float r) {
+  float c[8];
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = fminf(fmaxf(v[i] * r, -8.0f), 7.0f);
+    c[i] = rintf(t);
+    dmax = fmaxf(dmax, fabsf(t - c[i]));
+  }
+  if (!(dmax < 0.5f - 0x1p-12f) || !(r < 3.0e38f)) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= code_sym(v[i], s) << (4 * i);
+    return word;
+  }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * j] + 8.0f, j, lo);
+    hi = __builtin_amdgcn_cvt_pk_u8_f32(c[2 * j + 1] + 8.0f, j, hi);
+  }
+  return lo | (hi << 4);
+}
+
+// Scale, zero-point and reciprocal of a group from its min and max, for
+// either variant.
+template <typename TS, bool SYM>
+__device__ __forceinline__ void group_params(float mn, float mx, TS& st, float& s, float& r,
+                                             float& zpf) {
+  if constexpr (SYM) {
+    scale_sym<TS>(fmaxf(-mn, mx), st, s);
+    zpf = 8.0f;
+  } else {
+    int zp;
+    scale_zero<TS>(mn, mx, st, s, zp);
+    zpf = (float)zp;
+  }
+  r = __builtin_amdgcn_rcpf(s);
+}
+
+template <bool SYM>
+__device__ __forceinline__ uint32_t pack8v(const float* v, float s, float r, float zpf) {
+  if constexpr (SYM) return pack8_sym(v, s, r);
+  else return pack8(v, s, r, zpf);
+}
+
 // ---------------------------------------------------------------------------
 // Quantize + pack, groups of g = 32 L elements, L = 1, 2, 4, 8, 16.
 // The tensor is treated as a flat run of N*K elements: with K % g == 0 a
@@ -105,7 +177,7 @@ __device__ __forceinline__ uint32_t pack8(const float* v, float s, float r, floa
 // butterflies, so the per-group work (scale, zero-point, reciprocal) is
 // shared by 4 words.  U pieces per lane are loaded up front.
 // ---------------------------------------------------------------------------
-template <typename TIn, typename TS, int L, int U>
+template <typename TIn, typename TS, int L, int U, bool SYM>
 __global__ __launch_bounds__(256) void k_quantize_pack_sub(const void* __restrict__ w,
                                                           int64_t npieces,
                                                           uint32_t* __restrict__ packed,
@@ -171,16 +243,13 @@ __global__ __launch_bounds__(256) void k_quantize_pack_sub(const void* __restric
     mn = group_min<L>(mn);
     mx = group_max<L>(mx);
     TS st;
-    float s;
-    int zp;
-    scale_zero<TS>(mn, mx, st, s, zp);
-    const float r = __builtin_amdgcn_rcpf(s);
-    const float zpf = (float)zp;
+    float s, r, zpf;
+    group_params<TS, SYM>(mn, mx, st, s, r, zpf);
     u32x4 words;
-    words.x = pack8(v[u][0], s, r, zpf);
-    words.y = pack8(v[u][1], s, r, zpf);
-    words.z = pack8(v[u][2], s, r, zpf);
-    words.w = pack8(v[u][3], s, r, zpf);
+    words.x = pack8v<SYM>(v[u][0], s, r, zpf);
+    words.y = pack8v<SYM>(v[u][1], s, r, zpf);
+    words.z = pack8v<SYM>(v[u][2], s, r, zpf);
+    words.w = pack8v<SYM>(v[u][3], s, r, zpf);
     if (p < npieces) {
       ((u32x4*)packed)[p] = words;
       if ((threadIdx.x & (L - 1)) == 0) {
@@ -196,7 +265,7 @@ __global__ __launch_bounds__(256) void k_quantize_pack_sub(const void* __restric
 // Quantize + pack, any group size that is a multiple of 8: one wave per
 // group, two passes over the group (the second pass reads it from cache).
 // ---------------------------------------------------------------------------
-template <typename TIn, typename TS>
+template <typename TIn, typename TS, bool SYM>
 __global__ __launch_bounds__(256) void k_quantize_pack_wave(const void* __restrict__ w,
                                                            int64_t ngroups, int cpg,
                                                            uint32_t* __restrict__ packed,
@@ -219,22 +288,20 @@ __global__ __launch_bounds__(256) void k_quantize_pack_wave(const void* __restri
   mn = group_min<kWave>(mn);
   mx = group_max<kWave>(mx);
   TS st;
-  float s;
-  int zp;
-  scale_zero<TS>(mn, mx, st, s, zp);
-  const float r = __builtin_amdgcn_rcpf(s);
+  float s, r, zpf;
+  group_params<TS, SYM>(mn, mx, st, s, r, zpf);
   for (int c = lane; c < cpg; c += kWave) {
     float v[8];
     Load8<TIn>::run(w, c0 + c, v);
-    packed[c0 + c] = pack8(v, s, r, (float)zp);
+    packed[c0 + c] = pack8v<SYM>(v, s, r, zpf);
   }
   if (lane == 0) {
     scales[grp] = st;
-    zeros[grp] = (TS)(float)zp;
+    zeros[grp] = (TS)zpf;
   }
 }
 
-template <typename TIn, typename TS>
+template <typename TIn, typename TS, bool SYM>
 static hipError_t launch_qp(const void* w, int64_t n, int64_t k, int g, uint8_t* packed, void* scales,
                             void* zeros, hipStream_t st) {
   const int64_t npieces = n * k / 32;
@@ -249,38 +316,46 @@ static hipError_t launch_qp(const void* w, int64_t n, int64_t k, int g, uint8_t*
   const dim3 grid((unsigned)((npieces + per_block - 1) / per_block));
   switch (g) {
     case 32:
-      k_quantize_pack_sub<TIn, TS, 1, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 1, U, SYM><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 64:
-      k_quantize_pack_sub<TIn, TS, 2, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 2, U, SYM><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 128:
-      k_quantize_pack_sub<TIn, TS, 4, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 4, U, SYM><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 256:
-      k_quantize_pack_sub<TIn, TS, 8, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 8, U, SYM><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     case 512:
-      k_quantize_pack_sub<TIn, TS, 16, U><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
+      k_quantize_pack_sub<TIn, TS, 16, U, SYM><<<grid, 256, 0, st>>>(w, npieces, pk, sc, zr);
       break;
     default: {
       const int64_t ngroups = n * (k / g);
       const dim3 g2((unsigned)((ngroups + 3) / 4));
-      k_quantize_pack_wave<TIn, TS><<<g2, 256, 0, st>>>(w, ngroups, g / 8, pk, sc, zr);
+      k_quantize_pack_wave<TIn, TS, SYM><<<g2, 256, 0, st>>>(w, ngroups, g / 8, pk, sc, zr);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
-                                uint8_t* packed, void* scales, void* zeros, int sz_dtype,
-                                hipStream_t st) {
+template <bool SYM>
+static hipError_t launch_qp_sz(const void* w, int w_dtype, int64_t n, int64_t k, int g,
+                               uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                               hipStream_t st) {
   const bool in_bf16 = (w_dtype == W4_BF16);
   const bool s_f16 = (sz_dtype == W4_F16);
-  if (in_bf16 && s_f16) return launch_qp<__bf16, _Float16>(w, n, k, g, packed, scales, zeros, st);
-  if (in_bf16) return launch_qp<__bf16, float>(w, n, k, g, packed, scales, zeros, st);
-  if (s_f16) return launch_qp<float, _Float16>(w, n, k, g, packed, scales, zeros, st);
-  return launch_qp<float, float>(w, n, k, g, packed, scales, zeros, st);
+  if (in_bf16 && s_f16) return launch_qp<__bf16, _Float16, SYM>(w, n, k, g, packed, scales, zeros, st);
+  if (in_bf16) return launch_qp<__bf16, float, SYM>(w, n, k, g, packed, scales, zeros, st);
+  if (s_f16) return launch_qp<float, _Float16, SYM>(w, n, k, g, packed, scales, zeros, st);
+  return launch_qp<float, float, SYM>(w, n, k, g, packed, scales, zeros, st);
+}
+
+hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
+                                uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                                bool symmetric, hipStream_t st) {
+  if (symmetric) return launch_qp_sz<true>(w, w_dtype, n, k, g, packed, scales, zeros, sz_dtype, st);
+  return launch_qp_sz<false>(w, w_dtype, n, k, g, packed, scales, zeros, sz_dtype, st);
 }
 
 // ---------------------------------------------------------------------------

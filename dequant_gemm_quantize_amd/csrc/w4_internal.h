@@ -29,7 +29,7 @@ hipError_t once_per_device(std::atomic<uint64_t>& done, F set) {
 
 hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
                                 uint8_t* packed, void* scales, void* zeros, int sz_dtype,
-                                hipStream_t st);
+                                bool symmetric, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* packed, const void* scales, const void* zeros,
                           int sz_dtype, int64_t n, int64_t k, int g, void* out, int out_dtype,
                           hipStream_t st);

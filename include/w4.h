@@ -84,6 +84,25 @@ int quantize_pack_int4(const void* w, int w_dtype, int64_t n, int64_t k, int32_t
                        hipStream_t stream);
 
 /*
+ * quantize_pack_int4_sym -- group-wise symmetric INT4 round-to-nearest + pack.
+ *
+ * For each group G of W ([P4] Step 2 for scale and codes, Step 4 for the
+ * +8 storage offset), in IEEE float32 with round-to-nearest-even:
+ *   amax   = max(|G|)
+ *   scale  = amax / 7, rounded to sz_dtype; a stored 0 becomes 1
+ *   q(w)   = clamp(rint(w / scale), -8, 7) + 8   (with the stored scale;
+ *            the offset is added after rounding)
+ * and the codes are packed two per byte, even column in the low nibble.
+ * Every zero-point is 8, and zeros[] is written with 8, so dequant_int4,
+ * w4a16_matmul and w4a8_matmul take the three outputs unchanged and compute
+ * (q - 8) * scale.  Arguments, layout, limits and errors are those of
+ * quantize_pack_int4.  The outputs are bit-for-bit those of the definition.
+ */
+int quantize_pack_int4_sym(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                           uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                           hipStream_t stream);
+
+/*
  * dequant_int4 -- w_out[n, k] = (q[n, k] - zp[n, k/g]) * scale[n, k/g]
  * ([P5] Step 4), computed as one float32 product of the exact integer
  * difference and the scale, then rounded (nearest-even) to out_dtype

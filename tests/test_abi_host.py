@@ -33,8 +33,8 @@ def lib():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    for want in ("quantize_pack_int4", "dequant_int4", "quantize_act_int8", "w4a16_matmul",
-                 "w4a8_matmul", "w4_status_string", "w4_last_error", "w4_version"):
+    for want in ("quantize_pack_int4", "quantize_pack_int4_sym", "dequant_int4", "quantize_act_int8",
+                 "w4a16_matmul", "w4a8_matmul", "w4_status_string", "w4_last_error", "w4_version"):
         assert want in names, names
 
 
@@ -81,13 +81,16 @@ def _err(lib):
     ((A, 2, 1 << 14, 1 << 23, 32, A, A, A, 1, None), "n * k"),
     ((A, 2, 4, (1 << 23) + 32, 32, A, A, A, 1, None), "k = 8388640 is too large"),
 ])
-def test_quantize_pack_rejects(lib, args, msg):
-    assert lib.quantize_pack_int4(*args) == -1
+@pytest.mark.parametrize("name", ["quantize_pack_int4", "quantize_pack_int4_sym"])
+def test_quantize_pack_rejects(lib, name, args, msg):
+    assert getattr(lib, name)(*args) == -1
     assert msg in _err(lib), _err(lib)
+    assert _err(lib).startswith(name + ":"), _err(lib)
 
 
 def test_empty_calls_are_noops(lib):
     assert lib.quantize_pack_int4(None, 2, 0, 128, 32, None, None, None, 1, None) == 0
+    assert lib.quantize_pack_int4_sym(None, 2, 0, 128, 32, None, None, None, 1, None) == 0
     assert lib.dequant_int4(None, None, None, 1, 0, 128, 32, None, 2, None) == 0
     assert lib.quantize_act_int8(None, 2, 0, 128, None, None, None) == 0
     assert lib.w4a16_matmul(None, 2, 0, 128, None, None, None, 1, 64, 128, None, 2, None) == 0
@@ -149,6 +152,8 @@ def test_binding_refuses_cpu_tensors():
     import dequant_gemm_quantize_amd as w4
     with pytest.raises(ValueError, match="GPU only"):
         w4.quantize_pack_int4(torch.zeros(4, 128), 32)
+    with pytest.raises(ValueError, match="GPU only"):
+        w4.quantize_pack_int4_sym(torch.zeros(4, 128), 32)
 
 
 def test_product_path_does_not_import_the_oracle():
