@@ -98,12 +98,16 @@ template <> struct SZ<float> {
 
 // CH: 16-byte chunks (32 columns) per lane and row, K <= 2048 CH.  Lane l
 // takes chunks l, l + 64, ...; chunks past the row's K / 32 reuse its last
-// chunk's addresses and contribute nothing (zero scale pair).
-template <typename TS, typename TY, int MT, int CH>
+// chunk's addresses and contribute nothing (zero scale pair).  FULL: K is
+// exactly 2048 CH, so no chunk lies past the row and no index needs a clamp.
+// ng = K / g groups per row; cpg_magic = ceil(2^32 / cpg) for cpg = g / 32
+// chunks per group, so that umulhi(ci, cpg_magic) == ci / cpg exactly for
+// every chunk index (ci * cpg^2 < 2^32 holds for ci < 384, cpg <= 384).
+template <typename TS, typename TY, int MT, int CH, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
-    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
-    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
-    void* __restrict__ y) {
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ packed,
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int ng,
+    uint32_t cpg_magic, void* __restrict__ y) {
   // LDS: activations [MT][K] bf16 (natural order; region rounded up to the
   // staging lanes), scale tile [16][ng] as (s, -s*(128+zp)) float pairs
   // (region of 1024 pairs).
@@ -111,7 +115,6 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   constexpr int kRowsWave = rows_wave(CH);
   constexpr int kRowsWg = kWavesWg * kRowsWave;
   constexpr int XPER_ = (MT * CH * 2048 / 8 + kThreads - 1) / kThreads;
-  const int ng = (int)(K / g);
   u32x4* x_l = (u32x4*)lds;
   float2* sz_l = (float2*)(lds + XPER_ * kThreads * 16);
 
@@ -121,42 +124,50 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   const int64_t n0 = (int64_t)blockIdx.x * kRowsWg;
 
   // ---- 1. staging loads (activations, scale / zero-point tile), straight
-  //         line: XPER / SPER per thread, indices clamped into range -------
+  //         line: XPER / SPER per thread, indices clamped into range.  All
+  //         addresses are a uniform base plus a 32-bit lane offset. --------
   constexpr int XPER = XPER_;  // 16-byte activation groups per thread
-  const int xgroups = MT * (int)(K / 8);
-  const u32x4* xg = (const u32x4*)x;
+  // FULL: XPER * kThreads == MT * K / 8 exactly
+  const int xgroups = MT * (K / 8);
+  const char* xg = (const char*)x;
   u32x4 xv[XPER];
 #pragma unroll
   for (int r = 0; r < XPER; ++r) {
-    const int i = tid + kThreads * r;
-    xv[r] = xg[i < xgroups ? i : xgroups - 1];
+    int i = tid + kThreads * r;
+    if constexpr (!FULL) i = i < xgroups ? i : xgroups - 1;
+    xv[r] = *(const u32x4*)(xg + (uint32_t)i * 16u);
   }
-  const int tile = kRowsWg * ng;  // <= 16 * 16 CH elements for g >= 128
-  constexpr int SPER = (kRowsWg * 16 * CH + kThreads - 1) / kThreads;
+  // The workgroup's rows are consecutive, so their scales (and zeros) are
+  // one contiguous run of rows * ng elements; rows past N are never stored,
+  // so their slots just repeat the last valid element.
+  constexpr int SPER = (kRowsWg * 16 * CH + kThreads - 1) / kThreads;  // >= kRowsWg * ng
   typedef typename SZ<TS>::T R;
+  const int64_t nrows_valid = N - n0 < kRowsWg ? N - n0 : kRowsWg;
+  const int tvalid = (int)nrows_valid * ng;
+  const char* sbase = (const char*)scales + n0 * ng * (int64_t)sizeof(R);
+  const char* zbase = (const char*)zeros + n0 * ng * (int64_t)sizeof(R);
   R sv[SPER], zv[SPER];
 #pragma unroll
   for (int r = 0; r < SPER; ++r) {
     const int e = tid + kThreads * r;
-    const int ee = e < tile ? e : tile - 1;
-    const int rr = ee / ng, q = ee - rr * ng;
-    const int64_t row = (n0 + rr) < N ? (n0 + rr) : (N - 1);
-    sv[r] = ((const R*)scales)[row * ng + q];
-    zv[r] = ((const R*)zeros)[row * ng + q];
+    const uint32_t off = (uint32_t)(e < tvalid ? e : tvalid - 1) * (uint32_t)sizeof(R);
+    sv[r] = *(const R*)(sbase + off);
+    zv[r] = *(const R*)(zbase + off);
   }
 
   // ---- 2. codes of the wave's rows: kRowsWave x CH 16-byte loads per lane --
-  const int nchunk = (int)(K / 32);
+  const int nchunk = K / 32;
   u32x4 wq[kRowsWave][CH];
 #pragma unroll
   for (int r = 0; r < kRowsWave; ++r) {
     int64_t n = n0 + wave * kRowsWave + r;
     n = n < N ? n : N - 1;
-    const u32x4* row = (const u32x4*)(packed + n * (K / 2));
+    const char* row = (const char*)packed + n * (int64_t)(K / 2);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int ci = lane + 64 * c;
-      wq[r][c] = __builtin_nontemporal_load(row + (ci < nchunk ? ci : nchunk - 1));
+      int ci = lane + 64 * c;
+      if constexpr (!FULL) ci = ci < nchunk ? ci : nchunk - 1;
+      wq[r][c] = __builtin_nontemporal_load((const u32x4*)(row + (uint32_t)ci * 16u));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -181,8 +192,9 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     for (int c = 0; c < CH; ++c) {
       // columns 32*(lane + 64c) .. +31 = 16-byte groups 4*(lane + 64c) .. +3
       // (past K: the staged copies of the last group, never used)
-      const int ci = lane + 64 * c < nchunk ? lane + 64 * c : nchunk - 1;
-      const u32x4* src = x_l + (int64_t)m * (K / 8) + 4 * ci;
+      int ci = lane + 64 * c;
+      if constexpr (!FULL) ci = ci < nchunk ? ci : nchunk - 1;
+      const u32x4* src = x_l + m * (K / 8) + 4 * ci;
       float s = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -202,7 +214,11 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   const NibConst nk = NibConst::make();
   int gq[CH];  // group of the lane's chunk c, or -1 past the row's end
 #pragma unroll
-  for (int c = 0; c < CH; ++c) gq[c] = lane + 64 * c < nchunk ? (32 * (lane + 64 * c)) / g : -1;
+  for (int c = 0; c < CH; ++c) {
+    const int ci = lane + 64 * c;
+    gq[c] = (int)__umulhi((uint32_t)ci, cpg_magic);
+    if constexpr (!FULL) gq[c] = ci < nchunk ? gq[c] : -1;
+  }
 #pragma unroll
   for (int r = 0; r < kRowsWave; ++r) {
     const int rr = wave * kRowsWave + r;
@@ -211,7 +227,8 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const float2 sc = gq[c] >= 0 ? sz_l[rr * ng + gq[c]] : float2{0.0f, 0.0f};
+      float2 sc = sz_l[rr * ng + (gq[c] >= 0 ? gq[c] : 0)];
+      if constexpr (!FULL) sc = gq[c] >= 0 ? sc : float2{0.0f, 0.0f};
       const uint32_t w4[4] = {wq[r][c].x, wq[r][c].y, wq[r][c].z, wq[r][c].w};
       float d[MT];
 #pragma unroll
@@ -254,18 +271,32 @@ bool dot2_fits(int64_t m, int64_t k, int g) {
   return m == 1 && g >= 128 && k % 32 == 0 && k <= 6 * 2048;
 }
 
-template <typename TS, typename TY, int MT>
+template <typename TS, typename TY, int MT, bool FULL>
 static void dot2_go(dim3 grid, hipStream_t st, const uint16_t* x, int64_t k, const uint8_t* packed,
                     const void* scales, const void* zeros, int64_t n, int g, void* y) {
   const size_t lds = dot2_lds_bytes(MT, k, g);
+  const uint32_t cpg = (uint32_t)(g / 32);
+  const uint32_t magic = (uint32_t)((((uint64_t)1 << 32) + cpg - 1) / cpg);
+  const int ki = (int)k, ng = (int)(k / g);
+#define W4_DOT2_CASE(C)                                                                          \
+  k_w4a16_dot2<TS, TY, MT, C, FULL><<<grid, kThreads, lds, st>>>(x, MT, ki, packed, scales, zeros, \
+                                                                 n, ng, magic, y)
   switch (dot2_ch(k)) {
-    case 1: k_w4a16_dot2<TS, TY, MT, 1><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    case 2: k_w4a16_dot2<TS, TY, MT, 2><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    case 3: k_w4a16_dot2<TS, TY, MT, 3><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    case 4: k_w4a16_dot2<TS, TY, MT, 4><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    case 5: k_w4a16_dot2<TS, TY, MT, 5><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
-    default: k_w4a16_dot2<TS, TY, MT, 6><<<grid, kThreads, lds, st>>>(x, MT, k, packed, scales, zeros, n, g, y); break;
+    case 1: W4_DOT2_CASE(1); break;
+    case 2: W4_DOT2_CASE(2); break;
+    case 3: W4_DOT2_CASE(3); break;
+    case 4: W4_DOT2_CASE(4); break;
+    case 5: W4_DOT2_CASE(5); break;
+    default: W4_DOT2_CASE(6); break;
   }
+#undef W4_DOT2_CASE
+}
+
+template <typename TS, typename TY>
+static void dot2_full(dim3 grid, hipStream_t st, const uint16_t* x, int64_t k, const uint8_t* packed,
+                      const void* scales, const void* zeros, int64_t n, int g, void* y) {
+  if (k % 2048 == 0) dot2_go<TS, TY, 1, true>(grid, st, x, k, packed, scales, zeros, n, g, y);
+  else dot2_go<TS, TY, 1, false>(grid, st, x, k, packed, scales, zeros, n, g, y);
 }
 
 hipError_t launch_w4a16_dot2(const void* x, int64_t m, int64_t k, const uint8_t* packed,
@@ -276,10 +307,10 @@ hipError_t launch_w4a16_dot2(const void* x, int64_t m, int64_t k, const uint8_t*
   const uint16_t* xb = (const uint16_t*)x;
   const bool sh = sz_dtype == W4_F16, yf = y_dtype == W4_F32;
   (void)m;  // one token (dot2_fits)
-  if (sh && yf) dot2_go<_Float16, float, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
-  else if (sh) dot2_go<_Float16, __bf16, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
-  else if (yf) dot2_go<float, float, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
-  else dot2_go<float, __bf16, 1>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+  if (sh && yf) dot2_full<_Float16, float>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+  else if (sh) dot2_full<_Float16, __bf16>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+  else if (yf) dot2_full<float, float>(grid, st, xb, k, packed, scales, zeros, n, g, y);
+  else dot2_full<float, __bf16>(grid, st, xb, k, packed, scales, zeros, n, g, y);
   return hipGetLastError();
 }
 
