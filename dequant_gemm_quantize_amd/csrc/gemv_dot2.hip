@@ -16,10 +16,11 @@
 // Work layout.  A workgroup of W waves owns W * RW weight rows; wave w owns
 // rows RW*w .. RW*w + RW-1 over all of K.  Lane l covers the 16-byte chunks l, l+64, ...
 // of a row (32 columns each), so every load instruction reads 1 KB of one
-// row contiguously.  The activations of the lane's columns are read once
-// into registers (through LDS, staged by the workgroup) and reused for the
-// wave's rows; the chunk sums xs are formed once as well.  Each row's
-// 64 partial sums are added with DPP row operations.
+// row contiguously.  The workgroup stages the activations in LDS once,
+// already interleaved into the codes' pair order, with their chunk sums xs;
+// each lane reads its columns into registers and reuses them for the wave's
+// rows.  The rows' 64 partial sums are added together at the end (quad
+// exchanges, DPP row shifts, two cross-row shuffles).
 #include "w4_common.h"
 #include "w4_internal.h"
 
@@ -61,16 +62,36 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Sum over the 64 lanes of a wave, result valid in lane 63 (DPP row ops).
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  // within rows of 16 lanes
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));  // row_shr:1
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));  // row_shr:2
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));  // row_shr:4
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));  // row_shr:8
-  // across rows
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));  // row_bcast:15
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf,
+                                                               0xf, false));
+}
+
+// Sums over the 64 lanes of R per-lane values a[0..R-1] (R = 2 or 4) at
+// once: two quad exchanges leave lane l with the 4-lane partial of value
+// l mod R (l mod 4 for R = 4, each class held twice per quad for R = 2), row
+// shifts finish the rows of 16 lanes, and two cross-row shuffles the wave.
+// Lane 64 - R + j returns the total of a[j].
+template <int R>
+__device__ __forceinline__ float wave_sum_rows(const float (&a)[R], int lane) {
+  static_assert(R == 2 || R == 4, "two or four values");
+  constexpr int kXor1 = 0xB1, kXor2 = 0x4E;  // quad_perm [1,0,3,2], [2,3,0,1]
+  const bool odd = lane & 1;
+  float v;
+  if constexpr (R == 4) {
+    const float v01 = (odd ? a[1] : a[0]) + dpp<kXor1>(odd ? a[0] : a[1]);
+    const float v23 = (odd ? a[3] : a[2]) + dpp<kXor1>(odd ? a[2] : a[3]);
+    const bool hi = lane & 2;
+    v = (hi ? v23 : v01) + dpp<kXor2>(hi ? v01 : v23);
+  } else {
+    v = (odd ? a[1] : a[0]) + dpp<kXor1>(odd ? a[0] : a[1]);
+    v += dpp<kXor2>(v);
+  }
+  v += dpp<0x114>(v);  // row_shr:4 (lanes shifted in from outside the row add 0)
+  v += dpp<0x118>(v);  // row_shr:8
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -108,15 +129,17 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int ng,
     uint32_t cpg_magic, void* __restrict__ y) {
-  // LDS: activations [MT][K] bf16 (natural order; region rounded up to the
-  // staging lanes), scale tile [16][ng] as (s, -s*(128+zp)) float pairs
-  // (region of 1024 pairs).
+  // LDS: activations [MT][K] bf16, each 16-byte group interleaved into the
+  // codes' pair order; their 32-column chunk sums [MT][K/32]; scale tile
+  // [rows][ng] as (s, -s*(128+zp)) float pairs.  Each region is rounded up
+  // to the staging lanes.
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   constexpr int kRowsWave = rows_wave(CH);
   constexpr int kRowsWg = kWavesWg * kRowsWave;
   constexpr int XPER_ = (MT * CH * 2048 / 8 + kThreads - 1) / kThreads;
   u32x4* x_l = (u32x4*)lds;
-  float2* sz_l = (float2*)(lds + XPER_ * kThreads * 16);
+  float* xsum_l = (float*)(lds + XPER_ * kThreads * 16);
+  float2* sz_l = (float2*)(lds + XPER_ * kThreads * 20);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,9 +196,21 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 3. LDS stores (wait for the staging loads only) ---------------------
-  // unconditional: the LDS regions have room for every staging lane
+  // unconditional: the LDS regions have room for every staging lane.  The
+  // four 16-byte groups of a 32-column chunk sit in lanes 4j .. 4j+3, so two
+  // row shifts gather the chunk's sum in lane 4j+3.
 #pragma unroll
-  for (int r = 0; r < XPER; ++r) x_l[tid + kThreads * r] = xv[r];
+  for (int r = 0; r < XPER; ++r) {
+    uint32_t o[4];
+    interleave(xv[r], o);
+    x_l[tid + kThreads * r] = u32x4{o[0], o[1], o[2], o[3]};
+    float p = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) p = dot2(o[t], 0x3f803f80u, p);  // + x_a * 1.0 + x_b * 1.0
+    p += dpp<0x111>(p);  // row_shr:1
+    p += dpp<0x112>(p);  // row_shr:2
+    if ((tid & 3) == 3) xsum_l[(tid + kThreads * r) >> 2] = p;
+  }
 #pragma unroll
   for (int r = 0; r < SPER; ++r) {
     const float sf = SZ<TS>::f(sv[r]);
@@ -183,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
   }
   __syncthreads();
 
-  // ---- activations of this lane's columns, interleaved; chunk sums --------
+  // ---- activations of this lane's columns (interleaved) and chunk sums ----
   uint32_t xa[MT][CH][16];
   float xs[MT][CH];
 #pragma unroll
@@ -195,19 +230,15 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
       int ci = lane + 64 * c;
       if constexpr (!FULL) ci = ci < nchunk ? ci : nchunk - 1;
       const u32x4* src = x_l + m * (K / 8) + 4 * ci;
-      float s = 0.0f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x4 v = src[q];
-        uint32_t o[4];
-        interleave(v, o);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          xa[m][c][4 * q + t] = o[t];
-          s = dot2(o[t], 0x3f803f80u, s);  // + x_a * 1.0 + x_b * 1.0
-        }
+        xa[m][c][4 * q + 0] = v.x;
+        xa[m][c][4 * q + 1] = v.y;
+        xa[m][c][4 * q + 2] = v.z;
+        xa[m][c][4 * q + 3] = v.w;
       }
-      xs[m][c] = s;
+      xs[m][c] = xsum_l[m * (K / 32) + ci];
     }
 
   // ---- rows: dot products, scale, zero-point correction, wave sums --------
@@ -219,12 +250,12 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
     gq[c] = (int)__umulhi((uint32_t)ci, cpg_magic);
     if constexpr (!FULL) gq[c] = ci < nchunk ? gq[c] : -1;
   }
+  float acc[MT][kRowsWave];
 #pragma unroll
   for (int r = 0; r < kRowsWave; ++r) {
     const int rr = wave * kRowsWave + r;
-    float acc[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    for (int m = 0; m < MT; ++m) acc[m][r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       float2 sc = sz_l[rr * ng + (gq[c] >= 0 ? gq[c] : 0)];
@@ -243,14 +274,15 @@ __global__ __launch_bounds__(kThreads) void k_w4a16_dot2(
           for (int u = 0; u < 4; ++u) d[m] = dot2(b[u], xa[m][c][4 * t + u], d[m]);
       }
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = fmaf(sc.x, d[m], fmaf(sc.y, xs[m][c], acc[m]));
+      for (int m = 0; m < MT; ++m) acc[m][r] = fmaf(sc.x, d[m], fmaf(sc.y, xs[m][c], acc[m][r]));
     }
+  }
+  // ---- wave sums of the rows; lane 64 - kRowsWave + j stores row j --------
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float tot = wave_sum_dpp(acc[m]);
-      const int64_t n = n0 + rr;
-      if (lane == 63 && m < M && n < N) put<TY>(y, (int64_t)m * N + n, tot);
-    }
+  for (int m = 0; m < MT; ++m) {
+    const float tot = wave_sum_rows<kRowsWave>(acc[m], lane);
+    const int64_t n = n0 + wave * kRowsWave + (lane & (kRowsWave - 1));
+    if (lane >= 64 - kRowsWave && m < M && n < N) put<TY>(y, (int64_t)m * N + n, tot);
   }
 }
 
@@ -261,7 +293,7 @@ size_t dot2_lds_bytes(int64_t m, int64_t k, int g) {
   const int ch = dot2_ch(k);
   const int rows_wg = kWavesWg * rows_wave(ch);
   const int64_t xper = (m * ch * 2048 / 8 + kThreads - 1) / kThreads;
-  return (size_t)(xper * kThreads * 16 + ((rows_wg * 16 * ch + kThreads - 1) / kThreads) * kThreads * 8);
+  return (size_t)(xper * kThreads * 20 + ((rows_wg * 16 * ch + kThreads - 1) / kThreads) * kThreads * 8);
 }
 
 bool dot2_fits(int64_t m, int64_t k, int g) {
