@@ -98,7 +98,13 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           # one token, K not a multiple of 2048 (the dot2 kernel's partial
           # last chunk round), up to its K = 12288 limit
           (1, 50, 11008, 128, "f16", "bf16"), (1, 33, 2560, 256, "f32", "f32"),
-          (1, 20, 12288, 128, "f16", "bf16"), (1, 7, 640, 128, "f16", "bf16")]
+          (1, 20, 12288, 128, "f16", "bf16"), (1, 7, 640, 128, "f16", "bf16"),
+          # one token, K a whole number of 2048-column rounds (no clamps),
+          # groups of 128 .. 2048 columns, 384 among them (a group index
+          # that is not a shift)
+          (1, 33, 2048, 128, "f16", "bf16"), (1, 50, 6144, 256, "f32", "f32"),
+          (1, 17, 12288, 128, "f16", "bf16"), (1, 40, 8192, 2048, "f16", "bf16"),
+          (1, 20, 6144, 384, "f16", "bf16"), (1, 130, 10240, 128, "f32", "bf16")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz,ykind", DECODE)
