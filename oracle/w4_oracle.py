@@ -34,6 +34,12 @@ test in tests/test_oracle_pins.py):
   * symmetric variant: scale = absmax/7 and code clamp(round(w/scale), -8, 7)
     ([P4] Step 2), stored with the +8 offset of [P4] Step 4, i.e. a fixed
     zero-point of 8; same stored-scale and zero-guard readings as above;
+  * calibrated symmetric scales ([P3] Step 4): the p-th percentile of |w|
+    (linear between order statistics) as the range, or the step chosen by the
+    MSE search over n candidates from min|w| to max|w| (codes clamped to
+    +-7 during the search, w/c taken as w * fl32(1/c), squared errors summed
+    in fp32 in column order, first minimum wins); the codes are then the
+    symmetric ones with the stored scale;
   * per-token activation scale max(max|x|, 1e-8)/127 and
     clamp(round(x/s), -128, 127) ([P1] Step 3);
   * matmul y = x . dequant(W)^T ([P3] Step 2; [P4] Step 5), and for the
@@ -202,6 +208,93 @@ def quantize_pack_int4_sym(w: np.ndarray, kind: str, g: int, sz: str):
     q = quantize_codes_sym(w32, s_st, g)
     zeros = np.full(s_st.shape, SYM_OFFSET, SZ_DTYPES[sz])
     return pack_nibbles(q), s_st, zeros
+
+
+# --------------------------------------------------------------------------
+# Range-clipping calibrators for the symmetric variant ([P3] Step 4): they
+# choose each group's scale differently; the codes are then the symmetric
+# ones, clamp(rint(w / scale), -8, 7) + 8 with the stored scale.
+# --------------------------------------------------------------------------
+def store_scale(s32: np.ndarray, sz: str) -> np.ndarray:
+    """fp32 step -> storage dtype (nearest even); a stored 0 becomes 1."""
+    sd = SZ_DTYPES[sz]
+    s_st = np.asarray(s32, F32).astype(sd)
+    return np.where(s_st == 0, sd(1.0), s_st).astype(sd)
+
+
+def percentile_position(g: int, p: float):
+    """Where the p-th percentile of g sorted values lies: h = (g - 1) p / 100
+    in float64, returned as (i0, i1, f) with i0 = floor(h), i1 = min(i0 + 1,
+    g - 1) and f = fl32(h - i0)."""
+    h = (g - 1) * (p / 100.0)
+    i0 = int(np.floor(h))
+    return i0, min(i0 + 1, g - 1), F32(h - i0)
+
+
+def calib_percentile_range(w32: np.ndarray, g: int, p: float) -> np.ndarray:
+    """[P3] Step 4, "percentile": the p-th percentile of |w| per group, linear
+    between neighbouring order statistics a (ascending):
+    fl32(a[i0] + fl32(f * fl32(a[i1] - a[i0])))."""
+    a = np.sort(np.abs(split_groups(w32, g)), axis=2)
+    i0, i1, f = percentile_position(g, p)
+    lo = a[..., i0].astype(F32)
+    hi = a[..., i1].astype(F32)
+    return (lo + f * (hi - lo)).astype(F32)
+
+
+def quantize_pack_int4_sym_percentile(w: np.ndarray, kind: str, g: int, sz: str, p: float):
+    """Symmetric quantize + pack with range = the p-th percentile of |w|
+    (scale = range / 7, as scale_sym does with the maximum)."""
+    w32 = as_f32(w, kind)
+    s_st = scale_sym(calib_percentile_range(w32, g, p), sz)
+    q = quantize_codes_sym(w32, s_st, g)
+    return pack_nibbles(q), s_st, np.full(s_st.shape, SYM_OFFSET, SZ_DTYPES[sz])
+
+
+def mse_candidates(lo: np.ndarray, hi: np.ndarray, n: int) -> np.ndarray:
+    """n steps spaced linearly from lo to hi ([P3] Step 4 "mse_search"):
+    c_i = fl32(lo + fl32(i * d)) with d = fl32(fl32(hi - lo) / (n - 1))."""
+    d = ((hi.astype(F32) - lo.astype(F32)) / F32(n - 1)).astype(F32)
+    i = np.arange(n, dtype=F32)
+    return (lo.astype(F32)[..., None] + (i * d[..., None]).astype(F32)).astype(F32)
+
+
+MSE_SKIP_BELOW = F32(1e-10)
+MSE_NONE = F32(1e-8)
+
+
+def calib_mse_step(w32: np.ndarray, g: int, n: int) -> np.ndarray:
+    """[P3] Step 4, "mse_search", per group: candidate steps c from min|w| to
+    max|w|; each c below 1e-10 is skipped; for the others the codes are
+    q = clamp(rint(fl32(w * fl32(1 / c))), -7, 7) and the error is
+    E(c) = sum over the group, in column order, of fl32(fl32(q * c) - w)^2,
+    accumulated in fp32.  The first candidate with the least E is the step;
+    1e-8 when every candidate is skipped.  Minimising the sum is minimising
+    the page's mean."""
+    wg = split_groups(w32, g)
+    a = np.abs(wg)
+    c = mse_candidates(a.min(axis=2), a.max(axis=2), n)
+    valid = c >= MSE_SKIP_BELOW
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        r = (F32(1.0) / c).astype(F32)
+        E = np.zeros(c.shape, F32)
+        for k in range(g):
+            wk = wg[..., k][..., None]
+            q = np.clip(np.rint((wk * r).astype(F32)), -7, 7).astype(F32)
+            e = ((q * c).astype(F32) - wk).astype(F32)
+            E = (E + (e * e).astype(F32)).astype(F32)
+    E = np.where(valid, E, np.inf)
+    best = np.argmin(E, axis=2)  # first occurrence of the minimum
+    step = np.take_along_axis(c, best[..., None], 2)[..., 0]
+    return np.where(valid.any(axis=2), step, MSE_NONE).astype(F32)
+
+
+def quantize_pack_int4_sym_mse(w: np.ndarray, kind: str, g: int, sz: str, n: int):
+    """Symmetric quantize + pack with the step chosen by the MSE search."""
+    w32 = as_f32(w, kind)
+    s_st = store_scale(calib_mse_step(w32, g, n), sz)
+    q = quantize_codes_sym(w32, s_st, g)
+    return pack_nibbles(q), s_st, np.full(s_st.shape, SYM_OFFSET, SZ_DTYPES[sz])
 
 
 # --------------------------------------------------------------------------

@@ -553,6 +553,138 @@ def check_sym_invariants():
 
 
 # ---------------------------------------------------------------------------
+# Range-clipping calibrators ("Building a From-Scratch Group-Wise INT4
+# Quantization Layer for LLaMA Weights", Step 4)
+# ---------------------------------------------------------------------------
+def check_percentile_100_is_minmax():
+    """The 100th percentile is the maximum: the outputs equal the plain
+    symmetric quantizer's bit for bit."""
+    rng = np.random.default_rng(21)
+    w = rng.normal(0, 0.05, (16, 512)).astype(np.float32)
+    w[3, 7] = -0.9
+    for sz in ("f16", "f32"):
+        for g in (32, 128):
+            a = O.quantize_pack_int4_sym_percentile(w, "f32", g, sz, 100.0)
+            b = O.quantize_pack_int4_sym(w, "f32", g, sz)
+            for x, y in zip(a, b):
+                assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+
+
+def check_percentile_vs_numpy():
+    """Against NumPy's linear-interpolation quantile in float64, within fp32
+    rounding."""
+    rng = np.random.default_rng(22)
+    w = rng.normal(0, 1, (8, 1024)).astype(np.float32)
+    for g in (32, 128, 1024):
+        for p in (50.0, 90.0, 99.0, 99.9):
+            got = O.calib_percentile_range(w, g, p).astype(np.float64)
+            want = np.quantile(np.abs(w.astype(np.float64)).reshape(8, -1, g), p / 100.0, axis=2,
+                               method="linear")
+            assert np.allclose(got, want, rtol=4e-7, atol=0), (g, p, float(np.abs(got - want).max()))
+
+
+def check_percentile_exact_midpoint():
+    """g = 32, p = 50: h = 15.5, so the range is the exact midpoint of the
+    16th and 17th smallest |w| (values chosen exact in binary)."""
+    g = 32
+    mags = np.arange(1, 33, dtype=np.float32) * np.float32(2.0 ** -8)  # 16th: 16/256, 17th: 17/256
+    w = (mags * np.where(np.arange(32) % 3 == 0, -1, 1)).astype(np.float32)[np.random.default_rng(1).permutation(32)]
+    r = O.calib_percentile_range(w.reshape(1, g), g, 50.0)
+    assert float(r[0, 0]) == 16.5 / 256, float(r[0, 0])
+    assert O.percentile_position(g, 50.0) == (15, 16, np.float32(0.5))
+    # 100th and tiny percentiles: the extreme order statistics
+    assert float(O.calib_percentile_range(w.reshape(1, g), g, 100.0)[0, 0]) == 32 / 256
+    i0, i1, f = O.percentile_position(g, 1e-9)
+    assert (i0, i1) == (0, 1) and 0 < f < 1e-9
+
+
+def check_calibrators_brute_force():
+    rng = np.random.default_rng(23)
+    w = rng.normal(0, 0.05, (3, 64)).astype(np.float32)
+    w[0, 5] = 0.7
+    w[2, 32:] = 0.0
+    for sz in ("f16", "f32"):
+        for p in (99.9, 75.0):
+            a = O.quantize_pack_int4_sym_percentile(w, "f32", 32, sz, p)
+            b = BF.quantize_pack_calibrated(w, 32, sz, "percentile", p)
+            for x, y in zip(a, b):
+                assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)), (sz, p)
+        a = O.quantize_pack_int4_sym_mse(w, "f32", 32, sz, 40)
+        b = BF.quantize_pack_calibrated(w, 32, sz, "mse", 40)
+        for x, y in zip(a, b):
+            assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)), sz
+
+
+def check_mse_exact_grid():
+    """Values on the grid j * u (j = -7 .. 7, zero included) with n = 8
+    candidates: c_i = i * u exactly, c_0 = 0 is skipped and c_1 = u
+    reproduces every value (error 0), so the step is u and the codes j + 8."""
+    u = 2.0 ** -7
+    j = np.array(list(range(-7, 8)) + [3, -3, 0, 7, -7, 1, 2, -1, -2, 5, -5, 4, -4, 6, -6, 0, 2], np.int64)
+    w = (j * u).astype(np.float32).reshape(1, 32)
+    assert float(O.calib_mse_step(w, 32, 8)[0, 0]) == u
+    for sz in ("f16", "f32"):
+        p, s, z = O.quantize_pack_int4_sym_mse(w, "f32", 32, sz, 8)
+        assert float(s[0, 0]) == u and float(z[0, 0]) == 8
+        assert np.array_equal(O.unpack_nibbles(p)[0].astype(np.int64), j + 8)
+
+
+def check_mse_first_minimum_and_clamp():
+    """Ties: 16 zeros and 16 fives, n = 11 (c_i = i / 2): the steps 1, 2.5
+    and 5 all reproduce the group exactly, and the first (1) wins.
+    Clamp: 16 values -8, one 7 and 15 zeros, n = 9 (c_i = i): with codes
+    clamped to +-7 the step 1 leaves error 16 (each -8 becomes -7) and the
+    step 2 leaves 1 (7 becomes 8), so 2 wins; a search clamped at -8 would
+    pick 1."""
+    w = np.array([0.0] * 16 + [5.0] * 16, np.float32)[np.random.default_rng(2).permutation(32)].reshape(1, 32)
+    assert float(O.calib_mse_step(w, 32, 11)[0, 0]) == 1.0
+    w2 = np.array([-8.0] * 16 + [7.0] + [0.0] * 15, np.float32).reshape(1, 32)
+    assert float(O.calib_mse_step(w2, 32, 9)[0, 0]) == 2.0
+
+
+def check_mse_skipped_candidates():
+    """Candidates below 1e-10 are skipped; a group with none left takes
+    1e-8, which underflows fp16 and is then stored as 1."""
+    g = 32
+    w = np.zeros((3, g), np.float32)
+    w[1, :4] = np.float32(5e-11)                  # max|w| < 1e-10: every candidate skipped
+    w[2, :] = np.float32(3e-10) * (np.arange(g) % 4)  # min 0, max 9e-10: c_0 = 0 skipped
+    st = O.calib_mse_step(w, g, 10)
+    assert st[0, 0] == O.MSE_NONE and st[1, 0] == O.MSE_NONE
+    assert st[2, 0] >= O.MSE_SKIP_BELOW
+    p16, s16, _ = O.quantize_pack_int4_sym_mse(w, "f32", g, "f16", 10)
+    assert float(s16[0, 0]) == 1.0 and (O.unpack_nibbles(p16)[:2] == 8).all()
+    p32, s32, _ = O.quantize_pack_int4_sym_mse(w, "f32", g, "f32", 10)
+    assert s32[0, 0] == O.MSE_NONE and (O.unpack_nibbles(p32)[0] == 8).all()
+
+
+def check_mse_is_least_error():
+    """The chosen step's error (recomputed in float64) is the least over the
+    candidates, up to fp32 rounding of the sums, and never above the plain
+    absmax/7 step's error by more than that."""
+    rng = np.random.default_rng(24)
+    w = rng.normal(0, 0.02, (4, 256)).astype(np.float32)
+    w[1, 3] = 0.3
+    g, n = 64, 200
+    st = O.calib_mse_step(w, g, n).astype(np.float64)
+    wg = w.astype(np.float64).reshape(4, -1, g)
+    a = np.abs(wg)
+    c = O.mse_candidates(a.min(axis=2).astype(np.float32), a.max(axis=2).astype(np.float32), n).astype(np.float64)
+
+    def err(step):
+        q = np.clip(np.rint(wg / step[..., None]), -7, 7)
+        return ((q * step[..., None] - wg) ** 2).sum(axis=2)
+
+    e_best = err(st)
+    for i in range(n):
+        ci = c[..., i]
+        ok = ci >= 1e-10
+        e_i = err(np.where(ok, ci, 1.0))
+        assert (e_best[ok] <= e_i[ok] * (1 + 1e-5) + 1e-30).all(), i
+    assert (e_best <= err(a.max(axis=2) / 7.0) * (1 + 1e-5)).all()
+
+
+# ---------------------------------------------------------------------------
 # bf16 rounding of the oracle against the library routine (torch)
 # ---------------------------------------------------------------------------
 def check_bf16_rounding_vs_torch():
@@ -584,4 +716,7 @@ ALL_CHECKS = [
     check_bf16_rounding_vs_torch, check_max_rel_err,
     check_sym_worked_example, check_sym_special_groups, check_sym_brute_force,
     check_sym_exact_scaled_matmul, check_sym_invariants,
+    check_percentile_100_is_minmax, check_percentile_vs_numpy, check_percentile_exact_midpoint,
+    check_calibrators_brute_force, check_mse_exact_grid, check_mse_first_minimum_and_clamp,
+    check_mse_skipped_candidates, check_mse_is_least_error,
 ]

@@ -200,6 +200,84 @@ def _sym_zero_point_7(w, kind, g, sz):
     return p, s, np.full(z.shape, 7, z.dtype)
 
 
+def _pct_nearest_rank(w32, g, p):
+    a = np.sort(np.abs(O.split_groups(w32, g)), axis=2)
+    i = int(round((g - 1) * p / 100.0))
+    return a[..., i].astype(F32)
+
+
+def _pct_signed(w32, g, p):
+    a = np.sort(O.split_groups(w32, g), axis=2)
+    i0, i1, f = O.percentile_position(g, p)
+    return (a[..., i0] + f * (a[..., i1] - a[..., i0])).astype(F32)
+
+
+def _pct_position_from_g(g, p):
+    h = g * (p / 100.0)
+    i0 = min(int(np.floor(h)), g - 1)
+    return i0, min(i0 + 1, g - 1), F32(h - np.floor(h))
+
+
+def _mse_last_minimum(w32, g, n):
+    wg = O.split_groups(w32, g)
+    a = np.abs(wg)
+    c = O.mse_candidates(a.min(axis=2), a.max(axis=2), n)
+    valid = c >= O.MSE_SKIP_BELOW
+    with np.errstate(all="ignore"):
+        r = (F32(1.0) / c).astype(F32)
+        E = np.zeros(c.shape, F32)
+        for k in range(g):
+            wk = wg[..., k][..., None]
+            q = np.clip(np.rint(wk * r), -7, 7).astype(F32)
+            e = (q * c - wk).astype(F32)
+            E = (E + e * e).astype(F32)
+    E = np.where(valid, E, np.inf)
+    best = E.shape[2] - 1 - np.argmin(E[..., ::-1], axis=2)
+    step = np.take_along_axis(c, best[..., None], 2)[..., 0]
+    return np.where(valid.any(axis=2), step, O.MSE_NONE).astype(F32)
+
+
+def _mse_clamp_8(w32, g, n):
+    wg = O.split_groups(w32, g)
+    a = np.abs(wg)
+    c = O.mse_candidates(a.min(axis=2), a.max(axis=2), n)
+    valid = c >= O.MSE_SKIP_BELOW
+    with np.errstate(all="ignore"):
+        r = (F32(1.0) / c).astype(F32)
+        E = np.zeros(c.shape, F32)
+        for k in range(g):
+            wk = wg[..., k][..., None]
+            q = np.clip(np.rint(wk * r), -8, 7).astype(F32)
+            e = (q * c - wk).astype(F32)
+            E = (E + e * e).astype(F32)
+    E = np.where(valid, E, np.inf)
+    best = np.argmin(E, axis=2)
+    step = np.take_along_axis(c, best[..., None], 2)[..., 0]
+    return np.where(valid.any(axis=2), step, O.MSE_NONE).astype(F32)
+
+
+def _mse_candidates_from_zero(lo, hi, n):
+    return _orig["mse_candidates"](np.zeros_like(lo), hi, n)
+
+
+def _mse_candidates_n_steps(lo, hi, n):
+    d = ((hi.astype(F32) - lo.astype(F32)) / F32(n)).astype(F32)
+    i = np.arange(n, dtype=F32)
+    return (lo.astype(F32)[..., None] + i * d[..., None]).astype(F32)
+
+
+def _mse_no_none_default(w32, g, n):
+    st = _orig["calib_mse_step"](w32, g, n)
+    return np.where(st == O.MSE_NONE, F32(0.0), st).astype(F32)
+
+
+def _cal_scale_over_8(w, kind, g, sz, p):
+    w32 = O.as_f32(w, kind)
+    s_st = O.store_scale((O.calib_percentile_range(w32, g, p) / F32(8.0)).astype(F32), sz)
+    q = O.quantize_codes_sym(w32, s_st, g)
+    return O.pack_nibbles(q), s_st, np.full(s_st.shape, 8, O.SZ_DTYPES[sz])
+
+
 _uq_sz, _uq_codes = _codes_with_unrounded_scale_factory()
 
 MUTATIONS = {
@@ -228,6 +306,15 @@ MUTATIONS = {
     "sym_round_half_away": {"quantize_codes_sym": _sym_round_half_away},
     "sym_quantize_with_unrounded_scale": {"quantize_pack_int4_sym": _sym_quantize_with_unrounded_scale},
     "sym_zero_point_7": {"quantize_pack_int4_sym": _sym_zero_point_7},
+    "percentile_nearest_rank": {"calib_percentile_range": _pct_nearest_rank},
+    "percentile_of_signed_values": {"calib_percentile_range": _pct_signed},
+    "percentile_position_g_not_g_minus_1": {"percentile_position": _pct_position_from_g},
+    "percentile_scale_over_8": {"quantize_pack_int4_sym_percentile": _cal_scale_over_8},
+    "mse_last_minimum": {"calib_mse_step": _mse_last_minimum},
+    "mse_search_clamps_at_minus_8": {"calib_mse_step": _mse_clamp_8},
+    "mse_candidates_from_zero": {"mse_candidates": _mse_candidates_from_zero},
+    "mse_candidates_spacing_over_n": {"mse_candidates": _mse_candidates_n_steps},
+    "mse_no_default_step": {"calib_mse_step": _mse_no_none_default},
 }
 
 
