@@ -36,6 +36,10 @@ METRIC = "int4 dequant-matmul GB/s (% of HBM peak) at M=1; TFLOP/s at M=2048"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 INT8_PEAK_TOPS = 5000.0
+# fp32 vector ALU instruction rate: the 157.3 TFLOP/s fp32-vector peak counts
+# an FMA as two flops, so 78.6 T fp32 lane-instructions per second (256 CUs x
+# 4 SIMDs x 32 fp32 lanes per cycle x 2.4 GHz)
+VALU_PEAK_TOPS = 157.3 / 2
 
 
 # ---------------------------------------------------------------------------
@@ -269,6 +273,21 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
         qsec = time_region(lambda i: w4.quantize_pack_int4_sym(wt, g, torch.float16, out=qo), reps)
         out.setdefault("quantize_pack_sym", {})[name] = {
             "us": round(qsec * 1e6, 2), "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}
+        if name == "Wb":
+            # range-clipping calibrators: the percentile (rank counting, g^2
+            # compares per group) and the MSE search (1000 candidates, 7 fp32
+            # VALU operations per candidate and weight)
+            qsec = time_region(lambda i: w4.quantize_pack_int4_sym_percentile(wt, g, 99.9, torch.float16,
+                                                                             out=qo), 5)
+            cal = {"percentile_99.9": {"us": round(qsec * 1e6, 1),
+                                       "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}}
+            ncand = 1000
+            qsec = time_region(lambda i: w4.quantize_pack_int4_sym_mse(wt, g, ncand, torch.float16, out=qo), 3)
+            tops = 7 * n * k * ncand / qsec / 1e12
+            cal["mse_1000"] = {"us": round(qsec * 1e6, 1), "valu_TOP/s": round(tops, 2),
+                               "frac_valu_peak": round(tops / VALU_PEAK_TOPS, 4)}
+            out["calibrate_sym_Wb"] = cal
+            log(f"calibrators: {json.dumps(cal)}")
         del qo
         if name == "Wb":
             dq = torch.empty((n, k), dtype=torch.bfloat16, device=dev)

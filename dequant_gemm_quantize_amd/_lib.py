@@ -26,6 +26,9 @@ _VP, _I, _I64, _I32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_in
 SIGNATURES = [
     ("quantize_pack_int4", _I, [_VP, _I, _I64, _I64, _I32, _VP, _VP, _VP, _I, _VP]),
     ("quantize_pack_int4_sym", _I, [_VP, _I, _I64, _I64, _I32, _VP, _VP, _VP, _I, _VP]),
+    ("quantize_pack_int4_sym_percentile", _I,
+     [_VP, _I, _I64, _I64, _I32, ctypes.c_double, _VP, _VP, _VP, _I, _VP]),
+    ("quantize_pack_int4_sym_mse", _I, [_VP, _I, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _I, _VP]),
     ("dequant_int4", _I, [_VP, _VP, _VP, _I, _I64, _I64, _I32, _VP, _I, _VP]),
     ("quantize_act_int8", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP]),
     ("w4a16_matmul", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
@@ -112,6 +115,24 @@ def quantize_pack_int4_sym(w: torch.Tensor, group_size: int, sz_dtype: torch.dty
                            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """Symmetric variant: same arguments and outputs; every zero-point is 8."""
     return _quantize_pack(load().quantize_pack_int4_sym, w, group_size, sz_dtype, out)
+
+
+def quantize_pack_int4_sym_percentile(w: torch.Tensor, group_size: int, percentile: float = 99.9,
+                                      sz_dtype: torch.dtype = torch.float16,
+                                      out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Symmetric format, scale = (percentile of |w| per group) / 7."""
+    fn = load().quantize_pack_int4_sym_percentile
+    return _quantize_pack(lambda w_, d, n, k, g, *rest: fn(w_, d, n, k, g, float(percentile), *rest),
+                          w, group_size, sz_dtype, out)
+
+
+def quantize_pack_int4_sym_mse(w: torch.Tensor, group_size: int, candidates: int = 1000,
+                               sz_dtype: torch.dtype = torch.float16,
+                               out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Symmetric format, step chosen per group by the MSE search over `candidates` steps."""
+    fn = load().quantize_pack_int4_sym_mse
+    return _quantize_pack(lambda w_, d, n, k, g, *rest: fn(w_, d, n, k, g, int(candidates), *rest),
+                          w, group_size, sz_dtype, out)
 
 
 def _quantize_pack(fn, w, group_size, sz_dtype, out):

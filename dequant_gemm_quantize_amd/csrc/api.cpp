@@ -125,6 +125,45 @@ int quantize_pack_int4_sym(const void* w, int w_dtype, int64_t n, int64_t k, int
                               scales, zeros, sz_dtype, stream);
 }
 
+static int quantize_pack_cal(const char* fn, int mode, double param, const void* w, int w_dtype,
+                             int64_t n, int64_t k, int32_t group_size, uint8_t* packed, void* scales,
+                             void* zeros, int sz_dtype, hipStream_t stream) {
+  W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
+  if (!w4::quantize_cal_fits(group_size))
+    return fail(W4_EINVAL, "%s: group_size = %d is above the calibrators' limit of 1024", fn,
+                (int)group_size);
+  if (w_dtype != W4_F32 && w_dtype != W4_BF16)
+    return fail(W4_EINVAL, "%s: w dtype %d must be W4_F32 or W4_BF16", fn, w_dtype);
+  if (n == 0) return ok();
+  W4_TRY(check_ptr(fn, "w", w));
+  W4_TRY(check_ptr(fn, "packed", packed));
+  W4_TRY(check_ptr(fn, "scales", scales));
+  W4_TRY(check_ptr(fn, "zeros", zeros));
+  return hip_status(w4::launch_quantize_pack_cal(w, w_dtype, n, k, group_size, mode, param, packed,
+                                                 scales, zeros, sz_dtype, stream),
+                    fn);
+}
+
+int quantize_pack_int4_sym_percentile(const void* w, int w_dtype, int64_t n, int64_t k,
+                                      int32_t group_size, double percentile, uint8_t* packed,
+                                      void* scales, void* zeros, int sz_dtype, hipStream_t stream) {
+  static const char* fn = "quantize_pack_int4_sym_percentile";
+  if (!(percentile > 0.0 && percentile <= 100.0))
+    return fail(W4_EINVAL, "%s: percentile %g must lie in (0, 100]", fn, percentile);
+  return quantize_pack_cal(fn, 0, percentile, w, w_dtype, n, k, group_size, packed, scales, zeros,
+                           sz_dtype, stream);
+}
+
+int quantize_pack_int4_sym_mse(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                               int32_t candidates, uint8_t* packed, void* scales, void* zeros,
+                               int sz_dtype, hipStream_t stream) {
+  static const char* fn = "quantize_pack_int4_sym_mse";
+  if (candidates < 2 || candidates > 65536)
+    return fail(W4_EINVAL, "%s: candidates = %d must lie in [2, 65536]", fn, (int)candidates);
+  return quantize_pack_cal(fn, 1, (double)candidates, w, w_dtype, n, k, group_size, packed, scales,
+                           zeros, sz_dtype, stream);
+}
+
 int dequant_int4(const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
                  int64_t n, int64_t k, int32_t group_size, void* w_out, int out_dtype,
                  hipStream_t stream) {

@@ -4,6 +4,8 @@
 // the definition itself -- IEEE division (correctly rounded), rint with ties
 // to even, round-to-nearest-even narrowing -- so the outputs are bit-exact.
 // Contraction into FMA is switched off in this file: nothing here may fuse.
+#include <cmath>
+
 #include "w4_common.h"
 #include "w4_internal.h"
 
@@ -356,6 +358,154 @@ hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k
                                 bool symmetric, hipStream_t st) {
   if (symmetric) return launch_qp_sz<true>(w, w_dtype, n, k, g, packed, scales, zeros, sz_dtype, st);
   return launch_qp_sz<false>(w, w_dtype, n, k, g, packed, scales, zeros, sz_dtype, st);
+}
+
+// ---------------------------------------------------------------------------
+// Calibrated symmetric quantize + pack ("Building a From-Scratch Group-Wise
+// INT4 Quantization Layer for LLaMA Weights", Step 4): the group's scale
+// comes from a range-clipping calibrator, the codes are the symmetric ones
+// above with the stored scale.  One wave per group (g <= 1024); the group's
+// values sit in the wave's own LDS region, which needs no barrier (LDS
+// operations of a wave complete in order).
+//   MODE_PCT: range = the p-th percentile of |w|, linear between the order
+//     statistics i0 and i1 = min(i0 + 1, g - 1) with weight f (host values
+//     from h = (g - 1) p / 100); scale = range / 7.  The order statistics are
+//     found by rank counting: rank(e) = #{k : a_k < a_e} + #{k < e : a_k == a_e}.
+//   MODE_MSE: candidate steps c_i = lo + i d, d = (hi - lo) / (n - 1), from
+//     min|w| to max|w|; c < 1e-10 is skipped; codes clamp(rint(w * (1/c)),
+//     -7, 7); error sum over the group in column order, fp32; the first
+//     least sum wins (a 64-bit key of the sum's bits and the index; sums are
+//     non-negative, so their bits order like their values); 1e-8 if no
+//     candidate qualifies.  Lane l evaluates candidates l, l + 64, ...
+// ---------------------------------------------------------------------------
+constexpr int kCalMaxG = 1024;
+enum { MODE_PCT = 0, MODE_MSE = 1 };
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const uint64_t u = __shfl_xor(v, o, kWave);
+    v = u < v ? u : v;
+  }
+  return v;
+}
+
+template <typename TIn, typename TS, int MODE>
+__global__ __launch_bounds__(256) void k_quantize_pack_cal(const void* __restrict__ w, int64_t ngroups,
+                                                          int cpg, int i0, int i1, float frac, int ncand,
+                                                          uint32_t* __restrict__ packed,
+                                                          TS* __restrict__ scales,
+                                                          TS* __restrict__ zeros) {
+  extern __shared__ __attribute__((aligned(16))) float cal_lds[];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t grp = (int64_t)blockIdx.x * 4 + wv;
+  if (grp >= ngroups) return;  // uniform per wave; no workgroup barrier follows
+  const int g = 8 * cpg;
+  float* gl = cal_lds + wv * g;
+  const int64_t c0 = grp * cpg;
+  for (int c = lane; c < cpg; c += kWave) {
+    float v[8];
+    Load8<TIn>::run(w, c0 + c, v);
+    ((f32x4*)gl)[2 * c] = f32x4{v[0], v[1], v[2], v[3]};
+    ((f32x4*)gl)[2 * c + 1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  float s32;
+  if constexpr (MODE == MODE_PCT) {
+    float v0 = -1.0f, v1 = -1.0f;
+    for (int e = lane; e < g; e += kWave) {
+      const float ae = fabsf(gl[e]);
+      int rank = 0;
+      for (int kk = 0; kk < g; ++kk) {
+        const float ak = fabsf(gl[kk]);
+        rank += (ak < ae) || (ak == ae && kk < e);
+      }
+      if (rank == i0) v0 = ae;
+      if (rank == i1) v1 = ae;
+    }
+    v0 = group_max<kWave>(v0);
+    v1 = group_max<kWave>(v1);
+    s32 = (v0 + frac * (v1 - v0)) / 7.0f;
+  } else {
+    float lo = __builtin_huge_valf(), hi = 0.0f;
+    for (int e = lane; e < g; e += kWave) {
+      const float a = fabsf(gl[e]);
+      lo = fminf(lo, a);
+      hi = fmaxf(hi, a);
+    }
+    lo = group_min<kWave>(lo);
+    hi = group_max<kWave>(hi);
+    const float d = (hi - lo) / (float)(ncand - 1);
+    uint64_t best = ~0ull;
+    for (int i = lane; i < ncand; i += kWave) {
+      const float c = lo + (float)i * d;
+      if (!(c >= 1e-10f)) continue;
+      const float r = 1.0f / c;
+      float err = 0.0f;
+      for (int kk = 0; kk < g; kk += 4) {
+        const f32x4 w4 = ((const f32x4*)gl)[kk >> 2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float q = fminf(fmaxf(rintf(w4[j] * r), -7.0f), 7.0f);
+          const float e = q * c - w4[j];
+          err = err + e * e;
+        }
+      }
+      const uint64_t key = ((uint64_t)__float_as_uint(err) << 32) | (uint32_t)i;
+      best = key < best ? key : best;
+    }
+    best = wave_min_u64(best);
+    s32 = best == ~0ull ? 1e-8f : lo + (float)(uint32_t)best * d;
+  }
+  TS st = (TS)s32;
+  if (st == (TS)0.0f) st = (TS)1.0f;
+  const float s = (float)st;
+  const float r = __builtin_amdgcn_rcpf(s);
+  for (int c = lane; c < cpg; c += kWave) {
+    const f32x4 a = ((const f32x4*)gl)[2 * c], b = ((const f32x4*)gl)[2 * c + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    packed[c0 + c] = pack8_sym(v, s, r);
+  }
+  if (lane == 0) {
+    scales[grp] = st;
+    zeros[grp] = (TS)8.0f;
+  }
+}
+
+template <typename TIn, typename TS>
+static hipError_t launch_cal_t(const void* w, int64_t n, int64_t k, int g, int mode, double param,
+                               uint8_t* packed, void* scales, void* zeros, hipStream_t st) {
+  const int64_t ngroups = n * (k / g);
+  const dim3 grid((unsigned)((ngroups + 3) / 4));
+  const size_t lds = (size_t)4 * g * sizeof(float);
+  uint32_t* pk = (uint32_t*)packed;
+  if (mode == MODE_PCT) {
+    const double h = (g - 1) * (param / 100.0);
+    const int i0 = (int)std::floor(h);
+    const int i1 = i0 + 1 < g ? i0 + 1 : g - 1;
+    const float f = (float)(h - i0);
+    k_quantize_pack_cal<TIn, TS, MODE_PCT><<<grid, 256, lds, st>>>(w, ngroups, g / 8, i0, i1, f, 0, pk,
+                                                                     (TS*)scales, (TS*)zeros);
+  } else {
+    k_quantize_pack_cal<TIn, TS, MODE_MSE><<<grid, 256, lds, st>>>(w, ngroups, g / 8, 0, 0, 0.0f,
+                                                                     (int)param, pk, (TS*)scales,
+                                                                     (TS*)zeros);
+  }
+  return hipGetLastError();
+}
+
+bool quantize_cal_fits(int g) { return g <= kCalMaxG; }
+
+hipError_t launch_quantize_pack_cal(const void* w, int w_dtype, int64_t n, int64_t k, int g, int mode,
+                                    double param, uint8_t* packed, void* scales, void* zeros,
+                                    int sz_dtype, hipStream_t st) {
+  const bool in_bf16 = (w_dtype == W4_BF16);
+  const bool s_f16 = (sz_dtype == W4_F16);
+  if (in_bf16 && s_f16) return launch_cal_t<__bf16, _Float16>(w, n, k, g, mode, param, packed, scales, zeros, st);
+  if (in_bf16) return launch_cal_t<__bf16, float>(w, n, k, g, mode, param, packed, scales, zeros, st);
+  if (s_f16) return launch_cal_t<float, _Float16>(w, n, k, g, mode, param, packed, scales, zeros, st);
+  return launch_cal_t<float, float>(w, n, k, g, mode, param, packed, scales, zeros, st);
 }
 
 // ---------------------------------------------------------------------------

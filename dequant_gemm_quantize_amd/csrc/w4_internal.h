@@ -30,6 +30,12 @@ hipError_t once_per_device(std::atomic<uint64_t>& done, F set) {
 hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k, int g,
                                 uint8_t* packed, void* scales, void* zeros, int sz_dtype,
                                 bool symmetric, hipStream_t st);
+// Calibrated symmetric quantize + pack: mode 0 = percentile (param = p in
+// (0, 100]), mode 1 = MSE search (param = candidates, >= 2); g <= 1024.
+bool quantize_cal_fits(int g);
+hipError_t launch_quantize_pack_cal(const void* w, int w_dtype, int64_t n, int64_t k, int g, int mode,
+                                    double param, uint8_t* packed, void* scales, void* zeros,
+                                    int sz_dtype, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* packed, const void* scales, const void* zeros,
                           int sz_dtype, int64_t n, int64_t k, int g, void* out, int out_dtype,
                           hipStream_t st);

@@ -103,6 +103,34 @@ int quantize_pack_int4_sym(const void* w, int w_dtype, int64_t n, int64_t k, int
                            hipStream_t stream);
 
 /*
+ * quantize_pack_int4_sym_percentile / quantize_pack_int4_sym_mse -- the
+ * symmetric format with a calibrated scale per group ([P3] Step 4's
+ * range-clipping calibrators); the codes are then those of
+ * quantize_pack_int4_sym with the stored scale, zeros[] is written with 8.
+ *
+ * percentile: range = the `percentile`-th percentile of |G| (0 < p <= 100),
+ *   linear between order statistics: with a = sorted |G|,
+ *   h = (g - 1) p / 100 (double), i0 = floor(h), i1 = min(i0 + 1, g - 1),
+ *   f = (float)(h - i0): range = a[i0] + f (a[i1] - a[i0]) in float32;
+ *   scale = range / 7 (p = 100 gives quantize_pack_int4_sym exactly).
+ * mse: `candidates` = n (2 .. 65536) steps c_i = lo + i d, d = (hi - lo) /
+ *   (n - 1), lo = min|G|, hi = max|G| (float32); a step below 1e-10 is
+ *   skipped; for the others q = clamp(rint(w * (1/c)), -7, 7) and
+ *   E(c) = sum over G, in column order, of (q c - w)^2 in float32; the step
+ *   is the first c with the least E, or 1e-8 when none qualifies.  The cost
+ *   is about 7 g n float32 operations per group.
+ * Both: group_size <= 1024 (W4_EINVAL above); otherwise arguments, layout,
+ * limits and errors as quantize_pack_int4.  The outputs are bit-for-bit
+ * those of the definitions above.
+ */
+int quantize_pack_int4_sym_percentile(const void* w, int w_dtype, int64_t n, int64_t k,
+                                      int32_t group_size, double percentile, uint8_t* packed,
+                                      void* scales, void* zeros, int sz_dtype, hipStream_t stream);
+int quantize_pack_int4_sym_mse(const void* w, int w_dtype, int64_t n, int64_t k, int32_t group_size,
+                               int32_t candidates, uint8_t* packed, void* scales, void* zeros,
+                               int sz_dtype, hipStream_t stream);
+
+/*
  * dequant_int4 -- w_out[n, k] = (q[n, k] - zp[n, k/g]) * scale[n, k/g]
  * ([P5] Step 4), computed as one float32 product of the exact integer
  * difference and the scale, then rounded (nearest-even) to out_dtype

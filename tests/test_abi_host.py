@@ -88,9 +88,31 @@ def test_quantize_pack_rejects(lib, name, args, msg):
     assert _err(lib).startswith(name + ":"), _err(lib)
 
 
+@pytest.mark.parametrize("pct,g,msg", [(0.0, 128, "percentile 0 must lie in (0, 100]"),
+                                       (100.5, 128, "must lie in (0, 100]"),
+                                       (float("nan"), 128, "must lie in (0, 100]"),
+                                       (99.9, 2048, "above the calibrators' limit of 1024"),
+                                       (99.9, 48, "multiple of 32")])
+def test_percentile_rejects(lib, pct, g, msg):
+    assert lib.quantize_pack_int4_sym_percentile(A, 2, 4, 4096, g, pct, A, A, A, 1, None) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+@pytest.mark.parametrize("cand,g,msg", [(1, 128, "candidates = 1 must lie in [2, 65536]"),
+                                        (65537, 128, "must lie in [2, 65536]"),
+                                        (1000, 2048, "limit of 1024"),
+                                        (1000, 128, "zeros is NULL")])
+def test_mse_rejects(lib, cand, g, msg):
+    zeros = None if "zeros" in msg else A
+    assert lib.quantize_pack_int4_sym_mse(A, 2, 4, 4096, g, cand, A, A, zeros, 1, None) == -1
+    assert msg in _err(lib), _err(lib)
+
+
 def test_empty_calls_are_noops(lib):
     assert lib.quantize_pack_int4(None, 2, 0, 128, 32, None, None, None, 1, None) == 0
     assert lib.quantize_pack_int4_sym(None, 2, 0, 128, 32, None, None, None, 1, None) == 0
+    assert lib.quantize_pack_int4_sym_percentile(None, 2, 0, 128, 32, 99.9, None, None, None, 1, None) == 0
+    assert lib.quantize_pack_int4_sym_mse(None, 2, 0, 128, 32, 1000, None, None, None, 1, None) == 0
     assert lib.dequant_int4(None, None, None, 1, 0, 128, 32, None, 2, None) == 0
     assert lib.quantize_act_int8(None, 2, 0, 128, None, None, None) == 0
     assert lib.w4a16_matmul(None, 2, 0, 128, None, None, None, 1, 64, 128, None, 2, None) == 0

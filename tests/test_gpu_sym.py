@@ -212,3 +212,100 @@ def test_sym_exact_integers(w4, m, n, k):
     xq, xs = w4.quantize_act_int8(to_dev(WL.bf16_round_bits(x8.astype(np.float32)), "bf16"))
     y8 = w4.w4a8_matmul(xq, xs, p, s, z, g)
     assert np.array_equal(to_host(y8), O.to_bf16((x8 @ wi.T).astype(np.float32)))
+
+
+# ---------------------------------------------------------------------------
+# Range-clipping calibrators: bit-exact against the oracle
+# ---------------------------------------------------------------------------
+def gpu_quantize_cal(w4, w_np, kind, g, sz, method, param):
+    n, k = w_np.shape
+    cp = Canary((n, k // 2), torch.uint8)
+    cs = Canary((n, k // g), TORCH_SZ[sz])
+    cz = Canary((n, k // g), TORCH_SZ[sz])
+    fn = w4.quantize_pack_int4_sym_percentile if method == "percentile" else w4.quantize_pack_int4_sym_mse
+    fn(to_dev(w_np, kind), g, param, TORCH_SZ[sz], out=(cp.tensor, cs.tensor, cz.tensor))
+    for c in (cp, cs, cz):
+        c.check()
+    return to_host(cp.tensor), to_host(cs.tensor), to_host(cz.tensor)
+
+
+def oracle_cal(w_np, kind, g, sz, method, param):
+    if method == "percentile":
+        return O.quantize_pack_int4_sym_percentile(w_np, kind, g, sz, param)
+    return O.quantize_pack_int4_sym_mse(w_np, kind, g, sz, param)
+
+
+@pytest.mark.parametrize("n,k,g", [(37, 640, 32), (5, 640, 128), (3, 1024, 256), (2, 1536, 512),
+                                   (7, 384, 96), (2, 2048, 1024), (129, 256, 128)])
+@pytest.mark.parametrize("p", [99.9, 50.0, 100.0, 0.001])
+@pytest.mark.parametrize("kind,sz", [("bf16", "f16"), ("f32", "f32"), ("f32", "f16")])
+def test_percentile_small(w4, n, k, g, p, kind, sz):
+    rng = np.random.default_rng(3000 + n + k + g)
+    w = rng.normal(0, 0.02, (n, k)).astype(np.float32)
+    w.reshape(-1)[rng.choice(n * k, max(1, n * k // 300), replace=False)] = -0.4
+    if n > 2:
+        w[2, :g] = 0.0                      # all-zero group
+        w[1, :g] = np.float32(0.125)        # constant group: ties everywhere
+    src = WL.bf16_round_bits(w) if kind == "bf16" else w
+    got = gpu_quantize_cal(w4, src, kind, g, sz, "percentile", p)
+    assert_quant_equal(got, oracle_cal(src, kind, g, sz, "percentile", p))
+
+
+@pytest.mark.parametrize("n,k,g,cand", [(9, 640, 128, 1000), (37, 256, 32, 200), (3, 1024, 256, 300),
+                                        (2, 2048, 1024, 50), (5, 384, 96, 64), (4, 256, 128, 2)])
+@pytest.mark.parametrize("kind,sz", [("bf16", "f16"), ("f32", "f32")])
+def test_mse_small(w4, n, k, g, cand, kind, sz):
+    rng = np.random.default_rng(4000 + n + k + g)
+    w = rng.normal(0, 0.02, (n, k)).astype(np.float32)
+    w.reshape(-1)[rng.choice(n * k, max(1, n * k // 300), replace=False)] = 0.4
+    if n > 2:
+        w[2, :g] = 0.0
+    src = WL.bf16_round_bits(w) if kind == "bf16" else w
+    got = gpu_quantize_cal(w4, src, kind, g, sz, "mse", cand)
+    assert_quant_equal(got, oracle_cal(src, kind, g, sz, "mse", cand))
+
+
+def test_mse_pinned_groups(w4):
+    """The groups that pin the search: an exact grid (n = 8), a three-way
+    tie (n = 11), the -7 clamp (n = 9), skipped candidates (n = 10)."""
+    g = 32
+    u = 2.0 ** -7
+    j = np.array(list(range(-7, 8)) + [3, -3, 0, 7, -7, 1, 2, -1, -2, 5, -5, 4, -4, 6, -6, 0, 2])
+    rows = {8: (j * u).astype(np.float32),
+            11: np.array([0.0] * 16 + [5.0] * 16, np.float32)[np.random.default_rng(2).permutation(32)],
+            9: np.array([-8.0] * 16 + [7.0] + [0.0] * 15, np.float32),
+            10: np.where(np.arange(32) < 4, np.float32(5e-11), np.float32(0.0)).astype(np.float32)}
+    want_step = {8: u, 11: 1.0, 9: 2.0, 10: 1.0}
+    for cand, row in rows.items():
+        w = np.stack([row, -row[::-1]])
+        for sz in ("f16", "f32"):
+            got = gpu_quantize_cal(w4, w, "f32", g, sz, "mse", cand)
+            assert_quant_equal(got, oracle_cal(w, "f32", g, sz, "mse", cand))
+            if sz == "f16":
+                assert float(got[1][0, 0]) == want_step[cand], (cand, float(got[1][0, 0]))
+
+
+def test_calibrators_workload(w4):
+    """The 4096 x 4096 weight (bf16, g = 128, fp16 scales): percentile on
+    every row, MSE search (1000 candidates) on 64 sampled rows."""
+    t = WL.weight("Wa")
+    got = gpu_quantize_cal(w4, t.data, t.kind, 128, "f16", "percentile", 99.9)
+    assert_quant_equal(got, oracle_cal(t.data, t.kind, 128, "f16", "percentile", 99.9))
+    got = gpu_quantize_cal(w4, t.data, t.kind, 128, "f16", "mse", 1000)
+    rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(6).choice(4096, 62, replace=False)]))
+    assert_quant_equal(got, oracle_cal(t.data[rows], t.kind, 128, "f16", "mse", 1000), rows=rows)
+
+
+@pytest.mark.parametrize("m", [1, 16, 200])
+def test_calibrated_weights_matmul(w4, m):
+    """MSE-calibrated weights through the product (decode and GEMM paths)."""
+    n, k, g = 300, 1024, 128
+    w = np.random.default_rng(51).normal(0, 0.02, (n, k)).astype(np.float32)
+    wb = WL.bf16_round_bits(w)
+    dev = w4.quantize_pack_int4_sym_mse(to_dev(wb, "bf16"), g, 500, torch.float16)
+    P, S, Z = O.quantize_pack_int4_sym_mse(wb, "bf16", g, "f16", 500)
+    assert_quant_equal(tuple(to_host(t) for t in dev), (P, S, Z))
+    x = WL.bf16_round_bits(np.random.default_rng(m).normal(0, 1, (m, k)).astype(np.float32))
+    y = w4.w4a16_matmul(to_dev(x, "bf16"), *dev, g)
+    ref = O.matmul_w4a16_f64(O.widen_bf16(x), P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL["bf16"]
