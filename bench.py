@@ -366,7 +366,63 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
     y = torch.empty((1, 256), dtype=torch.float32, device=dev)
     sec = time_region(lambda i: w4.w4a16_matmul(x, p, s, z, 32, out=y), reps)
     out["single_layer_fp32_256"] = {"us": round(sec * 1e6, 2)}
+    del p, s, z, w1
+
+    out["llama7b_decode_32_layers"] = llama_decode(w4, torch, dev, time_region, log, g)
     return out
+
+
+# One Llama-7B decoder layer's linears with the usual fusions: q, k and v as
+# one [12288, 4096] product, gate and up as one [22016, 4096].
+LLAMA7B_LINEARS = (("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096), ("down", 4096, 11008))
+
+
+def llama_decode(w4, torch, dev, time_region, log, g, layers=32, tokens=8):
+    """Decode throughput over all 32 layers' linears of a Llama-7B-shaped
+    model at one token: 128 products per token, each consuming the previous
+    one's output (a slice of it stands in for attention and the MLP
+    activation, which are not part of this path).  Weights are synthetic
+    N(0, 0.02) bf16 drawn on the GPU, quantized by quantize_pack_int4
+    (group 128, fp16 scales); every token's launches are captured in a HIP
+    graph, so the figure is GPU time."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    model = []
+    nbytes = 0
+    for _ in range(layers):
+        per = {}
+        for name, n, k in LLAMA7B_LINEARS:
+            w = (torch.randn((n, k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            per[name] = w4.quantize_pack_int4(w, g, torch.float16)
+            nbytes += w4a16_bytes(1, n, k, g)
+            del w
+        model.append(per)
+    x = (torch.randn((1, 4096), generator=gen, device=dev)).to(torch.bfloat16)
+    qkv = torch.empty((1, 12288), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((1, 4096), dtype=torch.bfloat16, device=dev)
+    gu = torch.empty((1, 22016), dtype=torch.bfloat16, device=dev)
+    y = [torch.empty((1, 4096), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+
+    def token(i):
+        cur = x
+        for li, per in enumerate(model):
+            w4.w4a16_matmul(cur, *per["qkv"], g, out=qkv)
+            w4.w4a16_matmul(qkv[:, :4096], *per["o"], g, out=o)
+            w4.w4a16_matmul(o, *per["gate_up"], g, out=gu)
+            w4.w4a16_matmul(gu[:, :11008], *per["down"], g, out=y[li % 2])
+            cur = y[li % 2]
+
+    for i in range(2):
+        token(i)
+    sec = time_region(token, tokens, per_graph=1)
+    res = {"ms_per_token": round(sec * 1e3, 4), "tokens_per_s": round(1.0 / sec, 1),
+           "weight_bytes_per_token": nbytes, "GB/s": round(nbytes / sec / 1e9, 1),
+           "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "launches_per_token": 4 * layers,
+           "us_per_launch": round(sec * 1e6 / (4 * layers), 3)}
+    log(f"llama-7b decode, 32 layers: {json.dumps(res)}")
+    del model
+    torch.cuda.empty_cache()
+    return res
 
 
 def kernel_only(args, w4, WL, torch, dev, to_dev, log):

@@ -9,3 +9,4 @@ from ._lib import (  # noqa: F401
     w4a16_matmul, w4a8_matmul, version, LIB_PATH,
     W4_F32, W4_F16, W4_BF16, W4_OK, W4_EINVAL, W4_EUNSUPPORTED, W4_EHIP,
 )
+from .layer import QuantizedLinear, replace_linears  # noqa: F401

@@ -185,3 +185,20 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("no oracle", ""), f
+
+
+def test_layer_arguments_without_gpu():
+    """QuantizedLinear validates its shape arguments and refuses a biased
+    Linear or an unknown mode before any GPU work."""
+    import torch
+    import dequant_gemm_quantize_amd as w4
+    with pytest.raises(ValueError, match="multiple of group_size"):
+        w4.QuantizedLinear(200, 64, group_size=128)
+    with pytest.raises(ValueError, match="has one"):
+        w4.QuantizedLinear.from_linear(torch.nn.Linear(256, 64, bias=True))
+    with pytest.raises(ValueError, match="mode must be one of"):
+        w4.QuantizedLinear.from_weight(torch.zeros(64, 256), mode="gptq")
+    layer = w4.QuantizedLinear(256, 64, group_size=128)
+    assert tuple(layer.packed.shape) == (64, 128) and tuple(layer.scales.shape) == (64, 2)
+    with pytest.raises(ValueError, match="features"):
+        layer(torch.zeros(2, 128))
