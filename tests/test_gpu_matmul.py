@@ -93,6 +93,8 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           # 65..128 tokens: launches of up to 64 tokens
           (65, 48, 1024, 128, "f16", "bf16"), (100, 70, 11008, 128, "f16", "f32"),
           (128, 33, 2048, 256, "f32", "bf16"),
+          # two row blocks per workgroup (N >= 8192) with a ragged last one
+          (9, 8200, 1024, 128, "f16", "bf16"), (24, 8208, 1536, 256, "f32", "f32"),
           # three tokens at K = 4096: the fast LDS decode kernel
           (3, 70, 4096, 128, "f16", "bf16"),
           # one token, K not a multiple of 2048 (the dot2 kernel's partial
