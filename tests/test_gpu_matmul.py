@@ -263,7 +263,9 @@ W8_GEMM = [(17, 130, 128, 128, "f16"), (257, 1000, 2048, 128, "f16"), (300, 200,
            # up to 16 tokens, groups a multiple of 128, any K: the int8 MFMA GEMV
            # (slices shared by up to 8 waves, partial last slice)
            (1, 50, 28672, 128, "f16"), (7, 33, 1280, 256, "f16"), (12, 40, 11008, 128, "f32"),
-           (2, 17, 8192, 128, "f16"), (16, 64, 128, 128, "f16")]
+           (2, 17, 8192, 128, "f16"), (16, 64, 128, 128, "f16"),
+           # long K with N >= 8192: two row blocks per workgroup, ragged last one
+           (16, 8200, 16384, 128, "f16"), (5, 8208, 16384, 256, "f32")]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz", W8_GEMM)
