@@ -81,13 +81,15 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
   const int nw = blockDim.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * (16 * RB);
-  const int tok = r16 < M ? r16 : M - 1;  // operand rows past M repeat the last token
   const int64_t ng = K / g;
   const int nblk = (int)(K / 128);
   const int nsl = (nblk + kSliceB - 1) / kSliceB;
   constexpr int CPR = 4 * kSliceB;  // 16-byte code chunks per row and slice
-  u32x4* stg = (u32x4*)lds8 + 16 * CPR * w;
-  float* part8 = (float*)(lds8 + (size_t)nw * 256 * CPR);
+  // per wave: 16 tokens x the slice's 512 bytes of activations (8 KB), reused
+  // for the codes' regrouping (4 KB)
+  constexpr int XSLOTS = 16 * 2 * CPR;  // 16-byte slots: 16 tokens x 32 chunks
+  u32x4* stg = (u32x4*)lds8 + XSLOTS * w;
+  float* part8 = (float*)(lds8 + (size_t)nw * 16 * XSLOTS);
 
   // Code loads: 16 consecutive lanes read one row's 256 contiguous bytes of
   // the slice (4 rows per instruction); the slice is then regrouped through
@@ -113,7 +115,18 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
     srow[rb] = (const R*)scales + row * ng;
     zrow[rb] = (const R*)zeros + row * ng;
   }
-  const u32x4* xrow = (const u32x4*)(xq + (int64_t)tok * K) + 2 * q;  // + 8 * block
+  // activation loads: 16 consecutive lanes read 256 contiguous bytes of one
+  // token (token 4u + q, chunks r16 and r16 + 16 of the slice's 512 bytes),
+  // regrouped through LDS into operand order (lane (r, q) of half j of block
+  // i takes token r, chunk 8 i + 2 q + j); token t's chunk c at slot
+  // 32 t + (c ^ t), free of bank conflicts both ways
+  const u32x4* xtok[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int t = 4 * u + q;
+    t = t < M ? t : M - 1;  // tokens past M repeat the last one
+    xtok[u] = (const u32x4*)(xq + (int64_t)t * K);
+  }
 
   f32x4 acc[RB];
 #pragma unroll
@@ -134,11 +147,18 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
           const int cc = c < 4 * nb ? c : 4 * nb - 1;  // chunk of the slice's run
           cr[rb][j][h] = __builtin_nontemporal_load((const u32x4*)(crow[rb][j] + (int64_t)b0 * 64) + cc);
         }
+    u32x4 xr[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int c = r16 + 16 * s2;
+        const int cc = c < 8 * nb ? c : 8 * nb - 1;  // chunk of the slice's run
+        xr[u][s2] = xtok[u][8 * b0 + cc];
+      }
 #pragma unroll
     for (int i = 0; i < kSliceB; ++i) {
       const int b = b0 + (i < nb ? i : nb - 1);  // missing blocks reuse the last
-      xa[i][0] = xrow[8 * b];
-      xa[i][1] = xrow[8 * b + 1];
       const int64_t gi = (int64_t)b * 128 / g;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -146,6 +166,21 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
         zv[rb][i] = zrow[rb][gi];
       }
     }
+    // ---- regroup the activations into operand order ------------------------
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int t = 4 * u + q, c = r16 + 16 * s2;
+        stg[32 * t + (c ^ t)] = xr[u][s2];
+      }
+#pragma unroll
+    for (int i = 0; i < kSliceB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = 8 * i + 2 * q + j;  // the columns of the codes' half j (bw0 / bw1)
+        xa[i][j] = stg[32 * r16 + (c ^ r16)];
+      }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       // ---- regroup the codes: row 4j + q, chunk r16 -> operand order -------
@@ -208,7 +243,7 @@ static void w4a8_mfma_go(const int8_t* xq, const float* xs, int64_t m, int64_t k
   auto go = [&](auto rbc) {
     constexpr int RB = decltype(rbc)::value;
     const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
-    const size_t lds = (size_t)nw * (256 * 4 * kSliceB + RB * 256 * sizeof(float));
+    const size_t lds = (size_t)nw * (16 * 16 * 2 * 4 * kSliceB + RB * 256 * sizeof(float));
     k_w4a8_gemv_mfma<TS, TY, RB><<<grid, 64 * nw, lds, st>>>(xq, xs, (int)m, k, packed, scales, zeros,
                                                              n, g, y);
   };
