@@ -87,7 +87,9 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
   constexpr int CPR = 4 * kSliceB;  // 16-byte code chunks per row and slice
   // per wave: 16 tokens x the slice's 512 bytes of activations (8 KB), reused
   // for the codes' regrouping (4 KB)
-  constexpr int XSLOTS = 16 * 2 * CPR;  // 16-byte slots: 16 tokens x 32 chunks
+  constexpr int XCH = 2 * CPR;          // 16-byte activation chunks per token and slice
+  constexpr int XPL = XCH / 16;         // of them per lane and token group
+  constexpr int XSLOTS = 16 * XCH;      // 16-byte slots: 16 tokens x XCH chunks
   u32x4* stg = (u32x4*)lds8 + XSLOTS * w;
   float* part8 = (float*)(lds8 + (size_t)nw * 16 * XSLOTS);
 
@@ -116,10 +118,10 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
     zrow[rb] = (const R*)zeros + row * ng;
   }
   // activation loads: 16 consecutive lanes read 256 contiguous bytes of one
-  // token (token 4u + q, chunks r16 and r16 + 16 of the slice's 512 bytes),
-  // regrouped through LDS into operand order (lane (r, q) of half j of block
-  // i takes token r, chunk 8 i + 2 q + j); token t's chunk c at slot
-  // 32 t + (c ^ t), free of bank conflicts both ways
+  // token (token 4u + q, chunks r16 + 16 s of the slice's run), regrouped
+  // through LDS into operand order (lane (r, q) of half j of block i takes
+  // token r, chunk 8 i + 2 q + j); token t's chunk c at slot XCH t + (c ^ t),
+  // free of bank conflicts both ways
   const u32x4* xtok[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -147,11 +149,11 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
           const int cc = c < 4 * nb ? c : 4 * nb - 1;  // chunk of the slice's run
           cr[rb][j][h] = __builtin_nontemporal_load((const u32x4*)(crow[rb][j] + (int64_t)b0 * 64) + cc);
         }
-    u32x4 xr[4][2];
+    u32x4 xr[4][XPL];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2 = 0; s2 < XPL; ++s2) {
         const int c = r16 + 16 * s2;
         const int cc = c < 8 * nb ? c : 8 * nb - 1;  // chunk of the slice's run
         xr[u][s2] = xtok[u][8 * b0 + cc];
@@ -170,16 +172,16 @@ __global__ __launch_bounds__(512) void k_w4a8_gemv_mfma(
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2 = 0; s2 < XPL; ++s2) {
         const int t = 4 * u + q, c = r16 + 16 * s2;
-        stg[32 * t + (c ^ t)] = xr[u][s2];
+        stg[XCH * t + (c ^ t)] = xr[u][s2];
       }
 #pragma unroll
     for (int i = 0; i < kSliceB; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c = 8 * i + 2 * q + j;  // the columns of the codes' half j (bw0 / bw1)
-        xa[i][j] = stg[32 * r16 + (c ^ r16)];
+        xa[i][j] = stg[XCH * r16 + (c ^ r16)];
       }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -243,7 +245,7 @@ static void w4a8_mfma_go(const int8_t* xq, const float* xs, int64_t m, int64_t k
   auto go = [&](auto rbc) {
     constexpr int RB = decltype(rbc)::value;
     const dim3 grid((unsigned)((n + 16 * RB - 1) / (16 * RB)));
-    const size_t lds = (size_t)nw * (16 * 16 * 2 * 4 * kSliceB + RB * 256 * sizeof(float));
+    const size_t lds = (size_t)nw * (16 * 16 * 2 * 4 * kSliceB + RB * 256 * sizeof(float));  // 16 XSLOTS bytes
     k_w4a8_gemv_mfma<TS, TY, RB><<<grid, 64 * nw, lds, st>>>(xq, xs, (int)m, k, packed, scales, zeros,
                                                              n, g, y);
   };
