@@ -370,7 +370,8 @@ hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k
 //   MODE_PCT: range = the p-th percentile of |w|, linear between the order
 //     statistics i0 and i1 = min(i0 + 1, g - 1) with weight f (host values
 //     from h = (g - 1) p / 100); scale = range / 7.  The order statistics are
-//     found by rank counting: rank(e) = #{k : a_k < a_e} + #{k < e : a_k == a_e}.
+//     read from a bitonic sort of |w| in LDS (equal values are equal, so the
+//     order of ties does not matter).
 //   MODE_MSE: candidate steps c_i = lo + i d, d = (hi - lo) / (n - 1), from
 //     min|w| to max|w|; c < 1e-10 is skipped; codes clamp(rint(w * (1/c)),
 //     -7, 7); error sum over the group in column order, fp32; the first
@@ -401,7 +402,9 @@ __global__ __launch_bounds__(256) void k_quantize_pack_cal(const void* __restric
   const int64_t grp = (int64_t)blockIdx.x * 4 + wv;
   if (grp >= ngroups) return;  // uniform per wave; no workgroup barrier follows
   const int g = 8 * cpg;
-  float* gl = cal_lds + wv * g;
+  int Pg = 32;
+  while (Pg < g) Pg <<= 1;
+  float* gl = cal_lds + wv * (g + (MODE == MODE_PCT ? Pg : 0));
   const int64_t c0 = grp * cpg;
   for (int c = lane; c < cpg; c += kWave) {
     float v[8];
@@ -413,19 +416,29 @@ __global__ __launch_bounds__(256) void k_quantize_pack_cal(const void* __restric
 
   float s32;
   if constexpr (MODE == MODE_PCT) {
-    float v0 = -1.0f, v1 = -1.0f;
-    for (int e = lane; e < g; e += kWave) {
-      const float ae = fabsf(gl[e]);
-      int rank = 0;
-      for (int kk = 0; kk < g; ++kk) {
-        const float ak = fabsf(gl[kk]);
-        rank += (ak < ae) || (ak == ae && kk < e);
+    // bitonic sort of |w|, padded with +inf to P = the next power of two,
+    // in the LDS region after the group's values; each stage's comparators
+    // are spread over the lanes, and a wave's LDS operations complete in
+    // order, so stages follow one another with no barrier
+    int P = 32;
+    while (P < g) P <<= 1;
+    float* srt = gl + g;
+    for (int e = lane; e < P; e += kWave) srt[e] = e < g ? fabsf(gl[e]) : __builtin_huge_valf();
+    for (int k2 = 2; k2 <= P; k2 <<= 1) {
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        for (int i = lane; i < (P >> 1); i += kWave) {
+          const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));  // comparator i: a, a + j
+          const float va = srt[a], vb = srt[a + j];
+          const float lo = fminf(va, vb), hi = fmaxf(va, vb);
+          const bool up = (a & k2) == 0;
+          srt[a] = up ? lo : hi;
+          srt[a + j] = up ? hi : lo;
+        }
       }
-      if (rank == i0) v0 = ae;
-      if (rank == i1) v1 = ae;
     }
-    v0 = group_max<kWave>(v0);
-    v1 = group_max<kWave>(v1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const float v0 = srt[i0], v1 = srt[i1];
     s32 = (v0 + frac * (v1 - v0)) / 7.0f;
   } else {
     float lo = __builtin_huge_valf(), hi = 0.0f;
@@ -478,7 +491,9 @@ static hipError_t launch_cal_t(const void* w, int64_t n, int64_t k, int g, int m
                                uint8_t* packed, void* scales, void* zeros, hipStream_t st) {
   const int64_t ngroups = n * (k / g);
   const dim3 grid((unsigned)((ngroups + 3) / 4));
-  const size_t lds = (size_t)4 * g * sizeof(float);
+  int P = 32;
+  while (P < g) P <<= 1;
+  const size_t lds = (size_t)4 * (g + (mode == MODE_PCT ? P : 0)) * sizeof(float);
   uint32_t* pk = (uint32_t*)packed;
   if (mode == MODE_PCT) {
     const double h = (g - 1) * (param / 100.0);
