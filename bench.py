@@ -81,7 +81,7 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="skip the extra per-step measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
-    ap.add_argument("--kernel", choices=("decode_wb", "prefill_wb", "w4a8_m1", "w4a8_m512", "copy"),
+    ap.add_argument("--kernel", choices=("decode_wb", "prefill_wb", "w4a8_m1", "w4a8_m512", "copy", "gptq"),
                     default=None,
                     help="launch only this kernel --launches times, eagerly, for counter runs: "
                          "decode_wb = the [11008,4096] decode product on rotated weights, "
@@ -369,7 +369,58 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
     del p, s, z, w1
 
     out["llama7b_decode_32_layers"] = llama_decode(w4, torch, dev, time_region, log, g)
+    out["gptq_Wb"] = gptq_bench(w4, torch, np, dev, time_region, log)
     return out
+
+
+def gptq_setup(torch, np, dev, n=11008, k=4096, t=4096):
+    """Weight [n, k] from N(0, 0.02) and t calibration rows from N(0, 1)
+    (synthetic stand-ins for a layer's weight and its input activations)."""
+    rng = np.random.default_rng(77)
+    w = torch.from_numpy(rng.normal(0, 0.02, (n, k)).astype(np.float32)).to(dev)
+    x = torch.from_numpy(rng.normal(0, 1, (t, k)).astype(np.float32)).to(dev)
+    return w, x
+
+
+def gptq_update_flops(n, k, block=128):
+    """Algorithmic flops of the sweep's lazy updates: 2 n b (k - b1) per block."""
+    return sum(2 * n * min(block, k - b0) * (k - b0 - min(block, k - b0)) for b0 in range(0, k, block))
+
+
+def gptq_bench(w4, torch, np, dev, time_region, log, n=11008, k=4096, t=4096, g=128):
+    """GPTQ on the Llama-7B gate shape: Hessian from t calibration rows, the
+    inverse Cholesky factor, and the column sweep, each timed on its own.  The
+    factor and sweep timings include a device copy of their input (h: 134 MB,
+    w: 180 MB), because both calls use it as working storage."""
+    w, x = gptq_setup(torch, np, dev, n, k, t)
+    h = torch.empty((k, k), dtype=torch.float64, device=dev)
+    hsec = time_region(lambda i: w4.gptq_hessian(x, out=h), 3)
+    hw = torch.empty_like(h)
+    u = torch.empty_like(h)
+
+    def factor(i):
+        hw.copy_(h)
+        w4.gptq_inverse_cholesky(hw, out=u, overwrite_h=True, check=False)
+    usec = time_region(factor, 3)
+    work = torch.empty_like(w)
+    outs = (torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+            torch.empty((n, k // g), dtype=torch.float16, device=dev),
+            torch.empty((n, k // g), dtype=torch.float16, device=dev))
+
+    def sweep(i):
+        work.copy_(w)
+        w4.gptq_quantize_pack_int4(work, u, g, False, torch.float16, overwrite_w=True, out=outs)
+    ssec = time_region(sweep, 3)
+    upd = gptq_update_flops(n, k)
+    res = {"shape": [n, k], "calibration_rows": t, "group": g,
+           "hessian_ms": round(hsec * 1e3, 3),
+           "hessian_fp64_TFLOP/s": round(t * k * k / hsec / 1e12, 2),
+           "inverse_cholesky_ms": round(usec * 1e3, 3),
+           "sweep_ms": round(ssec * 1e3, 3),
+           "sweep_update_TFLOP/s": round(upd / ssec / 1e12, 2),
+           "total_ms": round((hsec + usec + ssec) * 1e3, 3)}
+    log(f"gptq: {json.dumps(res)}")
+    return res
 
 
 # One Llama-7B decoder layer's linears with the usual fusions: q, k and v as
@@ -439,6 +490,17 @@ def kernel_only(args, w4, WL, torch, dev, to_dev, log):
         torch.cuda.synchronize()
         print(json.dumps({"kernel": "copy", "launches": n_launch, "read_bytes": nbytes,
                           "write_bytes": nbytes}), flush=True)
+        return 0
+    if args.kernel == "gptq":
+        import numpy as np
+        w, x = gptq_setup(torch, np, dev)
+        torch.cuda.synchronize()
+        for _ in range(n_launch):
+            u = w4.gptq_inverse_cholesky(w4.gptq_hessian(x), overwrite_h=True)
+            w4.gptq_quantize_pack_int4(w, u, 128, False, torch.float16)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": "gptq", "passes": n_launch,
+                          "update_flops_per_pass": gptq_update_flops(*w.shape)}), flush=True)
         return 0
     if args.kernel == "prefill_wb":
         g, n, k = 128, 11008, 4096

@@ -33,6 +33,9 @@ SIGNATURES = [
     ("quantize_act_int8", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP]),
     ("w4a16_matmul", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
     ("w4a8_matmul", _I, [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
+    ("gptq_hessian", _I, [_VP, _I64, _I64, _VP, _VP]),
+    ("gptq_inverse_cholesky", _I, [_VP, _I64, _VP, _VP, _VP]),
+    ("gptq_quantize_pack_int4", _I, [_VP, _VP, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _I, _VP]),
     ("w4_status_string", ctypes.c_char_p, [_I]),
     ("w4_last_error", ctypes.c_char_p, []),
     ("w4_version", ctypes.c_char_p, []),
@@ -133,6 +136,67 @@ def quantize_pack_int4_sym_mse(w: torch.Tensor, group_size: int, candidates: int
     fn = load().quantize_pack_int4_sym_mse
     return _quantize_pack(lambda w_, d, n, k, g, *rest: fn(w_, d, n, k, g, int(candidates), *rest),
                           w, group_size, sz_dtype, out)
+
+
+def gptq_hessian(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H = X^T X / T + 1e-4 mean(diag) I (float64 [K, K]) from float32 calibration rows X [T, K]."""
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be a float32 [T, K] tensor")
+    t, k = x.shape
+    dev = _gpu(x)
+    h = torch.empty((k, k), dtype=torch.float64, device=dev) if out is None else out
+    _gpu(h)
+    _check(load().gptq_hessian(_ptr(x), t, k, _ptr(h), _stream(dev)))
+    return h
+
+
+def gptq_inverse_cholesky(h: torch.Tensor, out: Optional[torch.Tensor] = None, overwrite_h: bool = False,
+                          check: bool = True):
+    """U (float64 [K, K], upper triangular, U^T U = H^-1).  h is used as the
+    factorization's workspace: it is copied first unless overwrite_h.  With
+    check, waits for the device status and raises if H is not positive
+    definite; otherwise returns (u, info) with info a device int32 tensor."""
+    if h.dtype != torch.float64 or h.dim() != 2 or h.shape[0] != h.shape[1]:
+        raise ValueError("h must be a square float64 tensor")
+    k = h.shape[0]
+    dev = _gpu(h)
+    work = h if overwrite_h else h.clone()
+    u = torch.empty((k, k), dtype=torch.float64, device=dev) if out is None else out
+    _gpu(u)
+    info = torch.empty((1,), dtype=torch.int32, device=dev)
+    _check(load().gptq_inverse_cholesky(_ptr(work), k, _ptr(u), _ptr(info), _stream(dev)))
+    if not check:
+        return u, info
+    bad = int(info.item())
+    if bad:
+        raise ValueError(f"gptq_inverse_cholesky: H is not positive definite (pivot of column {bad - 1})")
+    return u
+
+
+def gptq_quantize_pack_int4(w: torch.Tensor, u: torch.Tensor, group_size: int, symmetric: bool = False,
+                            sz_dtype: torch.dtype = torch.float16, overwrite_w: bool = False,
+                            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """GPTQ column sweep of W [N, K] (float32) with U from gptq_inverse_cholesky;
+    returns (packed, scales, zeros) in the library's format.  W is copied
+    first unless overwrite_w (the sweep uses it as working storage)."""
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a float32 [N, K] tensor")
+    if u.dtype != torch.float64 or tuple(u.shape) != (w.shape[1], w.shape[1]):
+        raise ValueError("u must be a float64 [K, K] tensor")
+    n, k = w.shape
+    dev = _gpu(w, u)
+    work = w if overwrite_w else w.clone()
+    if out is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, k // group_size), dtype=sz_dtype, device=dev)
+        zeros = torch.empty((n, k // group_size), dtype=sz_dtype, device=dev)
+    else:
+        packed, scales, zeros = out
+        _gpu(packed, scales, zeros)
+    _check(load().gptq_quantize_pack_int4(_ptr(work), _ptr(u), n, k, group_size, int(bool(symmetric)),
+                                          _ptr(packed), _ptr(scales), _ptr(zeros),
+                                          _dtype_code(scales.dtype), _stream(dev)))
+    return packed, scales, zeros
 
 
 def _quantize_pack(fn, w, group_size, sz_dtype, out):

@@ -164,6 +164,51 @@ int quantize_pack_int4_sym_mse(const void* w, int w_dtype, int64_t n, int64_t k,
                            zeros, sz_dtype, stream);
 }
 
+static constexpr int64_t kGptqMaxK = 65536;
+
+int gptq_hessian(const float* x, int64_t t, int64_t k, double* h, hipStream_t stream) {
+  static const char* fn = "gptq_hessian";
+  if (t < 1) return fail(W4_EINVAL, "%s: t = %lld calibration rows, at least 1 needed", fn, (long long)t);
+  if (k < 1 || k > kGptqMaxK)
+    return fail(W4_EINVAL, "%s: k = %lld must lie in [1, %lld]", fn, (long long)k, (long long)kGptqMaxK);
+  if (t > kMaxElems / k) return fail(W4_EINVAL, "%s: t * k is too large", fn);
+  W4_TRY(check_ptr(fn, "x", x));
+  W4_TRY(check_ptr(fn, "h", h));
+  return hip_status(w4::launch_gptq_hessian(x, t, (int)k, h, stream), fn);
+}
+
+int gptq_inverse_cholesky(double* h, int64_t k, double* u, int32_t* info, hipStream_t stream) {
+  static const char* fn = "gptq_inverse_cholesky";
+  if (k < 1 || k > kGptqMaxK)
+    return fail(W4_EINVAL, "%s: k = %lld must lie in [1, %lld]", fn, (long long)k, (long long)kGptqMaxK);
+  W4_TRY(check_ptr(fn, "h", h));
+  W4_TRY(check_ptr(fn, "u", u));
+  if (info == nullptr) return fail(W4_EINVAL, "%s: info is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(info) & 3u) != 0) return fail(W4_EINVAL, "%s: info is not 4-byte aligned", fn);
+  if ((const void*)h == (const void*)u) return fail(W4_EINVAL, "%s: h and u must be distinct", fn);
+  return hip_status(w4::launch_gptq_inverse_cholesky(h, (int)k, u, info, stream), fn);
+}
+
+int gptq_quantize_pack_int4(float* w, const double* u, int64_t n, int64_t k, int32_t group_size,
+                            int32_t symmetric, uint8_t* packed, void* scales, void* zeros,
+                            int sz_dtype, hipStream_t stream) {
+  static const char* fn = "gptq_quantize_pack_int4";
+  W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
+  if (!w4::gptq_group_ok(group_size))
+    return fail(W4_EINVAL, "%s: group_size = %d must be 32, 64 or a multiple of 128", fn, (int)group_size);
+  if (k > kGptqMaxK)
+    return fail(W4_EINVAL, "%s: k = %lld must be at most %lld", fn, (long long)k, (long long)kGptqMaxK);
+  if (n == 0) return ok();
+  W4_TRY(check_ptr(fn, "w", w));
+  W4_TRY(check_ptr(fn, "u", u));
+  W4_TRY(check_ptr(fn, "packed", packed));
+  W4_TRY(check_ptr(fn, "scales", scales));
+  W4_TRY(check_ptr(fn, "zeros", zeros));
+  return hip_status(w4::launch_gptq_quantize_pack(w, u, n, (int)k, group_size, symmetric != 0, packed,
+                                                  scales, zeros, sz_dtype, stream),
+                    fn);
+}
+
 int dequant_int4(const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
                  int64_t n, int64_t k, int32_t group_size, void* w_out, int out_dtype,
                  hipStream_t stream) {

@@ -36,6 +36,13 @@ bool quantize_cal_fits(int g);
 hipError_t launch_quantize_pack_cal(const void* w, int w_dtype, int64_t n, int64_t k, int g, int mode,
                                     double param, uint8_t* packed, void* scales, void* zeros,
                                     int sz_dtype, hipStream_t st);
+// GPTQ ([P4] Step 3): Hessian, inverse Cholesky factor, column sweep.
+bool gptq_group_ok(int g);
+hipError_t launch_gptq_hessian(const float* x, int64_t t, int k, double* h, hipStream_t st);
+hipError_t launch_gptq_inverse_cholesky(double* h, int k, double* u, int* info, hipStream_t st);
+hipError_t launch_gptq_quantize_pack(float* w, const double* u, int64_t n, int k, int g, bool symmetric,
+                                     uint8_t* packed, void* scales, void* zeros, int sz_dtype,
+                                     hipStream_t st);
 hipError_t launch_dequant(const uint8_t* packed, const void* scales, const void* zeros,
                           int sz_dtype, int64_t n, int64_t k, int g, void* out, int out_dtype,
                           hipStream_t st);

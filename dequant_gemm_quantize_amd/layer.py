@@ -5,8 +5,8 @@ Layer for LLaMA Weights", Step 3: the quantized linear layer; Step 5: the
 replacement pass over a model).
 
 Every numeric step runs in the HIP kernels behind libw4.so: quantization at
-construction (asymmetric, symmetric, or symmetric with a percentile or MSE
-calibrated scale), the product in forward (W4A16, or W4A8 with per-token
+construction (asymmetric, symmetric, symmetric with a percentile or MSE
+calibrated scale, or GPTQ with calibration activations), the product in forward (W4A16, or W4A8 with per-token
 INT8 activations).  This module only reshapes tensors and keeps the buffers.
 """
 from __future__ import annotations
@@ -22,7 +22,19 @@ QUANTIZERS = {
     "sym": lambda w, g, sz, p: _lib.quantize_pack_int4_sym(w, g, sz),
     "percentile": lambda w, g, sz, p: _lib.quantize_pack_int4_sym_percentile(w, g, 99.9 if p is None else p, sz),
     "mse": lambda w, g, sz, p: _lib.quantize_pack_int4_sym_mse(w, g, 1000 if p is None else int(p), sz),
+    "gptq": lambda w, g, sz, p: _gptq(w, g, sz, p, False),
+    "gptq_sym": lambda w, g, sz, p: _gptq(w, g, sz, p, True),
 }
+
+
+def _gptq(w: torch.Tensor, g: int, sz: torch.dtype, x: Optional[torch.Tensor], symmetric: bool):
+    """GPTQ ([P4] Step 3) with calibration rows x [T, in_features] (float32,
+    on the weight's GPU): Hessian, inverse Cholesky factor, column sweep."""
+    if x is None:
+        raise ValueError("GPTQ modes need the calibration rows X [T, in_features] as param")
+    h = _lib.gptq_hessian(x.reshape(-1, x.shape[-1]).to(torch.float32).contiguous())
+    u = _lib.gptq_inverse_cholesky(h, overwrite_h=True)
+    return _lib.gptq_quantize_pack_int4(w.to(torch.float32).contiguous(), u, g, symmetric, sz, overwrite_w=True)
 
 
 class QuantizedLinear(torch.nn.Module):
@@ -57,7 +69,8 @@ class QuantizedLinear(torch.nn.Module):
                     out_dtype: Optional[torch.dtype] = None) -> "QuantizedLinear":
         """Quantize W [out, in] (bf16 or fp32, on the GPU) with ``mode`` in
         asym / sym / percentile (param: p, default 99.9) / mse (param:
-        candidates, default 1000)."""
+        candidates, default 1000) / gptq or gptq_sym (param: calibration
+        rows X [T, in], required)."""
         if mode not in QUANTIZERS:
             raise ValueError(f"mode must be one of {sorted(QUANTIZERS)}")
         n, k = weight.shape

@@ -181,6 +181,58 @@ int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
                 const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
                 int64_t n, int32_t group_size, void* y, int y_dtype, hipStream_t stream);
 
+/*
+ * GPTQ second-order quantization ([P4] Step 3), in three calls.  Together
+ * they produce the packed format above from a weight and calibration rows;
+ * every matmul here takes the result.
+ *
+ * gptq_hessian -- h[K, K] = X^T X / T + 1e-4 * mean(diag(X^T X / T)) * I,
+ *   x [T, K] float32 calibration rows (T >= 1), h float64 output (both
+ *   triangles written).  Products are exact in float64 and each entry is
+ *   summed in row order; the damping term's mean is a fixed-order sum.
+ *   1 <= K <= 65536; x and h 16-byte aligned.
+ */
+int gptq_hessian(const float* x, int64_t t, int64_t k, double* h, hipStream_t stream);
+
+/*
+ * gptq_inverse_cholesky -- u[K, K] float64 = the upper-triangular factor U
+ *   with U^T U = H^-1 and a positive diagonal (the Cholesky factor of the
+ *   inverse, "upper-triangular form"), strictly lower part set to 0.
+ *   h [K, K] float64 symmetric positive definite; only its upper triangle
+ *   is read, and h is used as workspace: on return its contents are
+ *   unspecified.  info: one device int32, set to 0 on success, or to
+ *   1 + the index of the first column (the factorization visits columns
+ *   from the last to the first) whose pivot was not positive; u is then
+ *   unspecified.  The status is decided on the device: the call does not
+ *   wait for it.  h, u 16-byte aligned and distinct; 1 <= K <= 65536.
+ *   Float64 throughout; the result matches the factor of the exact inverse
+ *   to about cond(H) * 1e-16.
+ */
+int gptq_inverse_cholesky(double* h, int64_t k, double* u, int32_t* info, hipStream_t stream);
+
+/*
+ * gptq_quantize_pack_int4 -- the column sweep.  For each row of W [N, K]
+ *   (float32, row-major) and each column i from left to right:
+ *     when i starts a group, the group's scale and zero-point are computed
+ *       from the group's current values with the formulas of
+ *       quantize_pack_int4 (symmetric = 0) or quantize_pack_int4_sym
+ *       (symmetric != 0, zero-points written as 8);
+ *     q_i = the code of w_i with those parameters (the same float32 steps);
+ *     e = (w_i - (q_i - zp) * scale) / U[i, i];
+ *     w_j -= e * U[i, j] for every j > i.
+ *   u is gptq_inverse_cholesky's output.  Outputs packed / scales / zeros
+ *   as quantize_pack_int4.  w is working storage: on return column i of
+ *   each row holds that row's e for column i.  group_size: 32, 64, or a
+ *   multiple of 128 (W4_EINVAL otherwise); 1 <= K <= 65536.  The updates
+ *   are applied 128 columns at a time with float32 products, so the values
+ *   a code is decided on differ from an exact sweep by rounding; a code or
+ *   zero-point can then differ by one where the decision is that close to
+ *   a tie.
+ */
+int gptq_quantize_pack_int4(float* w, const double* u, int64_t n, int64_t k, int32_t group_size,
+                            int32_t symmetric, uint8_t* packed, void* scales, void* zeros,
+                            int sz_dtype, hipStream_t stream);
+
 /* Static description of a w4_status value (never NULL). */
 const char* w4_status_string(int status);
 

@@ -43,7 +43,9 @@ output: given its codes and group parameters as a ``guide``, it replays the
 sweep, accepts a differing decision only where its own float64 decision
 variable lies within ``tol`` of the rounding boundary between the two (or a
 scale within ``scale_rtol``), continues with the guide's choice, and counts
-such acceptances; any other difference raises.
+such acceptances (codes, zero-points; a float32 scale is continuous in the
+values, so scales are only held to the tolerance); any other difference
+raises.
 """
 from __future__ import annotations
 
@@ -94,7 +96,7 @@ def _decide(v32, s, zp, symmetric):
 
 
 def gptq_quantize(w, u, g: int, sz: str, symmetric: bool, guide=None, tol: float = 1e-3,
-                  scale_rtol: float = 2e-3, trace: bool = False):
+                  scale_rtol=None, trace: bool = False):
     """The column sweep over W [N, K] (float32 values) with U [K, K].
 
     Returns (codes uint8 [N, K], scales [N, K/g] sz dtype, zeros [N, K/g] sz
@@ -109,7 +111,9 @@ def gptq_quantize(w, u, g: int, sz: str, symmetric: bool, guide=None, tol: float
     codes = np.zeros((n, k), np.uint8)
     scales = np.zeros((n, k // g), sd)
     zeros = np.zeros((n, k // g), np.int32)
-    stats = {"codes_accepted": 0, "params_accepted": 0}
+    stats = {"codes_accepted": 0, "zeros_accepted": 0, "scales_differing": 0}
+    if scale_rtol is None:                 # about one unit in the last place of the stored scale
+        scale_rtol = 2e-3 if sz == "f16" else 1e-5
     tr = np.zeros((n, k)) if trace else None
     s = zp = None
     if guide is not None:
@@ -172,7 +176,7 @@ def _accept_params(vals32, vals64, s_st, zpo, s_g, z_g, symmetric, sz, tol, rtol
         b = s_g[diff_s].astype(F64)
         if not (np.abs(a - b) <= rtol * np.abs(a)).all():
             raise AssertionError(f"group at column {i}: scale outside tolerance")
-        stats["params_accepted"] += int(diff_s.sum())
+        stats["scales_differing"] += int(diff_s.sum())
     s32 = s_g.astype(F32)
     if symmetric:
         if not (z_g == W.SYM_OFFSET).all():
@@ -186,7 +190,7 @@ def _accept_params(vals32, vals64, s_st, zpo, s_g, z_g, symmetric, sz, tol, rtol
         bound = (zp_due[bad] + z_g[bad]) / 2.0
         if not ((np.abs(zp_due[bad] - z_g[bad]) == 1) & (np.abs(t64 - bound) <= tol)).all():
             raise AssertionError(f"group at column {i}: zero-point outside tolerance")
-        stats["params_accepted"] += int(bad.size)
+        stats["zeros_accepted"] += int(bad.size)
     return s_g, z_g
 
 

@@ -197,8 +197,51 @@ def test_layer_arguments_without_gpu():
     with pytest.raises(ValueError, match="has one"):
         w4.QuantizedLinear.from_linear(torch.nn.Linear(256, 64, bias=True))
     with pytest.raises(ValueError, match="mode must be one of"):
+        w4.QuantizedLinear.from_weight(torch.zeros(64, 256), mode="awq")
+    with pytest.raises(ValueError, match="calibration rows"):
         w4.QuantizedLinear.from_weight(torch.zeros(64, 256), mode="gptq")
     layer = w4.QuantizedLinear(256, 64, group_size=128)
     assert tuple(layer.packed.shape) == (64, 128) and tuple(layer.scales.shape) == (64, 2)
     with pytest.raises(ValueError, match="features"):
         layer(torch.zeros(2, 128))
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, 0, 64, A, None), "t = 0 calibration rows"),
+    ((A, 8, 0, A, None), "k = 0 must lie in [1, 65536]"),
+    ((A, 8, 65537, A, None), "must lie in [1, 65536]"),
+    ((U, 8, 64, A, None), "x is not 16-byte aligned"),
+    ((A, 8, 64, None, None), "h is NULL"),
+    ((A, 1 << 40, 64, A, None), "t * k is too large"),
+])
+def test_gptq_hessian_rejects(lib, args, msg):
+    assert lib.gptq_hessian(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, 0, A + 256, A, None), "k = 0 must lie"),
+    ((A, 64, A + 256, None, None), "info is NULL"),
+    ((A, 64, A + 256, A + 2, None), "info is not 4-byte aligned"),
+    ((A, 64, A, A, None), "h and u must be distinct"),
+    ((U, 64, A, A, None), "h is not 16-byte aligned"),
+])
+def test_gptq_inverse_cholesky_rejects(lib, args, msg):
+    assert lib.gptq_inverse_cholesky(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((A, A, 4, 384, 96, 0, A, A, A, 1, None), "must be 32, 64 or a multiple of 128"),
+    ((A, A, 4, 384, 160, 0, A, A, A, 1, None), "not a multiple of group_size"),
+    ((A, A, 4, 131072, 128, 0, A, A, A, 1, None), "must be at most 65536"),
+    ((A, None, 4, 256, 128, 1, A, A, A, 1, None), "u is NULL"),
+    ((A, A, 4, 256, 128, 1, A, A, A, 7, None), "scale dtype"),
+])
+def test_gptq_quantize_rejects(lib, args, msg):
+    assert lib.gptq_quantize_pack_int4(*args) == -1
+    assert msg in _err(lib), _err(lib)
+
+
+def test_gptq_empty_sweep_is_noop(lib):
+    assert lib.gptq_quantize_pack_int4(None, None, 0, 256, 128, 0, None, None, None, 1, None) == 0

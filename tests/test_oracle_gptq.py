@@ -90,7 +90,7 @@ def test_replay_accepts_own_output_and_rejects_a_wrong_code():
     for symmetric in (False, True):
         packed, s, z = G.gptq_quantize_pack_int4(w, "f32", u, 32, "f16", symmetric)
         _, _, _, stats, _ = G.gptq_quantize(w, u, 32, "f16", symmetric, guide=(packed, s, z))
-        assert stats == {"codes_accepted": 0, "params_accepted": 0}
+        assert stats == {"codes_accepted": 0, "zeros_accepted": 0, "scales_differing": 0}
         codes = O.unpack_nibbles(packed)
         _, _, _, _, tr = G.gptq_quantize(w, u, 32, "f16", symmetric, trace=True)
         # the code whose decision variable is farthest from a rounding boundary
