@@ -17,8 +17,8 @@
 //     current values), its error e = (w - w_hat) / U[i, i] propagated into
 //     the later columns as w_j -= e * U[i, j].  Columns go in blocks of 128
 //     (the lazy-batch form of the method): one kernel runs the sequential
-//     part inside a block, one wave per weight row with the block's 128
-//     values in registers and U's diagonal block in LDS; a float32 MFMA
+//     part inside a block, one lane per weight row, with U's diagonal block
+//     in LDS; a float32 MFMA
 //     kernel then applies the block's errors to every later column at once,
 //     W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:].
 //
@@ -67,17 +67,19 @@ __global__ __launch_bounds__(256) void k_gptq_hessian(const float* __restrict__ 
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
   for (int64_t s0 = 0; s0 < t; s0 += HS) {
+    float va[(HS * HT) / 256], vb[(HS * HT) / 256];
 #pragma unroll
     for (int r = 0; r < (HS * HT) / 256; ++r) {
       const int e = tid + 256 * r, s = e >> 6, c = e & 63;
       const int64_t ts = s0 + s;
-      float va = 0.f, vb = 0.f;
-      if (ts < t) {
-        if (i0 + c < k) va = x[ts * k + i0 + c];
-        if (j0 + c < k) vb = x[ts * k + j0 + c];
-      }
-      xi[s][c] = va;
-      xj[s][c] = vb;
+      va[r] = (ts < t && i0 + c < k) ? x[ts * k + i0 + c] : 0.f;
+      vb[r] = (ts < t && j0 + c < k) ? x[ts * k + j0 + c] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < (HS * HT) / 256; ++r) {
+      const int e = tid + 256 * r, s = e >> 6, c = e & 63;
+      xi[s][c] = va[r];
+      xj[s][c] = vb[r];
     }
     __syncthreads();
 #pragma unroll 4
@@ -134,66 +136,86 @@ __device__ __forceinline__ double view_lower(const double* h, int k, int a, int 
   return a == b ? 1.0 : 0.0;
 }
 
-// Factor the diagonal tile kb (unblocked, in LDS).  info receives 1 + the
+// Factor the diagonal tile kb in one wave (left-looking): lane i keeps row
+// i of the tile in registers; at step j it forms
+// s_i = A[i][j] - sum_{m<j} L[i][m] L[j][m] with row j of L read from LDS
+// (a broadcast), and the pivot is sqrt(s_j).  info receives 1 + the
 // original column index of the first pivot that is not positive.
-__global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ h, int k, int kb,
-                                                   int* __restrict__ info) {
-  __shared__ double A[NB][LDP];
-  const int tid = threadIdx.x, o = kb * NB;
-  if (kb == 0 && tid == 0) *info = 0;
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    A[r][c] = c <= r ? view_lower(h, k, o + r, o + c) : 0.0;
-  }
-  __syncthreads();
+__global__ __launch_bounds__(64) void k_chol_diag(double* __restrict__ h, int k, int kb,
+                                                  int* __restrict__ info) {
+  __shared__ double Lr[NB][LDP];
+  const int i = threadIdx.x, o = kb * NB;
+  if (kb == 0 && i == 0) *info = 0;
+  double a[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) a[c] = c <= i ? view_lower(h, k, o + i, o + c) : 0.0;
+#pragma unroll
   for (int j = 0; j < NB; ++j) {
-    if (tid == 0) {
-      const double d = A[j][j];
-      if (!(d > 0.0) && o + j < k && *info == 0) *info = k - (o + j);
-      A[j][j] = sqrt(d);
+    double s0 = a[j], s1 = 0.0, s2 = 0.0, s3 = 0.0;
+#pragma unroll
+    for (int m = 0; m < j; ++m) {
+      const double l = Lr[j][m];
+      if ((m & 3) == 0) s0 = fma(-a[m], l, s0);
+      else if ((m & 3) == 1) s1 = fma(-a[m], l, s1);
+      else if ((m & 3) == 2) s2 = fma(-a[m], l, s2);
+      else s3 = fma(-a[m], l, s3);
     }
-    __syncthreads();
-    const double piv = A[j][j];
-    if (tid > j && tid < NB) A[tid][j] = A[tid][j] / piv;
-    __syncthreads();
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int r = e / NB, c = e % NB;
-      if (c > j && c <= r) A[r][c] = fma(-A[r][j], A[c][j], A[r][c]);
-    }
+    const double s = (s0 + s1) + (s2 + s3);
+    const double d = __shfl(s, j, kWave);
+    if (i == 0 && !(d > 0.0) && o + j < k && *info == 0) *info = k - (o + j);
+    const double piv = sqrt(d);
+    if (i == j) a[j] = piv;
+    else if (i > j) a[j] = s / piv;
+    Lr[i][j] = a[j];
     __syncthreads();
   }
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    if (c <= r && o + r < k) h[rev(k, o + r, o + c)] = A[r][c];
-  }
+  if (o + i < k)
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+      if (c <= i) h[rev(k, o + i, o + c)] = a[c];
 }
 
 // Panel: the tiles below diagonal tile kb, X L_kk^T = A, one tile row per
-// workgroup, one row of it per thread.
-__global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ h, int k, int kb) {
+// workgroup.  Each row is solved by four lanes of one wave; lane `sub` keeps
+// the row's columns sub, sub + 4, ... in registers, so every inner product
+// is split by m mod 4 and its parts combined with two butterflies.
+__global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ h, int k, int kb) {
   __shared__ double L[NB][LDP];
-  __shared__ double X[NB][LDP];
-  const int r = threadIdx.x, o = kb * NB, ob = (kb + 1 + (int)blockIdx.x) * NB;
-  for (int e = r; e < NB * NB; e += 64) {
+  const int tid = threadIdx.x, r = tid >> 2, sub = tid & 3;
+  const int o = kb * NB, ob = (kb + 1 + (int)blockIdx.x) * NB;
+  #pragma unroll
+  for (int r_ = 0; r_ < NB * NB / 256; ++r_) {
+    const int e = tid + 256 * r_;
     const int rr = e / NB, c = e % NB;
     L[rr][c] = c <= rr ? view_lower(h, k, o + rr, o + c) : 0.0;
-    X[rr][c] = (ob + rr < k && o + c < k) ? h[rev(k, ob + rr, o + c)] : 0.0;
+  }
+  const bool live = ob + r < k;
+  double x[NB / 4];
+#pragma unroll
+  for (int t = 0; t < NB / 4; ++t) {
+    const int c = sub + 4 * t;
+    x[t] = (live && o + c < k) ? h[rev(k, ob + r, o + c)] : 0.0;
   }
   __syncthreads();
+#pragma unroll
   for (int c = 0; c < NB; ++c) {
-    double s0 = X[r][c], s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    int m = 0;
-    for (; m + 4 <= c; m += 4) {
-      s0 = fma(-X[r][m], L[c][m], s0);
-      s1 = fma(-X[r][m + 1], L[c][m + 1], s1);
-      s2 = fma(-X[r][m + 2], L[c][m + 2], s2);
-      s3 = fma(-X[r][m + 3], L[c][m + 3], s3);
-    }
-    for (; m < c; ++m) s0 = fma(-X[r][m], L[c][m], s0);
-    X[r][c] = ((s0 + s1) + (s2 + s3)) / L[c][c];
+    double p = 0.0;
+#pragma unroll
+    for (int t = 0; t < NB / 4; ++t)
+      if (4 * t < c) {                       // m = sub + 4t < c, decided per lane below
+        const double v = sub + 4 * t < c ? x[t] : 0.0;
+        p = fma(v, L[c][sub + 4 * t], p);
+      }
+    p += __shfl_xor(p, 1, kWave);
+    p += __shfl_xor(p, 2, kWave);
+    if (sub == (c & 3)) x[c >> 2] = (x[c >> 2] - p) / L[c][c];
   }
-  if (ob + r < k)
-    for (int c = 0; c < NB && o + c < k; ++c) h[rev(k, ob + r, o + c)] = X[r][c];
+  if (live)
+#pragma unroll
+    for (int t = 0; t < NB / 4; ++t) {
+      const int c = sub + 4 * t;
+      if (o + c < k) h[rev(k, ob + r, o + c)] = x[t];
+    }
 }
 
 // Trailing update: tile (ib, jb), kb < jb <= ib, minus L_ib,kb L_jb,kb^T.
@@ -204,7 +226,9 @@ __global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ h, int
   __shared__ double Lj[NB][LDP];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int o = kb * NB, oi = ib * NB, oj = jb * NB;
-  for (int e = tid; e < NB * NB; e += 256) {
+  #pragma unroll
+  for (int r_ = 0; r_ < NB * NB / 256; ++r_) {
+    const int e = tid + 256 * r_;
     const int rr = e / NB, c = e % NB;
     const bool cin = o + c < k;
     Li[rr][c] = (cin && oi + rr < k) ? h[rev(k, oi + rr, o + c)] : 0.0;
@@ -240,13 +264,10 @@ __global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ h, int
     }
 }
 
-// Strictly lower part of U (never written by the inverse kernels) = 0.
-__global__ __launch_bounds__(256) void k_zero_lower(double* __restrict__ u, int k) {
-  const int64_t total = (int64_t)k * k;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t i = e / k, j = e - i * k;
-    if (i > j) u[e] = 0.0;
-  }
+// u = 0: the strictly lower part of U, and the accumulators of the inverse.
+__global__ __launch_bounds__(256) void k_zero(double* __restrict__ u, int64_t total) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+    u[e] = 0.0;
 }
 
 // Inverse of each diagonal tile of L; thread t solves column t.
@@ -255,7 +276,9 @@ __global__ __launch_bounds__(64) void k_trinv_diag(const double* __restrict__ h,
   __shared__ double L[NB][LDP];
   __shared__ double X[NB][LDP];
   const int t = threadIdx.x, o = (int)blockIdx.x * NB;
-  for (int e = t; e < NB * NB; e += 64) {
+  #pragma unroll
+  for (int r_ = 0; r_ < NB * NB / 64; ++r_) {
+    const int e = t + 64 * r_;
     const int rr = e / NB, c = e % NB;
     L[rr][c] = c <= rr ? view_lower(h, k, o + rr, o + c) : 0.0;
   }
@@ -280,72 +303,88 @@ __global__ __launch_bounds__(64) void k_trinv_diag(const double* __restrict__ h,
     for (int r = 0; r < NB && o + r < k; ++r) u[rev(k, o + r, o + t)] = X[r][t];
 }
 
-// Tile (ib, jb), jb < ib, of L^-1:  X_ij = -X_ii * sum_{m=jb}^{ib-1} L_im X_mj.
-__global__ __launch_bounds__(256) void k_trinv_row(const double* __restrict__ h, double* __restrict__ u,
-                                                   int k, int ib) {
-  __shared__ double A[NB][LDP];
-  __shared__ double B[NB][LDP];
-  const int jb = blockIdx.x;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int oi = ib * NB, oj = jb * NB;
-  double acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int mb = jb; mb < ib; ++mb) {
-    const int om = mb * NB;
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int rr = e / NB, c = e % NB;
-      A[rr][c] = (oi + rr < k && om + c < k) ? h[rev(k, oi + rr, om + c)] : 0.0;
-      B[rr][c] = (om + rr < k && oj + c < k) ? u[rev(k, om + rr, oj + c)] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < NB; ++c) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = A[ty + 16 * a][c];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = B[c][tx + 16 * b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) A[ty + 16 * a][tx + 16 * b] = acc[a][b];
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int rr = e / NB, c = e % NB;
-    B[rr][c] = (c <= rr && oi + rr < k && oi + c < k) ? u[rev(k, oi + rr, oi + c)] : 0.0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+// Right-looking inverse: tile (i, j), j < i, of X = L^-1 is
+// X_ij = -X_ii B_ij with B_ij = sum_{m=j}^{i-1} L_im X_mj.  B accumulates in
+// u at X's place: when block row m is final, every later block row ib gets
+// L_ib,m X_m,j added for all j <= m (k_trinv_update, many tiles at once),
+// and block row m + 1 is finalized (k_trinv_final).
+__device__ __forceinline__ void tile_mma(const double (*A)[LDP], const double (*B)[LDP], int tx, int ty,
+                                         double acc[4][4]) {
 #pragma unroll 4
   for (int c = 0; c < NB; ++c) {
     double av[4], bv[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) av[a] = B[ty + 16 * a][c];
+    for (int a = 0; a < 4; ++a) av[a] = A[ty + 16 * a][c];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bv[b] = A[c][tx + 16 * b];
+    for (int b = 0; b < 4; ++b) bv[b] = B[c][tx + 16 * b];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
   }
+}
+
+// B_ib,j += L_ib,m X_m,j for ib = m+1+blockIdx.y, j = blockIdx.x <= m.
+__global__ __launch_bounds__(256) void k_trinv_update(const double* __restrict__ h, double* __restrict__ u,
+                                                      int k, int m) {
+  __shared__ double A[NB][LDP];
+  __shared__ double B[NB][LDP];
+  const int jb = blockIdx.x, ib = m + 1 + (int)blockIdx.y;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int oi = ib * NB, oj = jb * NB, om = m * NB;
+  #pragma unroll
+  for (int r_ = 0; r_ < NB * NB / 256; ++r_) {
+    const int e = tid + 256 * r_;
+    const int rr = e / NB, c = e % NB;
+    A[rr][c] = (oi + rr < k && om + c < k) ? h[rev(k, oi + rr, om + c)] : 0.0;
+    B[rr][c] = (om + rr < k && oj + c < k) ? u[rev(k, om + rr, oj + c)] : 0.0;
+  }
+  __syncthreads();
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  tile_mma(A, B, tx, ty, acc);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int r = ty + 16 * a, q = tx + 16 * b;
-      if (oi + r < k && oj + q < k) u[rev(k, oi + r, oj + q)] = -acc[a][b];
+      if (oi + r < k && oj + q < k) {
+        const int64_t p = rev(k, oi + r, oj + q);
+        u[p] = u[p] + acc[a][b];
+      }
+    }
+}
+
+// X_m,j = -X_mm B_m,j for j = blockIdx.x < m (in place).
+__global__ __launch_bounds__(256) void k_trinv_final(double* __restrict__ u, int k, int m) {
+  __shared__ double A[NB][LDP];
+  __shared__ double B[NB][LDP];
+  const int jb = blockIdx.x;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int om = m * NB, oj = jb * NB;
+  #pragma unroll
+  for (int r_ = 0; r_ < NB * NB / 256; ++r_) {
+    const int e = tid + 256 * r_;
+    const int rr = e / NB, c = e % NB;
+    A[rr][c] = (c <= rr && om + rr < k && om + c < k) ? u[rev(k, om + rr, om + c)] : 0.0;
+    B[rr][c] = (om + rr < k && oj + c < k) ? u[rev(k, om + rr, oj + c)] : 0.0;
+  }
+  __syncthreads();
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  tile_mma(A, B, tx, ty, acc);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = ty + 16 * a, q = tx + 16 * b;
+      if (om + r < k && oj + q < k) u[rev(k, om + r, oj + q)] = -acc[a][b];
     }
 }
 
@@ -356,59 +395,108 @@ template <typename TS> __device__ __forceinline__ float stored(float v);
 template <> __device__ __forceinline__ float stored<float>(float v) { return v; }
 template <> __device__ __forceinline__ float stored<_Float16>(float v) { return (float)(_Float16)v; }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-  return v;
+constexpr int SB = 16;   // sub-block of the sweep (columns)
+constexpr int SWEEP_THREADS = 256;  // rows per sweep workgroup (one per lane)
+constexpr int ULD = CB + 4;  // LDS row of the U tile (floats; 16-byte multiple)
+
+// One column's decision with the group's scale s and zero-point zp: the
+// stored code and the dequantized value, in the same float32 steps as the
+// round-to-nearest quantizer.
+template <bool SYM>
+__device__ __forceinline__ float decide(float v, float s, float zp, float& dq) {
+  if (SYM) {
+    const float q = fminf(fmaxf(rintf(v / s), -8.f), 7.f);
+    dq = q * s;
+    return q + 8.f;
+  }
+  const float q = fminf(fmaxf(rintf(v / s + zp), 0.f), 15.f);
+  dq = (q - zp) * s;
+  return q;
 }
 
-// Columns [b0, b0 + bw) of every row: one wave per row, lane l holding
-// columns b0 + l and b0 + 64 + l.  On exit the block's columns of w hold the
-// scaled errors e, which the update kernel consumes.
+// dst = w[b0 + c .. + SB) of this row minus the updates from the block's
+// columns [b0, b0 + upto), whose errors e were stored in w already.
+__device__ __forceinline__ void load_updated(float (&dst)[SB], const float* wr, int b0, int c, int upto,
+                                             const float (*Us)[ULD]) {
+#pragma unroll
+  for (int q = 0; q < SB / 4; ++q) {
+    const f32x4 t = *(const f32x4*)(wr + b0 + c + 4 * q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[4 * q + j] = t[j];
+  }
+  for (int i = 0; i < upto; i += 4) {
+    const f32x4 e4 = *(const f32x4*)(wr + b0 + i);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int j = 0; j < SB; ++j) dst[j] = fmaf(-e4[ii], Us[i + ii][c + j], dst[j]);
+  }
+}
+
+// Columns [b0, b0 + bw) of 256 rows per workgroup, one lane per row, U's
+// diagonal block in LDS (float32).  The block is walked in sub-blocks of 16
+// columns: a sub-block's values are loaded and brought up to date with the
+// errors of the block's earlier sub-blocks (read back from w, where they
+// were stored), then its columns are quantized one at a time with the
+// updates inside the sub-block applied in registers.  The errors replace the
+// values in w (the update kernel consumes them), the codes are packed and
+// stored per sub-block.
 template <bool SYM, typename TS>
-__global__ __launch_bounds__(1024) void k_gptq_sweep(float* __restrict__ w, const double* __restrict__ u,
-                                                     int64_t n, int k, int g, int b0, int bw,
-                                                     uint8_t* __restrict__ packed, TS* __restrict__ scales,
-                                                     TS* __restrict__ zeros) {
-  __shared__ float Us[CB][CB];
+__global__ __launch_bounds__(SWEEP_THREADS) void k_gptq_sweep(float* __restrict__ w, const double* __restrict__ u,
+                                                   int64_t n, int k, int g, int b0, int bw,
+                                                   uint8_t* __restrict__ packed, TS* __restrict__ scales,
+                                                   TS* __restrict__ zeros) {
+  __shared__ __align__(16) float Us[CB][ULD];
+  __shared__ float rdiag[CB];
   const int tid = threadIdx.x;
-  for (int e = tid; e < CB * CB; e += 1024) {
-    const int i = e / CB, j = e % CB;
-    Us[i][j] = (i < bw && j < bw) ? (float)u[(int64_t)(b0 + i) * k + b0 + j] : 0.f;
+  constexpr int kPer = CB * CB / 2 / SWEEP_THREADS;   // double2 loads per thread
+  static_assert(kPer % 16 == 0, "staging batches");
+#pragma unroll
+  for (int bt = 0; bt < kPer; bt += 16) {
+    double2 d[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = tid + SWEEP_THREADS * (bt + r), i = e / (CB / 2), j = 2 * (e % (CB / 2));
+      d[r] = (i < bw && j < bw) ? *(const double2*)(u + (int64_t)(b0 + i) * k + b0 + j) : double2{0.0, 0.0};
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int e = tid + SWEEP_THREADS * (bt + r), i = e / (CB / 2), j = 2 * (e % (CB / 2));
+      Us[i][j] = (float)d[r].x;
+      Us[i][j + 1] = (float)d[r].y;
+    }
   }
   __syncthreads();
-  const int lane = tid & 63;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 6);
+  if (tid < CB) rdiag[tid] = tid < bw ? 1.f / Us[tid][tid] : 0.f;
+  __syncthreads();
+  const int64_t row = (int64_t)blockIdx.x * SWEEP_THREADS + tid;
   if (row >= n) return;
   float* wr = w + row * k;
   const int ng = k / g;
-  float v0 = lane < bw ? wr[b0 + lane] : 0.f;
-  float v1 = 64 + lane < bw ? wr[b0 + 64 + lane] : 0.f;
-  int c0 = 0, c1 = 0;
   float s = 1.f, zp = SYM ? 8.f : 0.f;
   if (b0 % g != 0) {  // a group of more than one block continues here
     s = (float)scales[row * ng + b0 / g];
     zp = (float)zeros[row * ng + b0 / g];
   }
-  for (int i = 0; i < bw; ++i) {
-    if ((b0 + i) % g == 0) {
-      const bool in0 = lane >= i && lane < i + g;
-      const bool in1 = 64 + lane >= i && 64 + lane < i + g;
-      float hi = -INFINITY, lo = INFINITY;
-      if (in0) { hi = v0; lo = v0; }
-      if (in1) { hi = fmaxf(hi, v1); lo = fminf(lo, v1); }
-      for (int c = b0 + bw + lane; c < b0 + g; c += 64) {
-        const float v = wr[c];
-        hi = fmaxf(hi, v);
-        lo = fminf(lo, v);
+  for (int c0 = 0; c0 < bw; c0 += SB) {
+    float v[SB];
+    load_updated(v, wr, b0, c0, c0, Us);
+    if ((b0 + c0) % g == 0) {
+      float hi = v[0], lo = v[0];
+#pragma unroll
+      for (int j = 1; j < SB; ++j) {
+        hi = fmaxf(hi, v[j]);
+        lo = fminf(lo, v[j]);
       }
-      hi = wave_max(hi);
-      lo = wave_min(lo);
+      for (int c2 = c0 + SB; c2 < c0 + g; c2 += SB) {
+        float t[SB];
+        load_updated(t, wr, b0, c2, c2 < bw ? c0 : 0, Us);
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          hi = fmaxf(hi, t[j]);
+          lo = fminf(lo, t[j]);
+        }
+      }
       float s_st;
       if (SYM) {
         s_st = stored<TS>(fmaxf(hi, -lo) / 7.f);
@@ -420,48 +508,31 @@ __global__ __launch_bounds__(1024) void k_gptq_sweep(float* __restrict__ w, cons
         zp = fminf(fmaxf(rintf(-lo / s_st), 0.f), 15.f);
       }
       s = s_st;
-      if (lane == 0) {
-        scales[row * ng + (b0 + i) / g] = (TS)s_st;
-        zeros[row * ng + (b0 + i) / g] = (TS)zp;
-      }
+      scales[row * ng + (b0 + c0) / g] = (TS)s_st;
+      zeros[row * ng + (b0 + c0) / g] = (TS)zp;
     }
-    const float src = i < 64 ? v0 : v1;
-    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), i & 63));
-    float q, dq;
-    if (SYM) {
-      q = fminf(fmaxf(rintf(v / s), -8.f), 7.f);
-      dq = q * s;
-      q = q + 8.f;
-    } else {
-      q = fminf(fmaxf(rintf(v / s + zp), 0.f), 15.f);
-      dq = (q - zp) * s;
+    uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+    for (int jj = 0; jj < SB; ++jj) {
+      float dq;
+      const float q = decide<SYM>(v[jj], s, zp, dq);
+      const float e = (v[jj] - dq) * rdiag[c0 + jj];
+#pragma unroll
+      for (int j2 = jj + 1; j2 < SB; ++j2) v[j2] = fmaf(-e, Us[c0 + jj][c0 + j2], v[j2]);
+      v[jj] = e;
+      cw[jj >> 3] |= (uint32_t)q << (4 * (jj & 7));
     }
-    const float e = (v - dq) / Us[i][i];
-    v0 = fmaf(-e, Us[i][lane], v0);
-    v1 = fmaf(-e, Us[i][64 + lane], v1);
-    if (lane == (i & 63)) {
-      if (i < 64) {
-        v0 = e;
-        c0 = (int)q;
-      } else {
-        v1 = e;
-        c1 = (int)q;
-      }
-    }
-  }
-  if (lane < bw) wr[b0 + lane] = v0;
-  if (64 + lane < bw) wr[b0 + 64 + lane] = v1;
-  const int h0 = __shfl_down(c0, 1, kWave), h1 = __shfl_down(c1, 1, kWave);
-  uint8_t* pr = packed + row * (k / 2);
-  if ((lane & 1) == 0) {
-    if (lane < bw) pr[(b0 + lane) / 2] = (uint8_t)(c0 | (h0 << 4));
-    if (64 + lane < bw) pr[(b0 + 64 + lane) / 2] = (uint8_t)(c1 | (h1 << 4));
+#pragma unroll
+    for (int q = 0; q < SB / 4; ++q)
+      *(f32x4*)(wr + b0 + c0 + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    *(u32x2*)(packed + row * (k / 2) + (b0 + c0) / 2) = u32x2{cw[0], cw[1]};
   }
 }
 
 // W[:, b1:] -= E[:, b0:b1] * U[b0:b1, b1:] with b1 = b0 + bw, float32 MFMA.
 // Workgroup tile 128 rows x 128 columns, four waves of 64 x 64 (2 x 2
-// v_mfma_f32_32x32x2f32 tiles), K = bw in LDS stages of 32.
+// v_mfma_f32_32x32x2f32 tiles), K = bw in LDS stages of 32; the next stage's
+// global loads are issued before the current stage's MFMAs.
 __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, const double* __restrict__ u,
                                                      int64_t n, int k, int b0, int bw) {
   __shared__ float Es[128][33];
@@ -471,6 +542,32 @@ __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, cons
   const int c0 = b1 + (int)blockIdx.y * 128;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wr = wv >> 1, wc = wv & 1;
   const int l32 = lane & 31, lk = lane >> 5;
+  // stage loads: E as 4 float4 per thread (row tid/8 + 32j, columns 4 (tid%8)),
+  // U as 8 double2 per thread (row tid/64 + 4j, columns 2 (tid%64))
+  const int er = tid >> 3, ec = 4 * (tid & 7);
+  const int ur = tid >> 6, uc = 2 * (tid & 63);
+  f32x4 ev[4];
+  double ua[8], ub[8];
+  auto load_stage = [&](int kk) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = r0 + er + 32 * j;
+      ev[j] = row < n ? *(const f32x4*)(w + row * k + b0 + kk + ec) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = c0 + uc;
+      const double* src = u + (int64_t)(b0 + kk + ur + 4 * j) * k + col;
+      if (col < k) {
+        const double2 d = *(const double2*)src;
+        ua[j] = d.x;
+        ub[j] = d.y;
+      } else {
+        ua[j] = 0.0;
+        ub[j] = 0.0;
+      }
+    }
+  };
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -478,20 +575,19 @@ __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, cons
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  load_stage(0);
   for (int kk = 0; kk < bw; kk += 32) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = tid + 256 * r, rr = e >> 5, c = e & 31;
-      const int64_t row = r0 + rr;
-      Es[rr][c] = row < n ? w[row * k + b0 + kk + c] : 0.f;
-    }
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = tid + 256 * r, rr = e >> 7, c = e & 127;
-      const int col = c0 + c;
-      Ub[rr][c] = col < k ? (float)u[(int64_t)(b0 + kk + rr) * k + col] : 0.f;
+      for (int c = 0; c < 4; ++c) Es[er + 32 * j][ec + c] = ev[j][c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      Ub[ur + 4 * j][uc] = (float)ua[j];
+      Ub[ur + 4 * j][uc + 1] = (float)ub[j];
     }
     __syncthreads();
+    if (kk + 32 < bw) load_stage(kk + 32);
 #pragma unroll
     for (int q = 0; q < 32; q += 2) {
       const float a0 = Es[wr * 64 + l32][q + lk];
@@ -521,10 +617,10 @@ __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, cons
 template <bool SYM, typename TS>
 hipError_t sweep_blocks(float* w, const double* u, int64_t n, int k, int g, uint8_t* packed, void* scales,
                         void* zeros, hipStream_t st) {
-  const unsigned rows_wg = (unsigned)((n + 15) / 16);
+  const unsigned rows_wg = (unsigned)((n + SWEEP_THREADS - 1) / SWEEP_THREADS);
   for (int b0 = 0; b0 < k; b0 += CB) {
     const int bw = k - b0 < CB ? k - b0 : CB;
-    k_gptq_sweep<SYM, TS><<<rows_wg, 1024, 0, st>>>(w, u, n, k, g, b0, bw, packed, (TS*)scales, (TS*)zeros);
+    k_gptq_sweep<SYM, TS><<<rows_wg, SWEEP_THREADS, 0, st>>>(w, u, n, k, g, b0, bw, packed, (TS*)scales, (TS*)zeros);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int rest = k - b0 - bw;
@@ -555,11 +651,11 @@ hipError_t launch_gptq_inverse_cholesky(double* h, int k, double* u, int* info, 
   const int nt = (k + NB - 1) / NB;
   hipError_t e;
   for (int kb = 0; kb < nt; ++kb) {
-    k_chol_diag<<<1, 256, 0, st>>>(h, k, kb, info);
+    k_chol_diag<<<1, 64, 0, st>>>(h, k, kb, info);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int rest = nt - kb - 1;
     if (rest > 0) {
-      k_chol_panel<<<rest, 64, 0, st>>>(h, k, kb);
+      k_chol_panel<<<rest, 256, 0, st>>>(h, k, kb);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       k_chol_update<<<dim3(rest, rest), 256, 0, st>>>(h, k, kb);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -567,13 +663,19 @@ hipError_t launch_gptq_inverse_cholesky(double* h, int k, double* u, int* info, 
   }
   const int64_t total = (int64_t)k * k;
   const int64_t blocks = (total + 255) / 256;
-  k_zero_lower<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(u, k);
+  k_zero<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(u, total);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_trinv_diag<<<nt, 64, 0, st>>>(h, u, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int ib = 1; ib < nt; ++ib) {
-    k_trinv_row<<<ib, 256, 0, st>>>(h, u, k, ib);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int m = 0; m < nt; ++m) {
+    if (m > 0) {
+      k_trinv_final<<<m, 256, 0, st>>>(u, k, m);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (m < nt - 1) {
+      k_trinv_update<<<dim3(m + 1, nt - m - 1), 256, 0, st>>>(h, u, k, m);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
