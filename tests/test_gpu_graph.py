@@ -25,6 +25,9 @@ def _inputs():
     w = to_dev(WL.bf16_round_bits(rng.normal(0, 0.02, (1100, 4096)).astype(np.float32)), "bf16")
     xs = {m: to_dev(WL.bf16_round_bits(rng.normal(0, 1, (m, 4096)).astype(np.float32)), "bf16")
           for m in (1, 3, 16, 300)}
+    # GPTQ: weight [300, 512] and 700 calibration rows
+    xs["gptq"] = (to_dev(rng.normal(0, 0.05, (300, 512)).astype(np.float32), "f32"),
+                  to_dev(rng.normal(0, 1, (700, 512)).astype(np.float32), "f32"))
     return w, xs
 
 
@@ -34,6 +37,15 @@ def _run(w4, w, xs, outs):
     w4.quantize_pack_int4(w, 128, torch.float16, out=(p, s, z))
     w4.quantize_pack_int4_sym(w, 128, torch.float16, out=outs["qs"])
     for m, x in xs.items():
+        if m == "gptq":
+            wg, xg = x
+            w4.gptq_hessian(xg, out=outs["gh"])
+            outs["ghw"].copy_(outs["gh"])
+            w4.gptq_inverse_cholesky(outs["ghw"], out=outs["gu"], overwrite_h=True, check=False)
+            outs["gwork"].copy_(wg)
+            w4.gptq_quantize_pack_int4(outs["gwork"], outs["gu"], 128, False, torch.float16, overwrite_w=True,
+                                       out=outs["gq"])
+            continue
         w4.w4a16_matmul(x, p, s, z, 128, out=outs[("y", m)])
         xq, xsc = outs[("a", m)]
         w4.quantize_act_int8(x, out=(xq, xsc))
@@ -49,7 +61,16 @@ def _alloc(w, xs):
                   torch.empty((n, k // 128), dtype=torch.float16, device=dev)),
             "d": torch.empty((n, k), dtype=torch.bfloat16, device=dev)}
     outs["qs"] = tuple(torch.empty_like(t) for t in outs["q"])
+    outs["gh"] = torch.empty((512, 512), dtype=torch.float64, device=dev)
+    outs["ghw"] = torch.empty_like(outs["gh"])
+    outs["gu"] = torch.empty_like(outs["gh"])
+    outs["gwork"] = torch.empty((300, 512), dtype=torch.float32, device=dev)
+    outs["gq"] = (torch.empty((300, 256), dtype=torch.uint8, device=dev),
+                  torch.empty((300, 4), dtype=torch.float16, device=dev),
+                  torch.empty((300, 4), dtype=torch.float16, device=dev))
     for m in xs:
+        if m == "gptq":
+            continue
         outs[("y", m)] = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         outs[("y8", m)] = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         outs[("a", m)] = (torch.empty((m, k), dtype=torch.int8, device=dev),
