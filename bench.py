@@ -373,13 +373,16 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
     return out
 
 
-def gptq_setup(torch, np, dev, n=11008, k=4096, t=4096):
+def gptq_arrays(np, n=11008, k=4096, t=4096):
     """Weight [n, k] from N(0, 0.02) and t calibration rows from N(0, 1)
     (synthetic stand-ins for a layer's weight and its input activations)."""
     rng = np.random.default_rng(77)
-    w = torch.from_numpy(rng.normal(0, 0.02, (n, k)).astype(np.float32)).to(dev)
-    x = torch.from_numpy(rng.normal(0, 1, (t, k)).astype(np.float32)).to(dev)
-    return w, x
+    return rng.normal(0, 0.02, (n, k)).astype(np.float32), rng.normal(0, 1, (t, k)).astype(np.float32)
+
+
+def gptq_setup(torch, np, dev, n=11008, k=4096, t=4096):
+    w, x = gptq_arrays(np, n, k, t)
+    return torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev)
 
 
 def gptq_update_flops(n, k, block=128):
@@ -586,6 +589,32 @@ def cpu_baseline(args, WL, np, log, wa, wb):
            "ms_per_step": round(sec * 1e3, 3), "host_cpus": os.cpu_count(),
            "affinity_cpus": len(os.sched_getaffinity(0)), "numpy": np.__version__}
     log(f"cpu baseline: {res['value']} GB/s over {steps} steps")
+    res["gptq"] = gptq_cpu(np, log)
+    return res
+
+
+def gptq_cpu(np, log, rows=64, g=128):
+    """The GPTQ oracle on the benchmark's [11008, 4096] layer with 4096
+    calibration rows: Hessian and factor in full, the sweep on the first
+    `rows` weight rows (rows are independent), scaled linearly to all rows.
+    The scaled figure is a lower bound: the full sweep's working set no
+    longer fits in the host's caches."""
+    import oracle.gptq_oracle as G
+    w, x = gptq_arrays(np)
+    t0 = time.perf_counter()
+    h = G.gptq_hessian(x)
+    t1 = time.perf_counter()
+    u = G.gptq_inverse_cholesky(h)
+    t2 = time.perf_counter()
+    G.gptq_quantize_pack_int4(w[:rows], "f32", u, g, "f16")
+    t3 = time.perf_counter()
+    per_row = (t3 - t2) / rows
+    res = {"hessian_s": round(t1 - t0, 3), "factor_s": round(t2 - t1, 3),
+           "sweep_s_per_row": round(per_row, 5), "sweep_s_all_rows": round(per_row * w.shape[0], 1),
+           "total_s": round((t1 - t0) + (t2 - t1) + per_row * w.shape[0], 1),
+           "sample": f"Hessian and factor in full; the sweep on {rows} of {w.shape[0]} rows, scaled "
+                     f"linearly (a lower bound for the full sweep)"}
+    log(f"gptq oracle: {json.dumps(res)}")
     return res
 
 
