@@ -163,9 +163,9 @@ __global__ __launch_bounds__(64) void k_chol_diag(double* __restrict__ h, int k,
     const double s = (s0 + s1) + (s2 + s3);
     const double d = __shfl(s, j, kWave);
     if (i == 0 && !(d > 0.0) && o + j < k && *info == 0) *info = k - (o + j);
-    const double piv = sqrt(d);
-    if (i == j) a[j] = piv;
-    else if (i > j) a[j] = s / piv;
+    const double r = rsqrt(d);              // pivot sqrt(d) = d r, column scale 1/pivot = r
+    if (i == j) a[j] = d * r;
+    else if (i > j) a[j] = s * r;
     Lr[i][j] = a[j];
     __syncthreads();
   }
@@ -181,6 +181,7 @@ __global__ __launch_bounds__(64) void k_chol_diag(double* __restrict__ h, int k,
 // is split by m mod 4 and its parts combined with two butterflies.
 __global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ h, int k, int kb) {
   __shared__ double L[NB][LDP];
+  __shared__ double rd[NB];
   const int tid = threadIdx.x, r = tid >> 2, sub = tid & 3;
   const int o = kb * NB, ob = (kb + 1 + (int)blockIdx.x) * NB;
   #pragma unroll
@@ -189,6 +190,8 @@ __global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ h, int 
     const int rr = e / NB, c = e % NB;
     L[rr][c] = c <= rr ? view_lower(h, k, o + rr, o + c) : 0.0;
   }
+  __syncthreads();
+  if (tid < NB) rd[tid] = 1.0 / L[tid][tid];
   const bool live = ob + r < k;
   double x[NB / 4];
 #pragma unroll
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ h, int 
       }
     p += __shfl_xor(p, 1, kWave);
     p += __shfl_xor(p, 2, kWave);
-    if (sub == (c & 3)) x[c >> 2] = (x[c >> 2] - p) / L[c][c];
+    if (sub == (c & 3)) x[c >> 2] = (x[c >> 2] - p) * rd[c];
   }
   if (live)
 #pragma unroll
@@ -275,6 +278,7 @@ __global__ __launch_bounds__(64) void k_trinv_diag(const double* __restrict__ h,
                                                    int k) {
   __shared__ double L[NB][LDP];
   __shared__ double X[NB][LDP];
+  __shared__ double rd[NB];
   const int t = threadIdx.x, o = (int)blockIdx.x * NB;
   #pragma unroll
   for (int r_ = 0; r_ < NB * NB / 64; ++r_) {
@@ -282,6 +286,8 @@ __global__ __launch_bounds__(64) void k_trinv_diag(const double* __restrict__ h,
     const int rr = e / NB, c = e % NB;
     L[rr][c] = c <= rr ? view_lower(h, k, o + rr, o + c) : 0.0;
   }
+  __syncthreads();
+  rd[t] = 1.0 / L[t][t];
   __syncthreads();
   for (int r = 0; r < NB; ++r) {
     if (r < t) {
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(64) void k_trinv_diag(const double* __restrict__ h,
       s3 = fma(-L[r][m + 3], X[m + 3][t], s3);
     }
     for (; m < r; ++m) s0 = fma(-L[r][m], X[m][t], s0);
-    X[r][t] = ((s0 + s1) + (s2 + s3)) / L[r][r];
+    X[r][t] = ((s0 + s1) + (s2 + s3)) * rd[r];
   }
   if (o + t < k)
     for (int r = 0; r < NB && o + r < k; ++r) u[rev(k, o + r, o + t)] = X[r][t];
