@@ -98,6 +98,8 @@ SWEEP_CASES = [  # n, k, g, symmetric, sz, calibration rows
     (16, 640, 64, False, "f32", 1000),
     (1, 128, 128, False, "f16", 50),
     (129, 768, 384, True, "f16", 800),     # a group of three blocks
+    (50, 1024, 1024, False, "f16", 300),   # one group per row, eight blocks
+    (300, 96, 32, False, "f32", 40),       # one partial block of 96 columns
 ]
 
 
@@ -179,3 +181,20 @@ def test_llama_gate_shape_sampled_rows(w4):
     p, s, z = (to_host(a)[rows] for a in out)
     _, _, _, stats, _ = G.gptq_quantize(w[rows], uref, g, "f16", False, guide=(p, s, z))
     assert stats["codes_accepted"] <= max(2, 5e-3 * len(rows) * k), stats
+
+
+def test_layer_gptq_sym_bf16(w4):
+    """QuantizedLinear(mode="gptq_sym") from a bf16 weight: the layer quantizes
+    the weight's float32 values; codes checked by the oracle's replay, the
+    forward against the oracle's product of the same codes."""
+    import workloads as WL
+    w, x = _data(256, 512, 400, 9)
+    wb = WL.bf16_round_bits(w)
+    layer = w4.QuantizedLinear.from_weight(to_dev(wb, "bf16"), group_size=64, mode="gptq_sym",
+                                           param=to_dev(x, "f32"))
+    out = (layer.packed, layer.scales, layer.zeros)
+    _replay_ok(O.widen_bf16(wb), G.gptq_inverse_cholesky(G.gptq_hessian(x)), 64, "f16", True, out)
+    xt = WL.bf16_round_bits(np.random.default_rng(2).normal(0, 1, (3, 512)).astype(np.float32))
+    y = layer(to_dev(xt, "bf16")).float().cpu().numpy().astype(np.float64)
+    ref = O.matmul_w4a16_f64(O.widen_bf16(xt), *(to_host(a) for a in out), 64)
+    assert O.max_rel_err(y, ref) <= 1e-2
