@@ -158,7 +158,10 @@ def main(argv=None):
     g = 128
     log("generating Llama-7B decode weights")
     wa, wb = WL.weight("Wa"), WL.weight("Wb")
-    x1 = to_dev(WL.activation(2, 1, 4096))
+    xa1 = WL.activation(2, 1, 4096)
+    x1 = to_dev(xa1)
+    data_sha = {name: hashlib.sha256(np.ascontiguousarray(t.data).tobytes()).hexdigest()[:16]
+                for name, t in (("Wa", wa), ("Wb", wb), ("x", xa1))}
     shapes = {"Wa": (4096, 4096), "Wb": (11008, 4096)}
 
     # quantize once on the GPU, then clone R copies of the packed weights
@@ -218,7 +221,8 @@ def main(argv=None):
                    "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
                    "rotated_weight_copies": R,
                    "rotated_bytes": int(R * sum(sum(a.numel() * a.element_size() for a in q[nm]) for nm in q)),
-                   "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2)},
+                   "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2),
+                   "data_sha256_16": data_sha, "numpy": np.__version__},
         "roofline": roof,
     }
     del q
@@ -370,7 +374,52 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
 
     out["llama7b_decode_32_layers"] = llama_decode(w4, torch, dev, time_region, log, g)
     out["gptq_Wb"] = gptq_bench(w4, torch, np, dev, time_region, log)
+    out["measured_peaks"] = measured_peaks(w4, WL, torch, dev, to_dev, time_region, log, copies, x1, out)
     return out
+
+
+def measured_peaks(w4, WL, torch, dev, to_dev, time_region, log, copies, x1, out, g=128):
+    """Context for the fractions above: the decode product with one weight
+    copy (resident in the 256 MB Infinity Cache, so not an HBM figure), a
+    1 GiB device copy as a measured HBM peak, and the dense bf16 library GEMM
+    (torch.matmul on a dequantized weight, run as a black box) on the M = 2048
+    shape."""
+    res = {}
+    y = torch.empty((1, 11008), dtype=torch.bfloat16, device=dev)
+    p, s, z = copies["Wb"][0]
+    sec = time_region(lambda i: w4.w4a16_matmul(x1, p, s, z, g, out=y), 200)
+    res["decode_Wb_warm"] = {"us": round(sec * 1e6, 3), "GB/s": round(w4a16_bytes(1, 11008, 4096, g) / sec / 1e9, 1),
+                             "note": "one weight copy, cache-resident: not an HBM figure"}
+    src = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    csec = time_region(lambda i: dst.copy_(src), 10)
+    copy_gbs = 2 * src.numel() * 4 / csec / 1e9
+    del src, dst
+    dec = out.get("w4a16_small_batch", {}).get("M=1", {}).get("Wb", {}).get("GB/s")
+    res["hbm_copy_1GiB"] = {"GB/s": round(copy_gbs, 1), "frac_of_8TBs": round(copy_gbs / HBM_PEAK_GBS, 4),
+                            "decode_Wb_frac_of_copy": round(dec / copy_gbs, 4) if dec else None,
+                            "note": "read + write bytes of a plain device-to-device copy"}
+    wd = w4.dequant_int4(*w4.quantize_pack_int4(to_dev(WL.weight("Wb")), g, torch.float16), g,
+                         out_dtype=torch.bfloat16)
+    xm = to_dev(WL.activation(4, 2048, 4096))
+    wt = wd.t()
+    for _ in range(3):                      # the library GEMM is timed eagerly: it cannot be graph-captured
+        torch.matmul(xm, wt)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(xm, wt)
+    e1.record()
+    e1.synchronize()
+    msec = e0.elapsed_time(e1) / 1e3 / 10
+    tflops = 2 * 2048 * 11008 * 4096 / msec / 1e12
+    ours = out.get("w4a16_prefill_m2048", {}).get("Wb", {}).get("TFLOP/s")
+    res["dense_bf16_library_gemm_Wb_m2048"] = {"us": round(msec * 1e6, 1), "TFLOP/s": round(tflops, 1),
+                                               "fused_w4a16_frac_of_it": round(ours / tflops, 4) if ours else None}
+    log(f"measured peaks: {json.dumps(res)}")
+    return res
 
 
 def gptq_arrays(np, n=11008, k=4096, t=4096):
