@@ -136,43 +136,63 @@ __device__ __forceinline__ double view_lower(const double* h, int k, int a, int 
   return a == b ? 1.0 : 0.0;
 }
 
-// Factor the diagonal tile kb in one wave (left-looking): lane i keeps row
-// i of the tile in registers; at step j it forms
-// s_i = A[i][j] - sum_{m<j} L[i][m] L[j][m] with row j of L read from LDS
-// (a broadcast), and the pivot is sqrt(s_j).  info receives 1 + the
-// original column index of the first pivot that is not positive.
-__global__ __launch_bounds__(64) void k_chol_diag(double* __restrict__ h, int k, int kb,
-                                                  int* __restrict__ info) {
-  __shared__ double Lr[NB][LDP];
-  const int i = threadIdx.x, o = kb * NB;
-  if (kb == 0 && i == 0) *info = 0;
+// Factor diagonal tile kb in wave 0 of the calling workgroup (left-looking):
+// lane i keeps row i of the tile (given in T, lower part) in registers; at
+// step j it forms s_i = A[i][j] - sum_{m<j} L[i][m] L[j][m] with row j of L
+// read from Lr (a broadcast), and the pivot is sqrt(s_j).  Every thread of
+// the workgroup must call this (it holds the workgroup's barriers).  info
+// receives 1 + the original column index of the first pivot that is not
+// positive.
+__device__ __forceinline__ void diag_factor(double* __restrict__ h, int k, int kb, int* __restrict__ info,
+                                            const double (*T)[LDP], double (*Lr)[LDP]) {
+  const int i = threadIdx.x & 63, o = kb * NB;
+  const bool w0 = threadIdx.x < 64;
   double a[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) a[c] = c <= i ? view_lower(h, k, o + i, o + c) : 0.0;
+  for (int c = 0; c < NB; ++c) a[c] = (w0 && c <= i) ? T[i][c] : 0.0;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    double s0 = a[j], s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    if (w0) {
+      double s0 = a[j], s1 = 0.0, s2 = 0.0, s3 = 0.0;
 #pragma unroll
-    for (int m = 0; m < j; ++m) {
-      const double l = Lr[j][m];
-      if ((m & 3) == 0) s0 = fma(-a[m], l, s0);
-      else if ((m & 3) == 1) s1 = fma(-a[m], l, s1);
-      else if ((m & 3) == 2) s2 = fma(-a[m], l, s2);
-      else s3 = fma(-a[m], l, s3);
+      for (int m = 0; m < j; ++m) {
+        const double l = Lr[j][m];
+        if ((m & 3) == 0) s0 = fma(-a[m], l, s0);
+        else if ((m & 3) == 1) s1 = fma(-a[m], l, s1);
+        else if ((m & 3) == 2) s2 = fma(-a[m], l, s2);
+        else s3 = fma(-a[m], l, s3);
+      }
+      const double s = (s0 + s1) + (s2 + s3);
+      const double d = __shfl(s, j, kWave);
+      if (i == 0 && !(d > 0.0) && o + j < k && *info == 0) *info = k - (o + j);
+      const double r = rsqrt(d);            // pivot sqrt(d) = d r, column scale 1/pivot = r
+      if (i == j) a[j] = d * r;
+      else if (i > j) a[j] = s * r;
+      Lr[i][j] = a[j];
     }
-    const double s = (s0 + s1) + (s2 + s3);
-    const double d = __shfl(s, j, kWave);
-    if (i == 0 && !(d > 0.0) && o + j < k && *info == 0) *info = k - (o + j);
-    const double r = rsqrt(d);              // pivot sqrt(d) = d r, column scale 1/pivot = r
-    if (i == j) a[j] = d * r;
-    else if (i > j) a[j] = s * r;
-    Lr[i][j] = a[j];
     __syncthreads();
   }
-  if (o + i < k)
+  if (w0 && o + i < k)
 #pragma unroll
     for (int c = 0; c < NB; ++c)
       if (c <= i) h[rev(k, o + i, o + c)] = a[c];
+}
+
+// The first diagonal tile (later ones are factored by k_chol_update).
+__global__ __launch_bounds__(64) void k_chol_diag(double* __restrict__ h, int k, int kb,
+                                                  int* __restrict__ info) {
+  __shared__ double T[NB][LDP];
+  __shared__ double Lr[NB][LDP];
+  const int t = threadIdx.x, o = kb * NB;
+  if (kb == 0 && t == 0) *info = 0;
+#pragma unroll
+  for (int r_ = 0; r_ < NB * NB / 64; ++r_) {
+    const int e = t + 64 * r_;
+    const int r = e / NB, c = e % NB;
+    T[r][c] = c <= r ? view_lower(h, k, o + r, o + c) : 0.0;
+  }
+  __syncthreads();
+  diag_factor(h, k, kb, info, T, Lr);
 }
 
 // Panel: the tiles below diagonal tile kb, X L_kk^T = A, one tile row per
@@ -222,7 +242,10 @@ __global__ __launch_bounds__(256) void k_chol_panel(double* __restrict__ h, int 
 }
 
 // Trailing update: tile (ib, jb), kb < jb <= ib, minus L_ib,kb L_jb,kb^T.
-__global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ h, int k, int kb) {
+// The workgroup of tile (kb+1, kb+1) then factors that tile at once (the
+// next step's diagonal), while the others are still updating theirs.
+__global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ h, int k, int kb,
+                                                     int* __restrict__ info) {
   const int ib = kb + 1 + (int)blockIdx.y, jb = kb + 1 + (int)blockIdx.x;
   if (jb > ib) return;
   __shared__ double Li[NB][LDP];
@@ -255,16 +278,24 @@ __global__ __launch_bounds__(256) void k_chol_update(double* __restrict__ h, int
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
   }
+  const bool next_diag = ib == kb + 1 && jb == kb + 1;
+  if (next_diag) __syncthreads();           // Li is reused for the updated tile
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int r = ty + 16 * a, q = tx + 16 * b;
-      if (oi + r < k && oj + q < k && (ib != jb || q <= r)) {
+      if (next_diag) {
+        if (q <= r) Li[r][q] = view_lower(h, k, oi + r, oi + q) - acc[a][b];
+      } else if (oi + r < k && oj + q < k && (ib != jb || q <= r)) {
         const int64_t p = rev(k, oi + r, oj + q);
         h[p] = h[p] - acc[a][b];
       }
     }
+  if (next_diag) {
+    __syncthreads();
+    diag_factor(h, k, ib, info, Li, Lj);
+  }
 }
 
 // u = 0: the strictly lower part of U, and the accumulators of the inverse.
@@ -313,7 +344,7 @@ __global__ __launch_bounds__(64) void k_trinv_diag(const double* __restrict__ h,
 // X_ij = -X_ii B_ij with B_ij = sum_{m=j}^{i-1} L_im X_mj.  B accumulates in
 // u at X's place: when block row m is final, every later block row ib gets
 // L_ib,m X_m,j added for all j <= m (k_trinv_update, many tiles at once),
-// and block row m + 1 is finalized (k_trinv_final).
+// and block row m + 1, now complete, is finished in the same launch.
 __device__ __forceinline__ void tile_mma(const double (*A)[LDP], const double (*B)[LDP], int tx, int ty,
                                          double acc[4][4]) {
 #pragma unroll 4
@@ -330,7 +361,9 @@ __device__ __forceinline__ void tile_mma(const double (*A)[LDP], const double (*
   }
 }
 
-// B_ib,j += L_ib,m X_m,j for ib = m+1+blockIdx.y, j = blockIdx.x <= m.
+// B_ib,j += L_ib,m X_m,j for ib = m+1+blockIdx.y, j = blockIdx.x <= m.  The
+// workgroups of block row m+1, whose sums are then complete, finish their
+// tile in place: X_m+1,j = -X_m+1,m+1 B_m+1,j.
 __global__ __launch_bounds__(256) void k_trinv_update(const double* __restrict__ h, double* __restrict__ u,
                                                       int k, int m) {
   __shared__ double A[NB][LDP];
@@ -352,34 +385,34 @@ __global__ __launch_bounds__(256) void k_trinv_update(const double* __restrict__
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
   tile_mma(A, B, tx, ty, acc);
+  if (ib != m + 1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int r = ty + 16 * a, q = tx + 16 * b;
+        if (oi + r < k && oj + q < k) {
+          const int64_t p = rev(k, oi + r, oj + q);
+          u[p] = u[p] + acc[a][b];
+        }
+      }
+    return;
+  }
+  __syncthreads();                          // A and B are reused
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int r = ty + 16 * a, q = tx + 16 * b;
-      if (oi + r < k && oj + q < k) {
-        const int64_t p = rev(k, oi + r, oj + q);
-        u[p] = u[p] + acc[a][b];
-      }
+      B[r][q] = (oi + r < k && oj + q < k) ? u[rev(k, oi + r, oj + q)] + acc[a][b] : 0.0;
     }
-}
-
-// X_m,j = -X_mm B_m,j for j = blockIdx.x < m (in place).
-__global__ __launch_bounds__(256) void k_trinv_final(double* __restrict__ u, int k, int m) {
-  __shared__ double A[NB][LDP];
-  __shared__ double B[NB][LDP];
-  const int jb = blockIdx.x;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int om = m * NB, oj = jb * NB;
   #pragma unroll
   for (int r_ = 0; r_ < NB * NB / 256; ++r_) {
     const int e = tid + 256 * r_;
     const int rr = e / NB, c = e % NB;
-    A[rr][c] = (c <= rr && om + rr < k && om + c < k) ? u[rev(k, om + rr, om + c)] : 0.0;
-    B[rr][c] = (om + rr < k && oj + c < k) ? u[rev(k, om + rr, oj + c)] : 0.0;
+    A[rr][c] = (c <= rr && oi + rr < k && oi + c < k) ? u[rev(k, oi + rr, oi + c)] : 0.0;
   }
   __syncthreads();
-  double acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -390,7 +423,7 @@ __global__ __launch_bounds__(256) void k_trinv_final(double* __restrict__ u, int
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int r = ty + 16 * a, q = tx + 16 * b;
-      if (om + r < k && oj + q < k) u[rev(k, om + r, oj + q)] = -acc[a][b];
+      if (oi + r < k && oj + q < k) u[rev(k, oi + r, oj + q)] = -acc[a][b];
     }
 }
 
@@ -656,16 +689,14 @@ hipError_t launch_gptq_hessian(const float* x, int64_t t, int k, double* h, hipS
 hipError_t launch_gptq_inverse_cholesky(double* h, int k, double* u, int* info, hipStream_t st) {
   const int nt = (k + NB - 1) / NB;
   hipError_t e;
-  for (int kb = 0; kb < nt; ++kb) {
-    k_chol_diag<<<1, 64, 0, st>>>(h, k, kb, info);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_chol_diag<<<1, 64, 0, st>>>(h, k, 0, info);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int kb = 0; kb + 1 < nt; ++kb) {   // the update of step kb factors diagonal tile kb + 1
     const int rest = nt - kb - 1;
-    if (rest > 0) {
-      k_chol_panel<<<rest, 256, 0, st>>>(h, k, kb);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      k_chol_update<<<dim3(rest, rest), 256, 0, st>>>(h, k, kb);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    k_chol_panel<<<rest, 256, 0, st>>>(h, k, kb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_chol_update<<<dim3(rest, rest), 256, 0, st>>>(h, k, kb, info);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t total = (int64_t)k * k;
   const int64_t blocks = (total + 255) / 256;
@@ -673,15 +704,9 @@ hipError_t launch_gptq_inverse_cholesky(double* h, int k, double* u, int* info, 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_trinv_diag<<<nt, 64, 0, st>>>(h, u, k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  for (int m = 0; m < nt; ++m) {
-    if (m > 0) {
-      k_trinv_final<<<m, 256, 0, st>>>(u, k, m);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (m < nt - 1) {
-      k_trinv_update<<<dim3(m + 1, nt - m - 1), 256, 0, st>>>(h, u, k, m);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+  for (int m = 0; m + 1 < nt; ++m) {       // step m also finishes block row m + 1
+    k_trinv_update<<<dim3(m + 1, nt - m - 1), 256, 0, st>>>(h, u, k, m);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
