@@ -40,6 +40,8 @@ INT8_PEAK_TOPS = 5000.0
 # an FMA as two flops, so 78.6 T fp32 lane-instructions per second (256 CUs x
 # 4 SIMDs x 32 fp32 lanes per cycle x 2.4 GHz)
 VALU_PEAK_TOPS = 157.3 / 2
+FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector (and matrix) peak
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X dense float32 matrix peak
 
 
 # ---------------------------------------------------------------------------
@@ -467,9 +469,11 @@ def gptq_bench(w4, torch, np, dev, time_region, log, n=11008, k=4096, t=4096, g=
     res = {"shape": [n, k], "calibration_rows": t, "group": g,
            "hessian_ms": round(hsec * 1e3, 3),
            "hessian_fp64_TFLOP/s": round(t * k * k / hsec / 1e12, 2),
+           "hessian_frac_fp64_peak": round(t * k * k / hsec / 1e12 / FP64_PEAK_TFLOPS, 4),
            "inverse_cholesky_ms": round(usec * 1e3, 3),
            "sweep_ms": round(ssec * 1e3, 3),
            "sweep_update_TFLOP/s": round(upd / ssec / 1e12, 2),
+           "sweep_frac_fp32_matrix_peak": round(upd / ssec / 1e12 / FP32_MATRIX_PEAK_TFLOPS, 4),
            "total_ms": round((hsec + usec + ssec) * 1e3, 3)}
     log(f"gptq: {json.dumps(res)}")
     return res
