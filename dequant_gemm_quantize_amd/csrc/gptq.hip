@@ -18,9 +18,8 @@
 //     the later columns as w_j -= e * U[i, j].  Columns go in blocks of 128
 //     (the lazy-batch form of the method): one kernel runs the sequential
 //     part inside a block, one lane per weight row, with U's diagonal block
-//     in LDS; a float32 MFMA
-//     kernel then applies the block's errors to every later column at once,
-//     W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:].
+//     in LDS; a float32 MFMA kernel then applies the block's errors to every
+//     later column at once, W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:].
 //
 // Integer decisions (codes, zero-points, scales) use the same float32 steps
 // as the round-to-nearest quantizer; contraction into FMA is switched off in
