@@ -570,7 +570,8 @@ __global__ __launch_bounds__(SWEEP_THREADS) void k_gptq_sweep(float* __restrict_
 // W[:, b1:] -= E[:, b0:b1] * U[b0:b1, b1:] with b1 = b0 + bw, float32 MFMA.
 // Workgroup tile 128 rows x 128 columns, four waves of 64 x 64 (2 x 2
 // v_mfma_f32_32x32x2f32 tiles), K = bw in LDS stages of 32; the next stage's
-// global loads are issued before the current stage's MFMAs.
+// global loads are issued before the current stage's MFMAs, and the output
+// tile's current values are loaded up front.
 __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, const double* __restrict__ u,
                                                      int64_t n, int k, int b0, int bw) {
   __shared__ float Es[128][33];
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, cons
       }
     }
   };
-  f32x16 acc[2][2];
+  f32x16 acc[2][2], wold[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -614,6 +615,17 @@ __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, cons
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   load_stage(0);
+  // the output tile's current values, read while the stages are multiplied
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = r0 + wr * 64 + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int col = c0 + wc * 64 + 32 * j + l32;
+        wold[i][j][r] = (row < n && col < k) ? w[row * k + col] : 0.f;
+      }
   for (int kk = 0; kk < bw; kk += 32) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -648,7 +660,7 @@ __global__ __launch_bounds__(256) void k_gptq_update(float* __restrict__ w, cons
       for (int r = 0; r < 16; ++r) {
         const int64_t row = r0 + wr * 64 + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
         const int col = c0 + wc * 64 + 32 * j + l32;
-        if (row < n && col < k) w[row * k + col] -= acc[i][j][r];
+        if (row < n && col < k) w[row * k + col] = wold[i][j][r] - acc[i][j][r];
       }
 }
 
