@@ -505,7 +505,7 @@ __global__ __launch_bounds__(SWEEP_THREADS) void k_gptq_sweep(float* __restrict_
     }
   }
   __syncthreads();
-  if (tid < CB) rdiag[tid] = tid < bw ? 1.f / Us[tid][tid] : 0.f;
+  for (int i = tid; i < CB; i += SWEEP_THREADS) rdiag[i] = i < bw ? 1.f / Us[i][i] : 0.f;
   __syncthreads();
   const int64_t row = (int64_t)blockIdx.x * SWEEP_THREADS + tid;
   if (row >= n) return;
