@@ -105,6 +105,44 @@ def _dtype_code(dt: torch.dtype) -> int:
     return _DT[dt]
 
 
+# Shape and dtype checks.  The C ABI sees only pointers and sizes, so a
+# tensor of the wrong shape or dtype would be read or written out of bounds
+# there; the wrappers, which know every tensor's size, refuse such calls
+# before anything reaches the library.
+def _expect(t: torch.Tensor, name: str, shape, dtypes) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} has dtype {str(t.dtype).replace('torch.', '')}, expected {names}")
+
+
+def _matrix(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor, got {t.dim()} dimensions")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _ngroups(k: int, group_size: int) -> int:
+    if group_size <= 0 or k % group_size:
+        raise ValueError(f"K = {k} is not a multiple of group_size = {group_size}")
+    return k // group_size
+
+
+SZ_DTYPES = (torch.float16, torch.float32)
+
+
+def _check_weights(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, k: int,
+                   group_size: int) -> int:
+    """packed uint8 [N, K/2], scales and zeros [N, K/g] of one dtype; returns N."""
+    n = _matrix(packed, "packed")[0]
+    _expect(packed, "packed", (n, k // 2), (torch.uint8,))
+    ng = _ngroups(k, group_size)
+    _expect(scales, "scales", (n, ng), SZ_DTYPES)
+    _expect(zeros, "zeros", (n, ng), (scales.dtype,))
+    return n
+
+
 # ---------------------------------------------------------------------------
 # Public wrappers (same names as the C ABI)
 # ---------------------------------------------------------------------------
@@ -143,6 +181,8 @@ def gptq_hessian(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.T
     if x.dtype != torch.float32 or x.dim() != 2:
         raise ValueError("x must be a float32 [T, K] tensor")
     t, k = x.shape
+    if out is not None:
+        _expect(out, "out", (k, k), (torch.float64,))
     dev = _gpu(x)
     h = torch.empty((k, k), dtype=torch.float64, device=dev) if out is None else out
     _gpu(h)
@@ -159,6 +199,8 @@ def gptq_inverse_cholesky(h: torch.Tensor, out: Optional[torch.Tensor] = None, o
     if h.dtype != torch.float64 or h.dim() != 2 or h.shape[0] != h.shape[1]:
         raise ValueError("h must be a square float64 tensor")
     k = h.shape[0]
+    if out is not None:
+        _expect(out, "out", (k, k), (torch.float64,))
     dev = _gpu(h)
     work = h if overwrite_h else h.clone()
     u = torch.empty((k, k), dtype=torch.float64, device=dev) if out is None else out
@@ -184,6 +226,9 @@ def gptq_quantize_pack_int4(w: torch.Tensor, u: torch.Tensor, group_size: int, s
     if u.dtype != torch.float64 or tuple(u.shape) != (w.shape[1], w.shape[1]):
         raise ValueError("u must be a float64 [K, K] tensor")
     n, k = w.shape
+    ng = _ngroups(k, group_size)
+    if out is not None:
+        _check_out3(out, n, k, ng)
     dev = _gpu(w, u)
     work = w if overwrite_w else w.clone()
     if out is None:
@@ -199,8 +244,22 @@ def gptq_quantize_pack_int4(w: torch.Tensor, u: torch.Tensor, group_size: int, s
     return packed, scales, zeros
 
 
+def _check_out3(out, n: int, k: int, ng: int) -> None:
+    packed, scales, zeros = out
+    _expect(packed, "packed", (n, k // 2), (torch.uint8,))
+    _expect(scales, "scales", (n, ng), SZ_DTYPES)
+    _expect(zeros, "zeros", (n, ng), (scales.dtype,))
+
+
 def _quantize_pack(fn, w, group_size, sz_dtype, out):
-    n, k = w.shape
+    n, k = _matrix(w, "w")
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"w has dtype {w.dtype}, expected float32 or bfloat16")
+    ng = _ngroups(k, group_size)
+    if out is not None:
+        _check_out3(out, n, k, ng)
+    elif sz_dtype not in SZ_DTYPES:
+        raise ValueError(f"sz_dtype must be float16 or float32, got {sz_dtype}")
     dev = _gpu(w)
     if out is None:
         packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
@@ -218,11 +277,12 @@ def dequant_int4(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor
                  out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
     """(packed, scales, zeros) -> dequantized W [N, K] in out_dtype."""
     lib = load()
-    n, half = packed.shape
+    n, half = _matrix(packed, "packed")
     k = 2 * half
+    _check_weights(packed, scales, zeros, k, group_size)
+    if out is not None:
+        _expect(out, "out", (n, k), tuple(_DT))
     dev = _gpu(packed, scales, zeros)
-    if scales.dtype != zeros.dtype:
-        raise ValueError("scales and zeros must share a dtype")
     w = torch.empty((n, k), dtype=out_dtype, device=dev) if out is None else out
     _gpu(w)
     _check(lib.dequant_int4(_ptr(packed), _ptr(scales), _ptr(zeros), _dtype_code(scales.dtype), n, k,
@@ -233,7 +293,12 @@ def dequant_int4(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor
 def quantize_act_int8(x: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     """x [M, K] (fp32 or bf16) -> (xq int8 [M, K], x_scale float32 [M])."""
     lib = load()
-    m, k = x.shape
+    m, k = _matrix(x, "x")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x has dtype {x.dtype}, expected float32 or bfloat16")
+    if out is not None:
+        _expect(out[0], "xq", (m, k), (torch.int8,))
+        _expect(out[1], "x_scale", (m,), (torch.float32,))
     dev = _gpu(x)
     if out is None:
         xq = torch.empty((m, k), dtype=torch.int8, device=dev)
@@ -250,10 +315,14 @@ def w4a16_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, ze
                  out: Optional[torch.Tensor] = None):
     """y [M, N] = x [M, K] . dequant(W)^T; out_dtype defaults to x's dtype."""
     lib = load()
-    m, k = x.shape
-    n = packed.shape[0]
-    if packed.shape[1] * 2 != k:
+    m, k = _matrix(x, "x")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"x has dtype {x.dtype}, expected float32 or bfloat16")
+    if _matrix(packed, "packed")[1] * 2 != k:
         raise ValueError(f"packed has {packed.shape[1] * 2} columns of codes, x has K={k}")
+    n = _check_weights(packed, scales, zeros, k, group_size)
+    if out is not None:
+        _expect(out, "out", (m, n), (torch.float32, torch.bfloat16))
     dev = _gpu(x, packed, scales, zeros)
     y = torch.empty((m, n), dtype=out_dtype or x.dtype, device=dev) if out is None else out
     _gpu(y)
@@ -268,10 +337,14 @@ def w4a8_matmul(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, s
                 out: Optional[torch.Tensor] = None):
     """y [M, N] = x_scale[m] * (xq [M, K] . dequant(W)^T)."""
     lib = load()
-    m, k = xq.shape
-    n = packed.shape[0]
-    if packed.shape[1] * 2 != k:
+    m, k = _matrix(xq, "xq")
+    _expect(xq, "xq", (m, k), (torch.int8,))
+    _expect(x_scale, "x_scale", (m,), (torch.float32,))
+    if _matrix(packed, "packed")[1] * 2 != k:
         raise ValueError(f"packed has {packed.shape[1] * 2} columns of codes, xq has K={k}")
+    n = _check_weights(packed, scales, zeros, k, group_size)
+    if out is not None:
+        _expect(out, "out", (m, n), (torch.float32, torch.bfloat16))
     dev = _gpu(xq, x_scale, packed, scales, zeros)
     y = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
     _gpu(y)

@@ -35,6 +35,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxK = (int64_t)1 << 23;      // columns
 constexpr int64_t kMaxElems = (int64_t)1 << 36;  // n*k, m*k, m*n
+constexpr int64_t kMaxActTokens = (int64_t)1 << 24;  // quantize_act_int8: m < 2^24
 
 // Shared checks of the weight-side arguments (shape, group, scale dtype).
 int check_weights(const char* fn, int64_t n, int64_t k, int32_t g, int sz_dtype) {
@@ -47,7 +48,8 @@ int check_weights(const char* fn, int64_t n, int64_t k, int32_t g, int sz_dtype)
   if (sz_dtype != W4_F32 && sz_dtype != W4_F16)
     return fail(W4_EINVAL, "%s: scale dtype %d must be W4_F32 or W4_F16", fn, sz_dtype);
   // Size limits that keep every kernel's 32-bit tile offsets (up to 256 rows
-  // of K elements) and launch sizes (under 2^32 work-items) in range.
+  // of K elements) and launch sizes (under 2^32 work-items) in range for the
+  // weight-side launches; quantize_act_int8 bounds its token count itself.
   if (k > kMaxK)
     return fail(W4_EINVAL, "%s: k = %lld is too large (at most %lld)", fn, (long long)k,
                 (long long)kMaxK);
@@ -237,6 +239,11 @@ int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
     return fail(W4_EINVAL, "%s: k = %lld is too large (at most %lld)", fn, (long long)k,
                 (long long)kMaxK);
   W4_TRY(check_tokens(fn, m, k, 0));
+  // One workgroup of up to 1024 (m < 64) or 256 work-items per token: below
+  // 2^24 tokens the launch stays under 2^32 work-items.
+  if (m >= kMaxActTokens)
+    return fail(W4_EINVAL, "%s: m = %lld is too large (at most %lld tokens)", fn, (long long)m,
+                (long long)(kMaxActTokens - 1));
   if (m == 0) return ok();
   W4_TRY(check_ptr(fn, "x", x));
   W4_TRY(check_ptr(fn, "xq", xq));

@@ -4,10 +4,14 @@
 // Math ("Building a From-Scratch Group-Wise INT4 Quantization Layer for
 // LLaMA Weights", Step 2, with the dequantization of "From Scratch: Building
 // a GPTQ INT4 Quantizer in Pure Python", Step 4): every weight tile is
-// dequantized once per workgroup to bf16, w = RNE((q - zp) * s) -- computed
-// as fma(q, s, -zp*s), exact in fp32 before the one rounding -- and written
-// to LDS, where it feeds v_mfma_f32_32x32x16_bf16 together with the
-// activation tile.  No dequantized matrix ever reaches memory.
+// dequantized once per workgroup to bf16 as fma(q, s, -zp*s) and written to
+// LDS, where it feeds v_mfma_f32_32x32x16_bf16 together with the activation
+// tile.  No dequantized matrix ever reaches memory.  With fp16 scales, q*s
+// and zp*s are exact in fp32 (4 + 11 significant bits), so the weight is
+// RNE((q - zp) * s) with one rounding.  With fp32 scales zp*s is itself
+// rounded, so a weight can differ from that by one bf16 step where the exact
+// product sits at a bf16 tie; the accuracy bound of the product holds either
+// way.
 //
 // Tiling.  Workgroup tile 256 (M) x 128 (N), K in steps of 64, both operand
 // tiles double-buffered in LDS (rows padded by 16 bytes).  Eight waves (two

@@ -34,7 +34,13 @@ def _gptq(w: torch.Tensor, g: int, sz: torch.dtype, x: Optional[torch.Tensor], s
         raise ValueError("GPTQ modes need the calibration rows X [T, in_features] as param")
     h = _lib.gptq_hessian(x.reshape(-1, x.shape[-1]).to(torch.float32).contiguous())
     u = _lib.gptq_inverse_cholesky(h, overwrite_h=True)
-    return _lib.gptq_quantize_pack_int4(w.to(torch.float32).contiguous(), u, g, symmetric, sz, overwrite_w=True)
+    # The sweep uses its weight argument as working storage.  A float32
+    # contiguous weight converts to itself, so the sweep may take it over
+    # only when the conversion made a copy; otherwise the wrapper copies it
+    # and the caller's weight (possibly a tied parameter) is left unchanged.
+    wf = w.to(torch.float32).contiguous()
+    owned = wf.data_ptr() != w.data_ptr()
+    return _lib.gptq_quantize_pack_int4(wf, u, g, symmetric, sz, overwrite_w=owned)
 
 
 class QuantizedLinear(torch.nn.Module):

@@ -36,7 +36,7 @@
  *  - M == 0 or N == 0 is a valid empty call: it returns W4_OK and enqueues
  *    nothing.  K must be > 0.
  *  - Size limits (W4_EINVAL beyond them): K <= 2^23; N*K, M*K and M*N each
- *    <= 2^36 elements; M < 2^31.
+ *    <= 2^36 elements; M < 2^31 (M < 2^24 for quantize_act_int8).
  *  - Inputs must be finite; NaN or Inf inputs, and group ranges that overflow
  *    the scale dtype (fp16 scales: (max - min) / 15 > 65504), give unspecified
  *    (but memory-safe) results.
@@ -147,7 +147,8 @@ int dequant_int4(const uint8_t* packed, const void* scales, const void* zeros, i
  *   x_scale[m] = max(max_k |x[m, k]|, 1e-8) / 127
  *   xq[m, k]   = clamp(rint(x[m, k] / x_scale[m]), -128, 127)
  *   x        [M, K] input, x_dtype W4_F32 or W4_BF16; K % 8 == 0
- *   xq       [M, K] int8 output;  x_scale [M] float32 output.
+ *   xq       [M, K] int8 output;  x_scale [M] float32 output (4-byte aligned).
+ *   M < 2^24 tokens (W4_EINVAL otherwise).
  * Bit-exact.
  */
 int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* xq,

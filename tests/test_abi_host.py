@@ -245,3 +245,75 @@ def test_gptq_quantize_rejects(lib, args, msg):
 
 def test_gptq_empty_sweep_is_noop(lib):
     assert lib.gptq_quantize_pack_int4(None, None, 0, 256, 128, 0, None, None, None, 1, None) == 0
+
+
+def _cpu_weights(n=8, k=256, g=128, sz=None, zsz=None):
+    import torch
+    sz = sz or torch.float16
+    return (torch.zeros(n, k // 2, dtype=torch.uint8), torch.ones(n, k // g, dtype=sz),
+            torch.zeros(n, k // g, dtype=zsz or sz))
+
+
+def test_binding_checks_shapes_and_dtypes():
+    """The wrappers refuse tensors whose shape or dtype does not match the
+    call before anything reaches the library (the C ABI cannot see sizes, so
+    such a call would read or write out of bounds there)."""
+    import torch
+    import dequant_gemm_quantize_amd as w4
+    bf = torch.bfloat16
+    p, s, z = _cpu_weights()
+    x = torch.zeros(3, 256, dtype=bf)
+    cases = [
+        # w4a16_matmul
+        (lambda: w4.w4a16_matmul(x, p, s, z, 128, out=torch.zeros(3, 9, dtype=bf)), "out has shape"),
+        (lambda: w4.w4a16_matmul(x, p, s, z, 128, out=torch.zeros(3, 8, dtype=torch.float16)), "out has dtype"),
+        (lambda: w4.w4a16_matmul(x, p, s[:, :1], z, 128), "scales has shape"),
+        (lambda: w4.w4a16_matmul(x, p, s, z, 64), "scales has shape"),
+        (lambda: w4.w4a16_matmul(x, p, s, z.float(), 128), "zeros has dtype"),
+        (lambda: w4.w4a16_matmul(x, p, s.to(bf), z.to(bf), 128), "scales has dtype"),
+        (lambda: w4.w4a16_matmul(x, p.to(torch.int8), s, z, 128), "packed has dtype"),
+        (lambda: w4.w4a16_matmul(x, p, s, z, 96), "not a multiple of group_size"),
+        (lambda: w4.w4a16_matmul(x.to(torch.float16), p, s, z, 128), "x has dtype"),
+        (lambda: w4.w4a16_matmul(x[0], p, s, z, 128), "x must be a 2-D"),
+        # w4a8_matmul
+        (lambda: w4.w4a8_matmul(torch.zeros(3, 256, dtype=torch.uint8), torch.ones(3), p, s, z, 128),
+         "xq has dtype"),
+        (lambda: w4.w4a8_matmul(torch.zeros(3, 256, dtype=torch.int8), torch.ones(2), p, s, z, 128),
+         "x_scale has shape"),
+        (lambda: w4.w4a8_matmul(torch.zeros(3, 256, dtype=torch.int8), torch.ones(3, dtype=torch.float64),
+                                p, s, z, 128), "x_scale has dtype"),
+        (lambda: w4.w4a8_matmul(torch.zeros(3, 256, dtype=torch.int8), torch.ones(3), p, s, z, 128,
+                                out=torch.zeros(8, 3, dtype=bf)), "out has shape"),
+        # dequant_int4
+        (lambda: w4.dequant_int4(p, s, z, 128, out=torch.zeros(8, 128, dtype=bf)), "out has shape"),
+        (lambda: w4.dequant_int4(p, s, z.float(), 128), "zeros has dtype"),
+        # quantizers
+        (lambda: w4.quantize_pack_int4(torch.zeros(8, 256), 128, out=(p, s, z[:4])), "zeros has shape"),
+        (lambda: w4.quantize_pack_int4(torch.zeros(8, 256), 128, out=(p[:, :64], s, z)), "packed has shape"),
+        (lambda: w4.quantize_pack_int4(torch.zeros(8, 256), 100), "not a multiple of group_size"),
+        (lambda: w4.quantize_pack_int4(torch.zeros(8, 256, dtype=torch.float16), 128), "w has dtype"),
+        (lambda: w4.quantize_pack_int4(torch.zeros(8, 256), 128, torch.bfloat16), "sz_dtype must be"),
+        (lambda: w4.quantize_pack_int4_sym_mse(torch.zeros(8, 256), 128, 10, out=(p, s, z.float())),
+         "zeros has dtype"),
+        # activations
+        (lambda: w4.quantize_act_int8(x, out=(torch.zeros(3, 256, dtype=torch.int8), torch.zeros(4))),
+         "x_scale has shape"),
+        (lambda: w4.quantize_act_int8(x, out=(torch.zeros(3, 128, dtype=torch.int8), torch.zeros(3))),
+         "xq has shape"),
+        # GPTQ
+        (lambda: w4.gptq_hessian(torch.zeros(5, 64), out=torch.zeros(64, 64)), "out has dtype"),
+        (lambda: w4.gptq_hessian(torch.zeros(5, 64), out=torch.zeros(64, 32, dtype=torch.float64)),
+         "out has shape"),
+        (lambda: w4.gptq_inverse_cholesky(torch.eye(64, dtype=torch.float64),
+                                          out=torch.zeros(63, 63, dtype=torch.float64)), "out has shape"),
+        (lambda: w4.gptq_quantize_pack_int4(torch.zeros(8, 256), torch.eye(256, dtype=torch.float64), 128,
+                                            out=(p, s[:, :1], z)), "scales has shape"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn()
+    # well-formed CPU tensors pass every check and are then refused for the device
+    with pytest.raises(ValueError, match="GPU only"):
+        w4.w4a16_matmul(x, p, s, z, 128)
+    with pytest.raises(ValueError, match="GPU only"):
+        w4.w4a8_matmul(torch.zeros(3, 256, dtype=torch.int8), torch.ones(3), p, s, z, 128)

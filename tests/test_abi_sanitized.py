@@ -72,6 +72,8 @@ int main() {
   expect(dequant_int4(P, A, A, W4_F16, BIG, BIG, 128, A, W4_BF16, nullptr), W4_EINVAL, "dq huge");
   expect(quantize_act_int8(A, W4_BF16, 3, 256, (int8_t*)A, (float*)A, nullptr), W4_OK, "act ok");
   expect(quantize_act_int8(A, W4_BF16, BIG, 256, (int8_t*)A, (float*)A, nullptr), W4_EINVAL, "act huge");
+  expect(quantize_act_int8(A, W4_BF16, (1LL << 24) - 1, 8, (int8_t*)A, (float*)A, nullptr), W4_OK, "act m max");
+  expect(quantize_act_int8(A, W4_BF16, 1LL << 24, 8, (int8_t*)A, (float*)A, nullptr), W4_EINVAL, "act m 2^24");
   for (int64_t m : {1, 3, 16, 64, 100, 2048})
     expect(w4a16_matmul(A, W4_BF16, m, 4096, P, A, A, W4_F16, 11008, 128, A, W4_BF16, nullptr), W4_OK, "w4a16 ok");
   expect(w4a16_matmul(A, W4_F32, 5, 256, P, A, A, W4_F32, 96, 32, A, W4_F32, nullptr), W4_OK, "w4a16 f32");

@@ -88,3 +88,26 @@ def test_replace_linears(w4):
         ref = O.matmul_w4a16_f64(O.widen_bf16(to_host(h)), P, S, Z, 128)
         h = model[i](h)
         assert O.max_rel_err(y_as_f64(h), ref) <= 1e-2
+
+
+@pytest.mark.parametrize("mode", ["gptq", "gptq_sym"])
+def test_layer_gptq_leaves_weight_unchanged(w4, mode):
+    """The GPTQ sweep uses its weight argument as working storage; a float32
+    contiguous weight (the usual nn.Linear case, possibly a tied parameter)
+    must come out of from_weight / replace_linears bit for bit unchanged."""
+    n, k, g = 64, 256, 64
+    rng = np.random.default_rng(65)
+    w = rng.normal(0, 0.05, (n, k)).astype(np.float32)
+    x = to_dev(rng.normal(0, 1, (300, k)).astype(np.float32), "f32")
+    wt = to_dev(w, "f32")
+    w4.QuantizedLinear.from_weight(wt, group_size=g, mode=mode, param=x)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(wt).view(np.uint32), w.view(np.uint32))
+    lin = torch.nn.Linear(k, n, bias=False).cuda()
+    with torch.no_grad():
+        lin.weight.copy_(wt)
+    model = torch.nn.Sequential(lin)
+    w4.replace_linears(model, group_size=g, mode=mode, param=x)
+    torch.cuda.synchronize()
+    assert type(model[0]).__name__ == "QuantizedLinear"
+    assert np.array_equal(to_host(lin.weight.detach()).view(np.uint32), w.view(np.uint32))
