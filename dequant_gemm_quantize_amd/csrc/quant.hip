@@ -367,17 +367,28 @@ hipError_t launch_quantize_pack(const void* w, int w_dtype, int64_t n, int64_t k
 // above with the stored scale.  One wave per group (g <= 1024); the group's
 // values sit in the wave's own LDS region, which needs no barrier (LDS
 // operations of a wave complete in order).
-//   MODE_PCT: range = the p-th percentile of |w|, linear between the order
-//     statistics i0 and i1 = min(i0 + 1, g - 1) with weight f (host values
-//     from h = (g - 1) p / 100); scale = range / 7.  The order statistics are
-//     read from a bitonic sort of |w| in LDS (equal values are equal, so the
-//     order of ties does not matter).
-//   MODE_MSE: candidate steps c_i = lo + i d, d = (hi - lo) / (n - 1), from
-//     min|w| to max|w|; c < 1e-10 is skipped; codes clamp(rint(w * (1/c)),
-//     -7, 7); error sum over the group in column order, fp32; the first
-//     least sum wins (a 64-bit key of the sum's bits and the index; sums are
+//   MODE_PCT: range = the p-th percentile of |w| as torch.quantile computes
+//     it in float32: the sorted order statistics i0 = floor(rank) and
+//     i1 = ceil(rank), rank = fl32(fl32(p / 100) * (g - 1)), interpolated
+//     with f = rank - i0 from the nearer end with one rounding
+//     (fma(f, d, a[i0]) for f < 1/2, else fma(f - 1, d, a[i1]), d = a[i1] -
+//     a[i0]); the host computes i0, i1 and f.  scale = range / 7.  The order
+//     statistics are read from a bitonic sort of |w| in LDS (equal values
+//     are equal, so the order of ties does not matter).
+//   MODE_MSE: candidate steps from min|w| to max|w| as torch.linspace gives
+//     them: d = (hi - lo) / (n - 1), c_i = fma(d, i, lo) for i < n / 2 and
+//     fma(-d, n - 1 - i, hi) above; c < 1e-10 is skipped; codes
+//     clamp(rint(fl32(w / c)), -7, 7); the error is the float32 sum over the
+//     group in column order of (q c - w)^2, divided by g; the first least
+//     mean wins (a 64-bit key of the mean's bits and the index; means are
 //     non-negative, so their bits order like their values); 1e-8 if no
 //     candidate qualifies.  Lane l evaluates candidates l, l + 64, ...
+//     The quotient w / c is taken as t = w * r with r = fl32(1 / c), within
+//     2^-19 of fl32(w / c) wherever |w / c| <= 8 (r and the product each
+//     add at most 2^-24 relative); beyond 8 both clamp to +-7.  A code
+//     depends only on which side of a half-integer the quotient falls, so
+//     where one of four consecutive t is within 2^-18 of one, the four codes
+//     are taken from the correctly rounded division instead.
 // ---------------------------------------------------------------------------
 constexpr int kCalMaxG = 1024;
 enum { MODE_PCT = 0, MODE_MSE = 1 };
@@ -439,7 +450,9 @@ __global__ __launch_bounds__(256) void k_quantize_pack_cal(const void* __restric
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     const float v0 = srt[i0], v1 = srt[i1];
-    s32 = (v0 + frac * (v1 - v0)) / 7.0f;
+    const float d = v1 - v0;
+    const float range = frac < 0.5f ? __builtin_fmaf(frac, d, v0) : __builtin_fmaf(frac - 1.0f, d, v1);
+    s32 = range / 7.0f;
   } else {
     float lo = __builtin_huge_valf(), hi = 0.0f;
     for (int e = lane; e < g; e += kWave) {
@@ -450,26 +463,44 @@ __global__ __launch_bounds__(256) void k_quantize_pack_cal(const void* __restric
     lo = group_min<kWave>(lo);
     hi = group_max<kWave>(hi);
     const float d = (hi - lo) / (float)(ncand - 1);
+    const int half = ncand >> 1;
+    auto cand = [&](int i) {
+      return i < half ? __builtin_fmaf(d, (float)i, lo) : __builtin_fmaf(-d, (float)(ncand - 1 - i), hi);
+    };
+    const float gf = (float)g;
     uint64_t best = ~0ull;
     for (int i = lane; i < ncand; i += kWave) {
-      const float c = lo + (float)i * d;
+      const float c = cand(i);
       if (!(c >= 1e-10f)) continue;
       const float r = 1.0f / c;
       float err = 0.0f;
       for (int kk = 0; kk < g; kk += 4) {
         const f32x4 w4 = ((const f32x4*)gl)[kk >> 2];
+        float qt[4], dev[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float q = fminf(fmaxf(rintf(w4[j] * r), -7.0f), 7.0f);
+          const float t = w4[j] * r;
+          qt[j] = rintf(t);
+          dev[j] = fabsf(t - qt[j]);  // exact; 1/2 at a half-integer
+        }
+        // any of the four within 2^-18 of a half-integer: the division decides
+        if (fmaxf(fmaxf(dev[0], dev[1]), fmaxf(dev[2], dev[3])) > 0.5f - 0x1p-18f) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qt[j] = rintf(w4[j] / c);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float q = __builtin_amdgcn_fmed3f(qt[j], -7.0f, 7.0f);
           const float e = q * c - w4[j];
           err = err + e * e;
         }
       }
-      const uint64_t key = ((uint64_t)__float_as_uint(err) << 32) | (uint32_t)i;
+      const float mean = err / gf;
+      const uint64_t key = ((uint64_t)__float_as_uint(mean) << 32) | (uint32_t)i;
       best = key < best ? key : best;
     }
     best = wave_min_u64(best);
-    s32 = best == ~0ull ? 1e-8f : lo + (float)(uint32_t)best * d;
+    s32 = best == ~0ull ? 1e-8f : cand((int)(uint32_t)best);
   }
   TS st = (TS)s32;
   if (st == (TS)0.0f) st = (TS)1.0f;
@@ -496,10 +527,13 @@ static hipError_t launch_cal_t(const void* w, int64_t n, int64_t k, int g, int m
   const size_t lds = (size_t)4 * (g + (mode == MODE_PCT ? P : 0)) * sizeof(float);
   uint32_t* pk = (uint32_t*)packed;
   if (mode == MODE_PCT) {
-    const double h = (g - 1) * (param / 100.0);
-    const int i0 = (int)std::floor(h);
-    const int i1 = i0 + 1 < g ? i0 + 1 : g - 1;
-    const float f = (float)(h - i0);
+    // torch.quantile's position of the p-th percentile among g sorted values:
+    // the fraction p / 100 as a float32, the rank fraction * (g - 1) in float32
+    const float q = (float)(param / 100.0);
+    const float rank = q * (float)(g - 1);
+    const int i0 = (int)std::floor(rank);
+    const int i1 = (int)std::ceil(rank);
+    const float f = rank - (float)i0;
     k_quantize_pack_cal<TIn, TS, MODE_PCT><<<grid, 256, lds, st>>>(w, ngroups, g / 8, i0, i1, f, 0, pk,
                                                                      (TS*)scales, (TS*)zeros);
   } else {

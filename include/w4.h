@@ -108,17 +108,21 @@ int quantize_pack_int4_sym(const void* w, int w_dtype, int64_t n, int64_t k, int
  * range-clipping calibrators); the codes are then those of
  * quantize_pack_int4_sym with the stored scale, zeros[] is written with 8.
  *
- * percentile: range = the `percentile`-th percentile of |G| (0 < p <= 100),
- *   linear between order statistics: with a = sorted |G|,
- *   h = (g - 1) p / 100 (double), i0 = floor(h), i1 = min(i0 + 1, g - 1),
- *   f = (float)(h - i0): range = a[i0] + f (a[i1] - a[i0]) in float32;
- *   scale = range / 7 (p = 100 gives quantize_pack_int4_sym exactly).
- * mse: `candidates` = n (2 .. 65536) steps c_i = lo + i d, d = (hi - lo) /
- *   (n - 1), lo = min|G|, hi = max|G| (float32); a step below 1e-10 is
- *   skipped; for the others q = clamp(rint(w * (1/c)), -7, 7) and
- *   E(c) = sum over G, in column order, of (q c - w)^2 in float32; the step
- *   is the first c with the least E, or 1e-8 when none qualifies.  The cost
- *   is about 7 g n float32 operations per group.
+ * Both follow the PyTorch calls of that step on the float32 group.
+ * percentile: range = torch.quantile(|G|, p / 100) for 0 < p <= 100, in
+ *   float32: with a = sorted |G|, rank = fl32(fl32(p / 100) * (g - 1)),
+ *   i0 = floor(rank), i1 = ceil(rank), f = rank - i0, d = a[i1] - a[i0]:
+ *   range = fma(f, d, a[i0]) if f < 1/2, else fma(f - 1, d, a[i1]) (one
+ *   rounding each); scale = range / 7 (p = 100 gives quantize_pack_int4_sym
+ *   exactly).
+ * mse: `candidates` = n (2 .. 65536) steps torch.linspace(lo, hi, n) with
+ *   lo = min|G|, hi = max|G|: d = (hi - lo) / (n - 1), c_i = fma(d, i, lo)
+ *   for i < n / 2 and fma(-d, n - 1 - i, hi) otherwise (float32); a step
+ *   below 1e-10 is skipped; for the others q = clamp(rint(w / c), -7, 7)
+ *   (float32 division) and E(c) = (sum over G, in column order, of
+ *   (q c - w)^2) / g in float32; the step is the first c with the least E,
+ *   or 1e-8 when none qualifies.  The cost is about 10 g n float32
+ *   operations per group.
  * Both: group_size <= 1024 (W4_EINVAL above); otherwise arguments, layout,
  * limits and errors as quantize_pack_int4.  The outputs are bit-for-bit
  * those of the definitions above.

@@ -34,11 +34,11 @@ test in tests/test_oracle_pins.py):
   * symmetric variant: scale = absmax/7 and code clamp(round(w/scale), -8, 7)
     ([P4] Step 2), stored with the +8 offset of [P4] Step 4, i.e. a fixed
     zero-point of 8; same stored-scale and zero-guard readings as above;
-  * calibrated symmetric scales ([P3] Step 4): the p-th percentile of |w|
-    (linear between order statistics) as the range, or the step chosen by the
-    MSE search over n candidates from min|w| to max|w| (codes clamped to
-    +-7 during the search, w/c taken as w * fl32(1/c), squared errors summed
-    in fp32 in column order, first minimum wins); the codes are then the
+  * calibrated symmetric scales ([P3] Step 4): the range is the p-th
+    percentile of |w| as torch.quantile computes it in float32, or the step
+    is the one the MSE search picks among torch.linspace(min|w|, max|w|, n)
+    (codes round(w / c) in float32 clamped to +-7 during the search, the
+    mean of the squared errors, first minimum wins); the codes are then the
     symmetric ones with the stored scale;
   * per-token activation scale max(max|x|, 1e-8)/127 and
     clamp(round(x/s), -128, 127) ([P1] Step 3);
@@ -214,6 +214,12 @@ def quantize_pack_int4_sym(w: np.ndarray, kind: str, g: int, sz: str):
 # Range-clipping calibrators for the symmetric variant ([P3] Step 4): they
 # choose each group's scale differently; the codes are then the symmetric
 # ones, clamp(rint(w / scale), -8, 7) + 8 with the stored scale.
+#
+# The page's calibrators are PyTorch calls on a float32 group:
+# torch.quantile(|w|, p / 100) and a search over torch.linspace(min|w|,
+# max|w|, n) with torch's float32 division, round, clamp and mse_loss.  The
+# functions below write out the float32 values those calls return (the
+# readings are pinned bit for bit against torch itself in the tests).
 # --------------------------------------------------------------------------
 def store_scale(s32: np.ndarray, sz: str) -> np.ndarray:
     """fp32 step -> storage dtype (nearest even); a stored 0 becomes 1."""
@@ -222,24 +228,54 @@ def store_scale(s32: np.ndarray, sz: str) -> np.ndarray:
     return np.where(s_st == 0, sd(1.0), s_st).astype(sd)
 
 
+def fma32(a, b, c) -> np.ndarray:
+    """a * b + c with ONE rounding to float32 (a fused multiply-add),
+    elementwise, for float32 a, b, c.
+
+    a * b of two float32 numbers is exact in float64.  The float64 sum with c
+    is then rounded to odd: when Knuth's TwoSum shows the sum was inexact and
+    the float64 result has an even last bit, it is moved one step towards the
+    exact value.  Rounding that value to float32 gives the correctly rounded
+    a * b + c, because float64 carries more than float32's 24 + 2 bits
+    (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+    proved algorithms using rounding to odd", IEEE Trans. Computers 2008)."""
+    a64 = np.asarray(a, F32).astype(np.float64)
+    b64 = np.asarray(b, F32).astype(np.float64)
+    c64 = np.asarray(c, F32).astype(np.float64)
+    prod = a64 * b64                          # exact: 24 + 24 significant bits
+    s = prod + c64
+    bv = s - prod                             # TwoSum: err = exact sum - s
+    err = (prod - (s - bv)) + (c64 - bv)
+    even = (np.ascontiguousarray(s).view(np.int64) & 1) == 0
+    s = np.where((err != 0) & even, np.nextafter(s, np.where(err > 0, np.inf, -np.inf)), s)
+    return s.astype(F32)
+
+
 def percentile_position(g: int, p: float):
-    """Where the p-th percentile of g sorted values lies: h = (g - 1) p / 100
-    in float64, returned as (i0, i1, f) with i0 = floor(h), i1 = min(i0 + 1,
-    g - 1) and f = fl32(h - i0)."""
-    h = (g - 1) * (p / 100.0)
-    i0 = int(np.floor(h))
-    return i0, min(i0 + 1, g - 1), F32(h - i0)
+    """Where torch.quantile(v, p / 100) of g values reads the sorted values:
+    q = fl32(p / 100) (the fraction becomes a float32 tensor), rank =
+    fl32(q * (g - 1)); returns (i0, i1, f) with i0 = floor(rank), i1 =
+    ceil(rank) and the interpolation weight f = rank - i0 (exact)."""
+    q = F32(p / 100.0)
+    rank = F32(q * F32(g - 1))
+    i0 = int(np.floor(rank))
+    return i0, int(np.ceil(rank)), F32(rank - F32(i0))
 
 
 def calib_percentile_range(w32: np.ndarray, g: int, p: float) -> np.ndarray:
-    """[P3] Step 4, "percentile": the p-th percentile of |w| per group, linear
-    between neighbouring order statistics a (ascending):
-    fl32(a[i0] + fl32(f * fl32(a[i1] - a[i0])))."""
+    """[P3] Step 4, "percentile": torch.quantile(|w|, p / 100) per group
+    (linear interpolation).  With a the group's |w| in ascending order and
+    (i0, i1, f) from percentile_position, d = fl32(a[i1] - a[i0]); the value
+    is taken from the nearer end with one rounding: a[i0] + f d when f < 1/2,
+    else a[i1] - (1 - f) d, i.e. fma(f, d, a[i0]) or fma(f - 1, d, a[i1])."""
     a = np.sort(np.abs(split_groups(w32, g)), axis=2)
     i0, i1, f = percentile_position(g, p)
     lo = a[..., i0].astype(F32)
     hi = a[..., i1].astype(F32)
-    return (lo + f * (hi - lo)).astype(F32)
+    d = (hi - lo).astype(F32)
+    if f < F32(0.5):
+        return fma32(f, d, lo)
+    return fma32(F32(f - F32(1.0)), d, hi)
 
 
 def quantize_pack_int4_sym_percentile(w: np.ndarray, kind: str, g: int, sz: str, p: float):
@@ -252,39 +288,51 @@ def quantize_pack_int4_sym_percentile(w: np.ndarray, kind: str, g: int, sz: str,
 
 
 def mse_candidates(lo: np.ndarray, hi: np.ndarray, n: int) -> np.ndarray:
-    """n steps spaced linearly from lo to hi ([P3] Step 4 "mse_search"):
-    c_i = fl32(lo + fl32(i * d)) with d = fl32(fl32(hi - lo) / (n - 1))."""
-    d = ((hi.astype(F32) - lo.astype(F32)) / F32(n - 1)).astype(F32)
-    i = np.arange(n, dtype=F32)
-    return (lo.astype(F32)[..., None] + (i * d[..., None]).astype(F32)).astype(F32)
+    """torch.linspace(lo, hi, n) in float32 ([P3] Step 4 "mse_search"): the
+    step d = fl32(fl32(hi - lo) / (n - 1)); the first n // 2 values are
+    counted up from lo, the rest down from hi, each with one rounding:
+    c_i = fma(d, i, lo) for i < n // 2, fma(-d, n - 1 - i, hi) otherwise.
+    So c_0 = lo and c_(n-1) = hi exactly."""
+    lo = np.asarray(lo, F32)[..., None]
+    hi = np.asarray(hi, F32)[..., None]
+    d = ((hi - lo) / F32(n - 1)).astype(F32)
+    i = np.arange(n)
+    up = fma32(d, i.astype(F32), lo)
+    down = fma32(-d, (n - 1 - i).astype(F32), hi)
+    return np.where(i < n // 2, up, down).astype(F32)
 
 
 MSE_SKIP_BELOW = F32(1e-10)
 MSE_NONE = F32(1e-8)
 
 
+def mse_codes(w: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """The search's codes for the candidate step c: clamp(rint(fl32(w / c)),
+    -7, 7) -- a float32 division, rounded half to even, clamped to +-7."""
+    return np.clip(np.rint((np.asarray(w, F32) / np.asarray(c, F32)).astype(F32)), -7, 7).astype(F32)
+
+
 def calib_mse_step(w32: np.ndarray, g: int, n: int) -> np.ndarray:
-    """[P3] Step 4, "mse_search", per group: candidate steps c from min|w| to
-    max|w|; each c below 1e-10 is skipped; for the others the codes are
-    q = clamp(rint(fl32(w * fl32(1 / c))), -7, 7) and the error is
-    E(c) = sum over the group, in column order, of fl32(fl32(q * c) - w)^2,
-    accumulated in fp32.  The first candidate with the least E is the step;
-    1e-8 when every candidate is skipped.  Minimising the sum is minimising
-    the page's mean."""
+    """[P3] Step 4, "mse_search", per group: candidate steps c =
+    mse_candidates(min|w|, max|w|, n); a c below 1e-10 is skipped; for the
+    others the codes are q = clamp(rint(fl32(w / c)), -7, 7) and the error
+    is the mean over the group of fl32(fl32(q * c) - w)^2: the float32 sum in
+    column order, divided by g in float32.  The first candidate with the
+    least mean is the step; 1e-8 when every candidate is skipped."""
     wg = split_groups(w32, g)
     a = np.abs(wg)
     c = mse_candidates(a.min(axis=2), a.max(axis=2), n)
     valid = c >= MSE_SKIP_BELOW
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        r = (F32(1.0) / c).astype(F32)
-        E = np.zeros(c.shape, F32)
-        for k in range(g):
-            wk = wg[..., k][..., None]
-            q = np.clip(np.rint((wk * r).astype(F32)), -7, 7).astype(F32)
-            e = ((q * c).astype(F32) - wk).astype(F32)
-            E = (E + (e * e).astype(F32)).astype(F32)
-    E = np.where(valid, E, np.inf)
-    best = np.argmin(E, axis=2)  # first occurrence of the minimum
+    csafe = np.where(valid, c, F32(1.0))
+    E = np.zeros(c.shape, F32)
+    for k in range(g):
+        wk = wg[..., k][..., None]
+        q = mse_codes(wk, csafe)
+        e = ((q * csafe).astype(F32) - wk).astype(F32)
+        E = (E + (e * e).astype(F32)).astype(F32)
+    mean = (E / F32(g)).astype(F32)
+    mean = np.where(valid, mean, np.inf)
+    best = np.argmin(mean, axis=2)  # first occurrence of the minimum
     step = np.take_along_axis(c, best[..., None], 2)[..., 0]
     return np.where(valid.any(axis=2), step, MSE_NONE).astype(F32)
 

@@ -11,6 +11,8 @@ import math
 
 import numpy as np
 
+from tests import page_calibrators as PC
+
 f32 = np.float32
 
 
@@ -103,41 +105,10 @@ def quantize_pack_sym(w32: np.ndarray, g: int, sz: str):
     return packed, scales, zeros
 
 
-def percentile_group(vals, p: float):
-    """One group: the p-th percentile of |v|, linear between order statistics."""
-    a = sorted(f32(abs(v)) for v in vals)
-    g = len(a)
-    h = (g - 1) * (p / 100.0)
-    i0 = math.floor(h)
-    i1 = min(i0 + 1, g - 1)
-    f = f32(h - i0)
-    return f32(a[i0] + f32(f * f32(a[i1] - a[i0])))
-
-
-def mse_group(vals, n: int):
-    """One group: the MSE search over n candidate steps, element by element."""
-    a = [f32(abs(v)) for v in vals]
-    lo, hi = min(a), max(a)
-    d = f32(f32(hi - lo) / f32(n - 1))
-    best_e, best_c = None, None
-    for i in range(n):
-        c = f32(lo + f32(f32(i) * d))
-        if c < f32(1e-10):
-            continue
-        r = f32(f32(1.0) / c)
-        e_sum = f32(0.0)
-        for v in vals:
-            q = _clamp(_rint(f32(v * r)), -7, 7)
-            e = f32(f32(f32(q) * c) - v)
-            e_sum = f32(e_sum + f32(e * e))
-        if best_e is None or e_sum < best_e:
-            best_e, best_c = e_sum, c
-    return best_c if best_c is not None else f32(1e-8)
-
-
 def quantize_pack_calibrated(w32: np.ndarray, g: int, sz: str, method: str, param):
     """Symmetric codes with a calibrated scale ("percentile" range / 7, or the
-    "mse" step), element by element."""
+    "mse" step), element by element; the range or step of each group comes
+    from the page's own torch calls, one group at a time."""
     n, k = w32.shape
     ng = k // g
     sdt = np.float16 if sz == "f16" else np.float32
@@ -149,9 +120,9 @@ def quantize_pack_calibrated(w32: np.ndarray, g: int, sz: str, method: str, para
         for gi in range(ng):
             vals = [f32(w32[r, gi * g + t]) for t in range(g)]
             if method == "percentile":
-                step = f32(percentile_group(vals, param) / f32(7.0))
+                step = f32(PC.percentile(vals, param) / f32(7.0))
             else:
-                step = mse_group(vals, param)
+                step = PC.mse_search(vals, param)
             stored = sdt(step)
             if float(stored) == 0.0:
                 stored = sdt(1.0)

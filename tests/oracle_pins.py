@@ -21,6 +21,7 @@ import numpy as np
 
 import oracle.w4_oracle as O
 from tests import brute_force as BF
+from tests import page_calibrators as PC
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 f32 = np.float32
@@ -580,12 +581,35 @@ def check_percentile_vs_numpy():
             got = O.calib_percentile_range(w, g, p).astype(np.float64)
             want = np.quantile(np.abs(w.astype(np.float64)).reshape(8, -1, g), p / 100.0, axis=2,
                                method="linear")
-            assert np.allclose(got, want, rtol=4e-7, atol=0), (g, p, float(np.abs(got - want).max()))
+            assert np.allclose(got, want, rtol=4e-6, atol=0), (g, p, float(np.abs(got - want).max()))
+
+
+def check_percentile_vs_torch_quantile():
+    """Bit for bit against the page's call, torch.quantile(|w|, p / 100), on
+    1536 random groups (batched) and 48 single groups (the page's 1-D call),
+    over sizes, scales, ties and percentiles that put the rank's fraction
+    below and above 1/2."""
+    import torch
+    rng = np.random.default_rng(25)
+    for g in (32, 96, 128, 640):
+        w = (rng.normal(0, 1, (12, 4 * g)) * 10.0 ** rng.uniform(-5, 1, (12, 1))).astype(np.float32)
+        w[0, : g // 2] = w[0, 0]                    # repeated values
+        w[1, :g] = 0.0                              # an all-zero group
+        for p in (0.5, 12.345, 33.3, 50.0, 75.0, 90.0, 99.0, 99.9, 99.99, 100.0):
+            got = O.calib_percentile_range(w, g, p)
+            ref = torch.quantile(torch.from_numpy(np.abs(w).reshape(12, 4, g)), p / 100, dim=2).numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (g, p)
+    for t in range(48):
+        g = (32, 128)[t % 2]
+        v = (rng.normal(0, 0.02, g) * (1 + 9 * (t % 3))).astype(np.float32)
+        p = float(rng.uniform(1, 100))
+        got = O.calib_percentile_range(v.reshape(1, g), g, p)[0, 0]
+        assert got.view(np.uint32) == PC.percentile(v, p).view(np.uint32), (t, g, p)
 
 
 def check_percentile_exact_midpoint():
-    """g = 32, p = 50: h = 15.5, so the range is the exact midpoint of the
-    16th and 17th smallest |w| (values chosen exact in binary)."""
+    """g = 32, p = 50: the rank is 15.5, so the range is the exact midpoint
+    of the 16th and 17th smallest |w| (values chosen exact in binary)."""
     g = 32
     mags = np.arange(1, 33, dtype=np.float32) * np.float32(2.0 ** -8)  # 16th: 16/256, 17th: 17/256
     w = (mags * np.where(np.arange(32) % 3 == 0, -1, 1)).astype(np.float32)[np.random.default_rng(1).permutation(32)]
@@ -596,6 +620,121 @@ def check_percentile_exact_midpoint():
     assert float(O.calib_percentile_range(w.reshape(1, g), g, 100.0)[0, 0]) == 32 / 256
     i0, i1, f = O.percentile_position(g, 1e-9)
     assert (i0, i1) == (0, 1) and 0 < f < 1e-9
+    # p = 99.9 at g = 128: rank fl32(fl32(0.999) * 127) = 126.873..., so the
+    # value is read from the upper end: a[127] - (1 - f)(a[127] - a[126])
+    i0, i1, f = O.percentile_position(128, 99.9)
+    assert (i0, i1) == (126, 127) and f == np.float32(np.float32(0.999) * np.float32(127)) - np.float32(126)
+
+
+def _exact_round_f32(x) -> np.float32:
+    """A rational (fractions.Fraction) rounded to the nearest float32, ties to
+    even, in integer arithmetic (normal range)."""
+    from fractions import Fraction
+    x = Fraction(x)
+    if x == 0:
+        return np.float32(0.0)
+    sign = -1 if x < 0 else 1
+    x = abs(x)
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    while Fraction(2) ** e > x:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= x:
+        e += 1
+    unit = Fraction(2) ** (e - 23)               # 2^e <= x < 2^(e+1): 24-bit significand
+    m = x / unit
+    q = m.numerator // m.denominator
+    rem = m - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return np.float32(sign * float(q * unit))
+
+
+def check_fma32_correctly_rounded():
+    """fma32 against the exact rational a * b + c rounded once, on random
+    operands of mixed scales and on sums that sit on, just off and across
+    float32 rounding midpoints (where two roundings would differ)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(26)
+    a = (rng.normal(0, 1, 400) * 2.0 ** rng.integers(-30, 30, 400)).astype(np.float32)
+    b = rng.integers(0, 70000, 400).astype(np.float32)
+    c = (rng.normal(0, 1, 400) * 2.0 ** rng.integers(-40, 30, 400)).astype(np.float32)
+    # midpoint constructions: a * b = 1 + 2^-24 (a midpoint of float32 at 1),
+    # plus a tiny c of either sign, or none
+    a = np.concatenate([a, np.float32([1.0 + 2.0 ** -23] * 3 + [3.0, 2.0 ** -24])])
+    b = np.concatenate([b, np.float32([1.0 - 2.0 ** -24] * 3 + [1.0 / 3.0, 1.0])])
+    c = np.concatenate([c, np.float32([2.0 ** -70, -(2.0 ** -70), 0.0, -1.0, 1.0])])
+    got = O.fma32(a, b, c)
+    for ai, bi, ci, gi in zip(a, b, c, got):
+        want = _exact_round_f32(Fraction(float(ai)) * Fraction(float(bi)) + Fraction(float(ci)))
+        assert gi.view(np.uint32) == want.view(np.uint32), (ai, bi, ci, gi, want)
+
+
+def check_mse_candidates_vs_torch_linspace():
+    """Bit for bit against torch.linspace(min|w|, max|w|, n) in float32 on
+    1200 random groups and a range of n, including tiny, zero and equal
+    ends; the ends are exact."""
+    import torch
+    rng = np.random.default_rng(27)
+    for t in range(1200):
+        v = np.abs(rng.normal(0, 1, 128) * 10.0 ** rng.uniform(-8, 2)).astype(np.float32)
+        if t % 13 == 0:
+            v[:] = v[0]
+        if t % 7 == 0:
+            v[5] = 0.0
+        lo, hi = v.min(), v.max()
+        n = (2, 3, 5, 17, 64, 100, 999, 1000, 1001, 4096)[t % 10]
+        got = O.mse_candidates(np.float32(lo), np.float32(hi), n)
+        ref = torch.linspace(torch.tensor(lo), torch.tensor(hi), n).numpy()
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (t, n)
+        assert got[0] == lo and got[-1] == hi
+
+
+def check_mse_codes_vs_torch():
+    """The search's codes against torch's float32 division, round and clamp,
+    on random pairs and on pairs where w / c is exactly a half-integer or one
+    ulp from one, so that a product with a rounded reciprocal 1/c would take
+    the other side (for example 0.04443359375 / (7 * 2^-10) = 6.5 rounds to
+    6, while 0.04443359375 * fl32(1 / (7 * 2^-10)) rounds up to 6.5000005)."""
+    import torch
+    rng = np.random.default_rng(28)
+    w = rng.normal(0, 0.05, 4000).astype(np.float32)
+    c = np.abs(rng.normal(0, 0.01, 4000)).astype(np.float32) + np.float32(1e-6)
+    tw, tc = [], []
+    for j in range(3, 200, 2):
+        cj = np.float32(j * 2.0 ** -10)
+        for k in range(7):
+            base = np.float32((k + 0.5) * float(cj))
+            for d in (-1, 0, 1):
+                tw.append((base.view(np.int32) + d).view(np.float32) * (1 if (j + k) % 2 else -1))
+                tc.append(cj)
+    w = np.concatenate([w, np.array(tw, np.float32)])
+    c = np.concatenate([c, np.array(tc, np.float32)])
+    got = O.mse_codes(w, c)
+    ref = torch.clamp(torch.round(torch.from_numpy(w) / torch.from_numpy(c)), -7, 7).numpy()
+    assert np.array_equal(got, ref)
+    recip = np.clip(np.rint(w * (np.float32(1.0) / c)), -7, 7)
+    assert (recip != ref).sum() > 50   # the constructed pairs do separate the two forms
+
+
+def check_mse_step_vs_page_search():
+    """The chosen step, bit for bit, against the page's mse_search evaluated
+    with torch one group at a time: 1000 random groups with 100 candidates
+    and 100 groups with 1000 (Gaussian weights at several scales, with and
+    without an outlier, and a few all-equal or zero-containing groups)."""
+    rng = np.random.default_rng(29)
+    for n, count in ((100, 1000), (1000, 100)):
+        for t in range(count):
+            g = (32, 128, 64)[t % 3]
+            v = (rng.normal(0, 1, g) * 10.0 ** rng.uniform(-4, 0)).astype(np.float32)
+            if t % 4 == 0:
+                v[rng.integers(0, g)] = np.float32(8.0 * np.abs(v).max())
+            if t % 97 == 0:
+                v[:] = v[0]
+            if t % 89 == 0:
+                v[: g // 4] = 0.0
+            got = O.calib_mse_step(v.reshape(1, g), g, n)[0, 0]
+            ref = PC.mse_search(v, n)
+            assert got.view(np.uint32) == ref.view(np.uint32), (n, t, g, got, ref)
 
 
 def check_calibrators_brute_force():
@@ -717,6 +856,9 @@ ALL_CHECKS = [
     check_sym_worked_example, check_sym_special_groups, check_sym_brute_force,
     check_sym_exact_scaled_matmul, check_sym_invariants,
     check_percentile_100_is_minmax, check_percentile_vs_numpy, check_percentile_exact_midpoint,
+    check_percentile_vs_torch_quantile, check_fma32_correctly_rounded,
+    check_mse_candidates_vs_torch_linspace, check_mse_codes_vs_torch,
     check_calibrators_brute_force, check_mse_exact_grid, check_mse_first_minimum_and_clamp,
     check_mse_skipped_candidates, check_mse_is_least_error,
+    check_mse_step_vs_page_search,  # slowest: keep last
 ]

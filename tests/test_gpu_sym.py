@@ -285,6 +285,53 @@ def test_mse_pinned_groups(w4):
                 assert float(got[1][0, 0]) == want_step[cand], (cand, float(got[1][0, 0]))
 
 
+def _mse_tie_rows(rng, rows, k):
+    """Rows whose groups make the search's quotients w / c land exactly on,
+    or one ulp beside, half-integers: each group holds 0 and 63 * 2^-10, so
+    with 64 candidates c_i = i * 2^-10 exactly, and the other values are
+    (k + 1/2) * j * 2^-10 for odd j (steps with inexact reciprocals), nudged
+    by -1, 0 or +1 ulp, with random signs."""
+    u = 2.0 ** -10
+    vals = []
+    for j in range(3, 64, 2):
+        for kk in range(7):
+            if (kk + 0.5) * j <= 63:
+                base = np.float32((kk + 0.5) * j * u)
+                for d in (-1, 0, 1):
+                    vals.append((base.view(np.int32) + d).view(np.float32))
+    vals = np.array(vals, np.float32)
+    w = rng.choice(vals, (rows, k)) * rng.choice(np.float32([-1, 1]), (rows, k))
+    w[:, 0::32] = 0.0
+    w[:, 1::32] = np.float32(63 * u)
+    return w.astype(np.float32)
+
+
+@pytest.mark.parametrize("g", [32, 128])
+@pytest.mark.parametrize("sz", ["f16", "f32"])
+def test_mse_quotient_ties(w4, g, sz):
+    """Quotients on and beside half-integers (here about 90 of every 64,000
+    quotients take the other side when computed with the rounded reciprocal
+    1/c), so the kernel's near-tie path, the correctly rounded division, runs
+    often; the outputs must still equal the oracle's bit for bit.  (Which
+    side a near-tie takes moves an error by about one ulp of the step, so it
+    rarely changes the chosen step; the division itself is pinned against
+    torch on the CPU.)"""
+    w = _mse_tie_rows(np.random.default_rng(4100 + g), 48, 256)
+    got = gpu_quantize_cal(w4, w, "f32", g, sz, "mse", 64)
+    assert_quant_equal(got, oracle_cal(w, "f32", g, sz, "mse", 64))
+
+
+@pytest.mark.parametrize("p", [12.345, 33.3, 66.6, 99.99])
+def test_percentile_both_interpolation_ends(w4, p):
+    """Percentiles whose rank fraction lies below and above 1/2 (read from
+    the lower or the upper order statistic)."""
+    rng = np.random.default_rng(4200)
+    w = (rng.normal(0, 0.02, (64, 512)) * 10.0 ** rng.uniform(-3, 1, (64, 1))).astype(np.float32)
+    for g in (32, 128):
+        got = gpu_quantize_cal(w4, w, "f32", g, "f32", "percentile", p)
+        assert_quant_equal(got, oracle_cal(w, "f32", g, "f32", "percentile", p))
+
+
 def test_calibrators_workload(w4):
     """The 4096 x 4096 weight (bf16, g = 128, fp16 scales): percentile on
     every row, MSE search (1000 candidates) on 64 sampled rows."""

@@ -218,42 +218,62 @@ def _pct_position_from_g(g, p):
     return i0, min(i0 + 1, g - 1), F32(h - np.floor(h))
 
 
-def _mse_last_minimum(w32, g, n):
+def _mse_search_with(w32, g, n, lo_clamp=-7, last=False):
+    # calib_mse_step with one of two planted mistakes: codes clamped at
+    # lo_clamp instead of -7, or the last (not the first) least mean kept
     wg = O.split_groups(w32, g)
     a = np.abs(wg)
     c = O.mse_candidates(a.min(axis=2), a.max(axis=2), n)
     valid = c >= O.MSE_SKIP_BELOW
-    with np.errstate(all="ignore"):
-        r = (F32(1.0) / c).astype(F32)
-        E = np.zeros(c.shape, F32)
-        for k in range(g):
-            wk = wg[..., k][..., None]
-            q = np.clip(np.rint(wk * r), -7, 7).astype(F32)
-            e = (q * c - wk).astype(F32)
-            E = (E + e * e).astype(F32)
-    E = np.where(valid, E, np.inf)
-    best = E.shape[2] - 1 - np.argmin(E[..., ::-1], axis=2)
+    cs = np.where(valid, c, F32(1.0))
+    E = np.zeros(c.shape, F32)
+    for k in range(g):
+        wk = wg[..., k][..., None]
+        q = np.clip(np.rint((wk / cs).astype(F32)), lo_clamp, 7).astype(F32)
+        e = ((q * cs).astype(F32) - wk).astype(F32)
+        E = (E + (e * e).astype(F32)).astype(F32)
+    E = np.where(valid, (E / F32(g)).astype(F32), np.inf)
+    best = E.shape[2] - 1 - np.argmin(E[..., ::-1], axis=2) if last else np.argmin(E, axis=2)
     step = np.take_along_axis(c, best[..., None], 2)[..., 0]
     return np.where(valid.any(axis=2), step, O.MSE_NONE).astype(F32)
+
+
+def _mse_last_minimum(w32, g, n):
+    return _mse_search_with(w32, g, n, last=True)
 
 
 def _mse_clamp_8(w32, g, n):
-    wg = O.split_groups(w32, g)
-    a = np.abs(wg)
-    c = O.mse_candidates(a.min(axis=2), a.max(axis=2), n)
-    valid = c >= O.MSE_SKIP_BELOW
-    with np.errstate(all="ignore"):
-        r = (F32(1.0) / c).astype(F32)
-        E = np.zeros(c.shape, F32)
-        for k in range(g):
-            wk = wg[..., k][..., None]
-            q = np.clip(np.rint(wk * r), -8, 7).astype(F32)
-            e = (q * c - wk).astype(F32)
-            E = (E + e * e).astype(F32)
-    E = np.where(valid, E, np.inf)
-    best = np.argmin(E, axis=2)
-    step = np.take_along_axis(c, best[..., None], 2)[..., 0]
-    return np.where(valid.any(axis=2), step, O.MSE_NONE).astype(F32)
+    return _mse_search_with(w32, g, n, lo_clamp=-8)
+
+
+def _mse_candidates_one_ended(lo, hi, n):
+    # every candidate counted up from lo: c_i = fl32(lo + fl32(i * d))
+    lo = np.asarray(lo, F32)[..., None]
+    hi = np.asarray(hi, F32)[..., None]
+    d = ((hi - lo) / F32(n - 1)).astype(F32)
+    return (lo + (np.arange(n, dtype=F32) * d).astype(F32)).astype(F32)
+
+
+def _mse_codes_by_reciprocal(w, c):
+    return np.clip(np.rint((np.asarray(w, F32) * (F32(1.0) / np.asarray(c, F32)).astype(F32)).astype(F32)),
+                   -7, 7).astype(F32)
+
+
+def _pct_lower_end_two_roundings(w32, g, p):
+    a = np.sort(np.abs(O.split_groups(w32, g)), axis=2)
+    i0, i1, f = O.percentile_position(g, p)
+    lo = a[..., i0].astype(F32)
+    return (lo + (f * (a[..., i1] - lo).astype(F32)).astype(F32)).astype(F32)
+
+
+def _pct_position_float64(g, p):
+    h = (g - 1) * (p / 100.0)
+    i0 = int(np.floor(h))
+    return i0, min(i0 + 1, g - 1), F32(h - i0)
+
+
+def _fma32_two_roundings(a, b, c):
+    return ((np.asarray(a, F32) * np.asarray(b, F32)).astype(F32) + np.asarray(c, F32)).astype(F32)
 
 
 def _mse_candidates_from_zero(lo, hi, n):
@@ -315,6 +335,11 @@ MUTATIONS = {
     "mse_candidates_from_zero": {"mse_candidates": _mse_candidates_from_zero},
     "mse_candidates_spacing_over_n": {"mse_candidates": _mse_candidates_n_steps},
     "mse_no_default_step": {"calib_mse_step": _mse_no_none_default},
+    "mse_candidates_one_ended": {"mse_candidates": _mse_candidates_one_ended},
+    "mse_codes_by_reciprocal": {"mse_codes": _mse_codes_by_reciprocal},
+    "percentile_lower_end_two_roundings": {"calib_percentile_range": _pct_lower_end_two_roundings},
+    "percentile_position_float64": {"percentile_position": _pct_position_float64},
+    "fma32_two_roundings": {"fma32": _fma32_two_roundings},
 }
 
 
@@ -323,10 +348,11 @@ def test_mutation_is_caught(name, monkeypatch):
     for attr, fn in MUTATIONS[name].items():
         monkeypatch.setattr(O, attr, fn)
     failed = []
-    for check in P.ALL_CHECKS:
+    for check in P.ALL_CHECKS:  # the slowest pins come last; stop at the first that fails
         try:
             with np.errstate(all="ignore"):
                 check()
         except Exception as exc:  # AssertionError or a shape error: caught either way
             failed.append((check.__name__, type(exc).__name__))
+            break
     assert failed, f"planted mistake {name!r} passed every pin"
