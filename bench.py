@@ -83,13 +83,16 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="skip the extra per-step measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
-    ap.add_argument("--kernel", choices=("decode_wb", "prefill_wb", "w4a8_m1", "w4a8_m512", "copy", "gptq"),
+    ap.add_argument("--kernel", choices=("decode_wb", "prefill_wb", "w4a8_m1", "w4a8_m512", "copy", "gptq",
+                                         "read"),
                     default=None,
                     help="launch only this kernel --launches times, eagerly, for counter runs: "
                          "decode_wb = the [11008,4096] decode product on rotated weights, "
                          "prefill_wb = the M=2048 product on [11008,4096], "
                          "w4a8_m1 / w4a8_m512 = the W4A8 product on [28672,8192], "
-                         "copy = a plain device copy of --copy-mib MiB (calibrates byte counters)")
+                         "copy = a plain device copy of --copy-mib MiB (calibrates byte counters), "
+                         "read = the streaming-read measurement kernel over the decode product's byte "
+                         "count, rotated through a 1 GiB buffer")
     ap.add_argument("--launches", type=int, default=40)
     ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args(argv)
@@ -154,6 +157,22 @@ def main(argv=None):
         del graphs
         return e0.elapsed_time(e1) / 1e3 / iters
 
+    def time_each(fn, iters):
+        """Per-launch durations (seconds) of fn(i), i = 0..iters-1: each
+        launch is bracketed by two HIP events on the launch stream and the
+        launches are issued eagerly, so every figure is one kernel's own
+        start-to-end time, the quantity a kernel trace records (no overlap
+        with neighbouring launches)."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) / 1e3 for a, b in ev]
+
     if args.kernel is not None:
         return kernel_only(args, w4, WL, torch, dev, to_dev, log)
 
@@ -197,12 +216,24 @@ def main(argv=None):
 
     for i in range(args.warmup):
         dom(i)
-    dsec = time_region(dom, args.steps)
+    nlaunch = max(100, args.steps)
+    durs = sorted(time_each(dom, nlaunch))
+    dsec = sum(durs) / len(durs)
+    dmed = durs[len(durs) // 2]
+    gsec = time_region(dom, args.steps)
     dbytes = w4a16_bytes(1, 11008, 4096, g)
     achieved = dbytes / dsec / 1e9
     roof = {"kernel": "w4a16 decode, W [11008,4096] int4 g128, x bf16 [1,4096]",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_launch_us": round(dsec * 1e6, 3),
+            "median_launch_us": round(dmed * 1e6, 3),
+            "frac_at_median": round(dbytes / dmed / 1e9 / HBM_PEAK_GBS, 4),
+            "launches_timed": nlaunch,
+            "timing": "per-launch HIP event pairs on the launch stream, eager launches over the "
+                      "rotated weight copies (the kernel's own start-to-end time, as a kernel trace "
+                      "records it)",
+            "graph_replay_us_per_launch": round(gsec * 1e6, 3),
+            "graph_replay_frac": round(dbytes / gsec / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_launch": dbytes, "traffic": None}
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
@@ -211,7 +242,8 @@ def main(argv=None):
         ent = tr.get("w4a16_decode_Wb")
         if ent and ent.get("src_hash") == src_hash():
             roof["traffic"] = ent.get("bytes_per_launch")
-    log(f"dominant kernel: {dsec * 1e6:.2f} us/launch, {achieved:.1f} GB/s")
+    log(f"dominant kernel: {dsec * 1e6:.2f} us/launch (median {dmed * 1e6:.2f}), {achieved:.1f} GB/s; "
+        f"graph replay {gsec * 1e6:.2f} us per launch")
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -230,7 +262,8 @@ def main(argv=None):
     del q
 
     if not args.quick:
-        result["extra"] = extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copies, x1)
+        result["extra"] = extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, time_each, log,
+                                 copies, x1, dsec * 1e6)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, WL, np, log, wa, wb)
@@ -239,7 +272,7 @@ def main(argv=None):
     return 0
 
 
-def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copies, x1):
+def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, time_each, log, copies, x1, dom_us):
     """Rates of every other step of the path; each is timed with HIP events."""
     out = {}
     g = 128
@@ -376,30 +409,107 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
 
     out["llama7b_decode_32_layers"] = llama_decode(w4, torch, dev, time_region, log, g)
     out["gptq_Wb"] = gptq_bench(w4, torch, np, dev, time_region, log)
-    out["measured_peaks"] = measured_peaks(w4, WL, torch, dev, to_dev, time_region, log, copies, x1, out)
+    out["measured_peaks"] = measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copies,
+                                           x1, out, dom_us)
     return out
 
 
-def measured_peaks(w4, WL, torch, dev, to_dev, time_region, log, copies, x1, out, g=128):
-    """Context for the fractions above: the decode product with one weight
-    copy (resident in the 256 MB Infinity Cache, so not an HBM figure), a
-    1 GiB device copy as a measured HBM peak, and the dense bf16 library GEMM
-    (torch.matmul on a dequantized weight, run as a black box) on the M = 2048
-    shape."""
+def load_peaks_lib():
+    """libw4peaks.so (measurement kernels, built next to libw4.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "dequant_gemm_quantize_amd", "libw4peaks.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it first (__graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.w4_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.w4_peak_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def _stats(durs):
+    d = sorted(durs)
+    return sum(d) / len(d), d[len(d) // 2]
+
+
+def measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copies, x1, out, dom_us, g=128):
+    """Context for the fractions above, measured in the same process:
+    - the decode product with one weight copy (resident in the 256 MB
+      Infinity Cache, so not an HBM figure);
+    - a plain streaming read of the decode product's byte count with the
+      decode kernels' geometry (rotated through a 1 GiB buffer, so from HBM),
+      and of 1 GiB: the read bandwidth this GPU sustains for such launches;
+    - back-to-back bf16 and int8 matrix instructions (MFMA-only loops): the
+      matrix rate this GPU sustains under that load;
+    - a 1 GiB device copy, and the dense bf16 library GEMM (torch.matmul on a
+      dequantized weight, run as a black box) on the M = 2048 shape."""
+    import ctypes
+    lib = load_peaks_lib()
+    sid = torch.cuda.current_stream(dev).cuda_stream
     res = {}
     y = torch.empty((1, 11008), dtype=torch.bfloat16, device=dev)
     p, s, z = copies["Wb"][0]
     sec = time_region(lambda i: w4.w4a16_matmul(x1, p, s, z, g, out=y), 200)
     res["decode_Wb_warm"] = {"us": round(sec * 1e6, 3), "GB/s": round(w4a16_bytes(1, 11008, 4096, g) / sec / 1e9, 1),
                              "note": "one weight copy, cache-resident: not an HBM figure"}
+
+    # streaming reads
+    big = torch.empty(1 << 28, dtype=torch.int32, device=dev).random_()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    dbytes = w4a16_bytes(1, 11008, 4096, g)            # 23,983,616: a multiple of 16
+    nreg = (big.numel() * 4) // dbytes
+    base = big.data_ptr()
+
+    def rd(i, nbytes=dbytes, lanes=8, stride=dbytes, regions=nreg):
+        rc = lib.w4_peak_stream_read(ctypes.c_void_p(base + (i % regions) * stride), nbytes, lanes,
+                                     ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(sid))
+        if rc != 0:
+            raise RuntimeError(f"w4_peak_stream_read failed ({rc})")
+    for i in range(5):
+        rd(i)
+    avg, med = _stats(time_each(rd, 200))
+    gsec = time_region(rd, 200)
+    dec = dom_us
+    res["stream_read_decode_bytes"] = {
+        "bytes": dbytes, "avg_us": round(avg * 1e6, 3), "median_us": round(med * 1e6, 3),
+        "GB/s": round(dbytes / avg / 1e9, 1), "frac_of_8TBs": round(dbytes / avg / 1e9 / HBM_PEAK_GBS, 4),
+        "graph_replay_us": round(gsec * 1e6, 3),
+        "decode_Wb_frac_of_it": round(avg * 1e6 / dec, 4),
+        "note": "the decode product's byte count read once, 688+ workgroups of 256 lanes, 8 x 16 B "
+                "non-temporal loads per lane (the decode kernels' pattern), rotated over a 1 GiB buffer"}
+    gib = big.numel() * 4
+    avg1, med1 = _stats(time_each(lambda i: rd(0, gib, 16, 0, 1), 20))
+    res["stream_read_1GiB"] = {"avg_us": round(avg1 * 1e6, 2), "GB/s": round(gib / avg1 / 1e9, 1),
+                               "frac_of_8TBs": round(gib / avg1 / 1e9 / HBM_PEAK_GBS, 4)}
+
+    # matrix-instruction loops on random operands
+    ops = torch.randn(1024, dtype=torch.float32, device=dev).to(torch.bfloat16)  # 128 x 16 B of bf16
+    ops8 = torch.randint(-128, 128, (2048,), dtype=torch.int8, device=dev)
+    blocks, iters = 512, 2000
+    mout = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for kind, buf, unit_ops, peak, name in ((0, ops, 32768, BF16_PEAK_TFLOPS, "mfma_loop_bf16"),
+                                            (1, ops8, 65536, INT8_PEAK_TOPS, "mfma_loop_i8")):
+        def mf(i, kind=kind, buf=buf):
+            rc = lib.w4_peak_mfma_loop(kind, ctypes.c_void_p(buf.data_ptr()), blocks, iters,
+                                       ctypes.c_void_p(mout.data_ptr()), ctypes.c_void_p(sid))
+            if rc != 0:
+                raise RuntimeError(f"w4_peak_mfma_loop failed ({rc})")
+        for i in range(3):
+            mf(i)
+        a, m = _stats(time_each(mf, 20))
+        work = blocks * 4 * iters * 4 * unit_ops
+        res[name] = {"avg_us": round(a * 1e6, 1), "T/s": round(work / a / 1e12, 1),
+                     "frac_of_peak": round(work / a / 1e12 / peak, 4),
+                     "note": f"{blocks} workgroups x 4 waves, {iters} rounds of 4 independent chains"}
+    del big, sink, mout
+
     src = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
     dst = torch.empty_like(src)
     csec = time_region(lambda i: dst.copy_(src), 10)
     copy_gbs = 2 * src.numel() * 4 / csec / 1e9
     del src, dst
-    dec = out.get("w4a16_small_batch", {}).get("M=1", {}).get("Wb", {}).get("GB/s")
     res["hbm_copy_1GiB"] = {"GB/s": round(copy_gbs, 1), "frac_of_8TBs": round(copy_gbs / HBM_PEAK_GBS, 4),
-                            "decode_Wb_frac_of_copy": round(dec / copy_gbs, 4) if dec else None,
                             "note": "read + write bytes of a plain device-to-device copy"}
     wd = w4.dequant_int4(*w4.quantize_pack_int4(to_dev(WL.weight("Wb")), g, torch.float16), g,
                          out_dtype=torch.bfloat16)
@@ -546,6 +656,22 @@ def kernel_only(args, w4, WL, torch, dev, to_dev, log):
         torch.cuda.synchronize()
         print(json.dumps({"kernel": "copy", "launches": n_launch, "read_bytes": nbytes,
                           "write_bytes": nbytes}), flush=True)
+        return 0
+    if args.kernel == "read":
+        import ctypes
+        lib = load_peaks_lib()
+        big = torch.empty(1 << 28, dtype=torch.int32, device=dev).random_()
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        nbytes = w4a16_bytes(1, 11008, 4096, 128)
+        nreg = (big.numel() * 4) // nbytes
+        sid = torch.cuda.current_stream(dev).cuda_stream
+        torch.cuda.synchronize()
+        for i in range(n_launch):
+            rc = lib.w4_peak_stream_read(ctypes.c_void_p(big.data_ptr() + (i % nreg) * nbytes), nbytes, 8,
+                                         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(sid))
+            assert rc == 0, rc
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel": "read", "launches": n_launch, "bytes_per_launch": nbytes}), flush=True)
         return 0
     if args.kernel == "gptq":
         import numpy as np

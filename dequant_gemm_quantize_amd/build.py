@@ -18,6 +18,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libw4.so")
+# measurement kernels (streaming read, matrix-instruction loops) for the
+# roofline denominators; a library of their own, outside the method's ABI
+PEAKS_SOURCES = ["peaks.hip"]
+PEAKS_LIB_PATH = os.path.join(HERE, "libw4peaks.so")
 
 SOURCES = ["api.cpp", "quant.hip", "gemv_generic.hip", "gemv_dot2.hip", "gemv_mfma.hip", "gemv_decode.hip", "gemm_mfma.hip", "gemm_w4a8.hip", "gemv_w4a8.hip", "gemv_w4a8_mfma.hip", "gptq.hip"]
 
@@ -56,9 +60,16 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link libw4.so; returns its path."""
+    """Compile every source and link libw4.so (and libw4peaks.so); returns
+    libw4.so's path."""
+    _build_lib(SOURCES, LIB_PATH, verbose, jobs)
+    _build_lib(PEAKS_SOURCES, PEAKS_LIB_PATH, verbose, jobs)
+    return LIB_PATH
+
+
+def _build_lib(sources, lib_path: str, verbose: bool, jobs: int) -> None:
     cc = hipcc()
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    srcs = [s for s in sources if os.path.exists(os.path.join(CSRC, s))]
     with tempfile.TemporaryDirectory(prefix="w4build_") as tmp:
         objs = []
         procs = []
@@ -75,11 +86,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 _wait(procs.pop(0), verbose)
         for p in procs:
             _wait(p, verbose)
-        tmp_lib = os.path.join(tmp, "libw4.so")
+        tmp_lib = os.path.join(tmp, os.path.basename(lib_path))
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
-        shutil.copyfile(tmp_lib, LIB_PATH + ".tmp")
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        shutil.copyfile(tmp_lib, lib_path + ".tmp")
+        os.replace(lib_path + ".tmp", lib_path)
 
 
 def _wait(item, verbose):

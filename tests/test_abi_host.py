@@ -317,3 +317,30 @@ def test_binding_checks_shapes_and_dtypes():
         w4.w4a16_matmul(x, p, s, z, 128)
     with pytest.raises(ValueError, match="GPU only"):
         w4.w4a8_matmul(torch.zeros(3, 256, dtype=torch.int8), torch.ones(3), p, s, z, 128)
+
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "w4_peaks.h")
+PEAKS_LIB = os.path.join(ROOT, "dequant_gemm_quantize_amd", "libw4peaks.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PEAKS_LIB), reason="libw4peaks.so not built")
+def test_peaks_library_exports_and_rejects():
+    """The measurement library exports what include/w4_peaks.h declares and
+    rejects bad arguments before any HIP call."""
+    text = re.sub(r"/\*.*?\*/", "", open(PEAKS_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^int\s+([a-z0-9_]+)\s*\(", text, flags=re.M)))
+    assert names == ["w4_peak_mfma_loop", "w4_peak_stream_read"]
+    raw = ctypes.CDLL(PEAKS_LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+    sr = raw.w4_peak_stream_read
+    sr.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    mf = raw.w4_peak_mfma_loop
+    mf.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    for args in ((None, 1024, 8, A, None), (A, 1000, 8, A, None), (A, 1024, 4, A, None),
+                 (U, 1024, 8, A, None), (A, 0, 8, A, None), (A, 1024, 8, None, None)):
+        assert sr(*args) == -1, args
+    for args in ((2, A, 512, 10, A, None), (0, None, 512, 10, A, None), (0, A, 0, 10, A, None),
+                 (1, A, 512, 0, A, None), (0, U, 512, 10, A, None)):
+        assert mf(*args) == -1, args
