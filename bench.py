@@ -157,22 +157,6 @@ def main(argv=None):
         del graphs
         return e0.elapsed_time(e1) / 1e3 / iters
 
-    def time_each(fn, iters):
-        """Per-launch durations (seconds) of fn(i), i = 0..iters-1: each
-        launch is bracketed by two HIP events on the launch stream and the
-        launches are issued eagerly, so every figure is one kernel's own
-        start-to-end time, the quantity a kernel trace records (no overlap
-        with neighbouring launches)."""
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(iters)]
-        torch.cuda.synchronize()
-        for i in range(iters):
-            ev[i][0].record(stream)
-            fn(i)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) / 1e3 for a, b in ev]
-
     if args.kernel is not None:
         return kernel_only(args, w4, WL, torch, dev, to_dev, log)
 
@@ -216,25 +200,15 @@ def main(argv=None):
 
     for i in range(args.warmup):
         dom(i)
-    nlaunch = max(100, args.steps)
-    durs = sorted(time_each(dom, nlaunch))
-    dsec = sum(durs) / len(durs)
-    dmed = durs[len(durs) // 2]
-    gsec = time_region(dom, args.steps)
+    dsec = time_region(dom, args.steps)
     dbytes = w4a16_bytes(1, 11008, 4096, g)
     achieved = dbytes / dsec / 1e9
     roof = {"kernel": "w4a16 decode, W [11008,4096] int4 g128, x bf16 [1,4096]",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_launch_us": round(dsec * 1e6, 3),
-            "median_launch_us": round(dmed * 1e6, 3),
-            "frac_at_median": round(dbytes / dmed / 1e9 / HBM_PEAK_GBS, 4),
-            "launches_timed": nlaunch,
-            "timing": "per-launch HIP event pairs on the launch stream, eager launches over the "
-                      "rotated weight copies (the kernel's own start-to-end time, as a kernel trace "
-                      "records it)",
-            "graph_replay_us_per_launch": round(gsec * 1e6, 3),
-            "graph_replay_frac": round(dbytes / gsec / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": dbytes, "traffic": None}
+            "timing": "HIP events on the launch stream around graph replays of back-to-back launches "
+                      "over the rotated weight copies",
+            "bytes_per_launch": dbytes, "traffic": None, "kernel_trace": None}
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as fh:
@@ -242,8 +216,10 @@ def main(argv=None):
         ent = tr.get("w4a16_decode_Wb")
         if ent and ent.get("src_hash") == src_hash():
             roof["traffic"] = ent.get("bytes_per_launch")
-    log(f"dominant kernel: {dsec * 1e6:.2f} us/launch (median {dmed * 1e6:.2f}), {achieved:.1f} GB/s; "
-        f"graph replay {gsec * 1e6:.2f} us per launch")
+            kt = ent.get("kernel_trace")
+            if kt:  # the rocprofv3 kernel trace of this kernel, same sources
+                roof["kernel_trace"] = dict(kt, frac_at_median=round(dbytes / kt["median_us"] / 1e3 / HBM_PEAK_GBS, 4))
+    log(f"dominant kernel: {dsec * 1e6:.2f} us/launch, {achieved:.1f} GB/s")
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -262,8 +238,8 @@ def main(argv=None):
     del q
 
     if not args.quick:
-        result["extra"] = extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, time_each, log,
-                                 copies, x1, dsec * 1e6)
+        result["extra"] = extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copies, x1,
+                                 dsec * 1e6)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, WL, np, log, wa, wb)
@@ -272,7 +248,7 @@ def main(argv=None):
     return 0
 
 
-def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, time_each, log, copies, x1, dom_us):
+def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copies, x1, dom_us):
     """Rates of every other step of the path; each is timed with HIP events."""
     out = {}
     g = 128
@@ -409,8 +385,8 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, time_each,
 
     out["llama7b_decode_32_layers"] = llama_decode(w4, torch, dev, time_region, log, g)
     out["gptq_Wb"] = gptq_bench(w4, torch, np, dev, time_region, log)
-    out["measured_peaks"] = measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copies,
-                                           x1, out, dom_us)
+    out["measured_peaks"] = measured_peaks(w4, WL, torch, dev, to_dev, time_region, log, copies, x1, out,
+                                           dom_us)
     return out
 
 
@@ -428,12 +404,7 @@ def load_peaks_lib():
     return lib
 
 
-def _stats(durs):
-    d = sorted(durs)
-    return sum(d) / len(d), d[len(d) // 2]
-
-
-def measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copies, x1, out, dom_us, g=128):
+def measured_peaks(w4, WL, torch, dev, to_dev, time_region, log, copies, x1, out, dom_us, g=128):
     """Context for the fractions above, measured in the same process:
     - the decode product with one weight copy (resident in the 256 MB
       Infinity Cache, so not an HBM figure);
@@ -446,7 +417,9 @@ def measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copi
       dequantized weight, run as a black box) on the M = 2048 shape."""
     import ctypes
     lib = load_peaks_lib()
-    sid = torch.cuda.current_stream(dev).cuda_stream
+
+    def sid():  # the stream being captured or run on, at call time
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     res = {}
     y = torch.empty((1, 11008), dtype=torch.bfloat16, device=dev)
     p, s, z = copies["Wb"][0]
@@ -463,25 +436,22 @@ def measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copi
 
     def rd(i, nbytes=dbytes, lanes=8, stride=dbytes, regions=nreg):
         rc = lib.w4_peak_stream_read(ctypes.c_void_p(base + (i % regions) * stride), nbytes, lanes,
-                                     ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(sid))
+                                     ctypes.c_void_p(sink.data_ptr()), sid())
         if rc != 0:
             raise RuntimeError(f"w4_peak_stream_read failed ({rc})")
     for i in range(5):
         rd(i)
-    avg, med = _stats(time_each(rd, 200))
-    gsec = time_region(rd, 200)
-    dec = dom_us
+    rsec = time_region(rd, 200)
     res["stream_read_decode_bytes"] = {
-        "bytes": dbytes, "avg_us": round(avg * 1e6, 3), "median_us": round(med * 1e6, 3),
-        "GB/s": round(dbytes / avg / 1e9, 1), "frac_of_8TBs": round(dbytes / avg / 1e9 / HBM_PEAK_GBS, 4),
-        "graph_replay_us": round(gsec * 1e6, 3),
-        "decode_Wb_frac_of_it": round(avg * 1e6 / dec, 4),
-        "note": "the decode product's byte count read once, 688+ workgroups of 256 lanes, 8 x 16 B "
+        "bytes": dbytes, "us": round(rsec * 1e6, 3), "GB/s": round(dbytes / rsec / 1e9, 1),
+        "frac_of_8TBs": round(dbytes / rsec / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_Wb_time_over_it": round(dom_us / (rsec * 1e6), 4),
+        "note": "the decode product's byte count read once, 732 workgroups of 256 lanes, 8 x 16 B "
                 "non-temporal loads per lane (the decode kernels' pattern), rotated over a 1 GiB buffer"}
     gib = big.numel() * 4
-    avg1, med1 = _stats(time_each(lambda i: rd(0, gib, 16, 0, 1), 20))
-    res["stream_read_1GiB"] = {"avg_us": round(avg1 * 1e6, 2), "GB/s": round(gib / avg1 / 1e9, 1),
-                               "frac_of_8TBs": round(gib / avg1 / 1e9 / HBM_PEAK_GBS, 4)}
+    gsec = time_region(lambda i: rd(0, gib, 16, 0, 1), 10)
+    res["stream_read_1GiB"] = {"us": round(gsec * 1e6, 2), "GB/s": round(gib / gsec / 1e9, 1),
+                               "frac_of_8TBs": round(gib / gsec / 1e9 / HBM_PEAK_GBS, 4)}
 
     # matrix-instruction loops on random operands
     ops = torch.randn(1024, dtype=torch.float32, device=dev).to(torch.bfloat16)  # 128 x 16 B of bf16
@@ -492,15 +462,15 @@ def measured_peaks(w4, WL, torch, dev, to_dev, time_region, time_each, log, copi
                                             (1, ops8, 65536, INT8_PEAK_TOPS, "mfma_loop_i8")):
         def mf(i, kind=kind, buf=buf):
             rc = lib.w4_peak_mfma_loop(kind, ctypes.c_void_p(buf.data_ptr()), blocks, iters,
-                                       ctypes.c_void_p(mout.data_ptr()), ctypes.c_void_p(sid))
+                                       ctypes.c_void_p(mout.data_ptr()), sid())
             if rc != 0:
                 raise RuntimeError(f"w4_peak_mfma_loop failed ({rc})")
         for i in range(3):
             mf(i)
-        a, m = _stats(time_each(mf, 20))
+        msec = time_region(mf, 10)
         work = blocks * 4 * iters * 4 * unit_ops
-        res[name] = {"avg_us": round(a * 1e6, 1), "T/s": round(work / a / 1e12, 1),
-                     "frac_of_peak": round(work / a / 1e12 / peak, 4),
+        res[name] = {"us": round(msec * 1e6, 1), "T/s": round(work / msec / 1e12, 1),
+                     "frac_of_peak": round(work / msec / 1e12 / peak, 4),
                      "note": f"{blocks} workgroups x 4 waves, {iters} rounds of 4 independent chains"}
     del big, sink, mout
 

@@ -253,10 +253,28 @@ int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
   return hip_status(w4::launch_act_quant(x, x_dtype, m, k, xq, x_scale, stream), fn);
 }
 
-int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
-                 const void* scales, const void* zeros, int sz_dtype, int64_t n,
-                 int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
-  static const char* fn = "w4a16_matmul";
+// Which kernel w4a16_matmul runs for a (validated) shape.
+enum class W16Path { DOT2, DECODE, GEMV, GEMM, GENERIC };
+
+static W16Path w4a16_path(int x_dtype, int64_t m, int64_t k, int32_t group_size) {
+  // Kernel choice (bf16 activations): one token, groups of at least 128, K up
+  // to 12288 -> the dot2 GEMV; up to four tokens with the activations fitting
+  // in LDS, groups of a multiple of 128 -> the LDS decode kernel; up to 128
+  // tokens, groups of a multiple of 128 -> the MFMA GEMV (in launches of up
+  // to 64 tokens); more tokens -> the MFMA GEMM; everything else (fp32
+  // activations, smaller group sizes at few tokens) -> the general kernel.
+  if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size)) return W16Path::DOT2;
+  if (x_dtype == W4_BF16 && m <= 4 && group_size % 128 == 0 && w4::decode_lds_fits(m, k))
+    return W16Path::DECODE;
+  if (x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size)) return W16Path::GEMV;
+  if (x_dtype == W4_BF16 && w4::gemm_fits(m, k, group_size)) return W16Path::GEMM;
+  return W16Path::GENERIC;
+}
+
+static int w4a16_common(const char* fn, const void* x, int x_dtype, int64_t m, int64_t k,
+                        const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                        int64_t n, int32_t group_size, void* y, int y_dtype, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
   if (x_dtype != W4_F32 && x_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: x dtype %d must be W4_F32 or W4_BF16", fn, x_dtype);
@@ -269,32 +287,56 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
   W4_TRY(check_ptr(fn, "scales", scales));
   W4_TRY(check_ptr(fn, "zeros", zeros));
   W4_TRY(check_ptr(fn, "y", y));
-  // Kernel choice (bf16 activations): one token, groups of at least 128, K up
-  // to 12288 -> the dot2 GEMV; up to four tokens with the activations fitting
-  // in LDS, groups of a multiple of 128 -> the LDS decode kernel; up to 128
-  // tokens, groups of a multiple of 128 -> the MFMA GEMV (in launches of up
-  // to 64 tokens); more tokens -> the MFMA GEMM; everything else (fp32
-  // activations, smaller group sizes at few tokens) -> the general kernel.
-  if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size))
-    return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
-                                            group_size, y, y_dtype, stream),
-                      fn);
-  const bool dec = x_dtype == W4_BF16 && m <= 4 && group_size % 128 == 0;
-  if (dec && w4::decode_lds_fits(m, k))
-    return hip_status(w4::launch_w4a16_decode(x, m, k, packed, scales, zeros, sz_dtype, n,
+  if (ws != nullptr && ws_bytes > 0 && !aligned16(ws))
+    return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+  switch (w4a16_path(x_dtype, m, k, group_size)) {
+    case W16Path::DOT2:
+      return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
-                      fn);
-  if (x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size))
-    return hip_status(w4::launch_w4a16_gemv(x, m, k, packed, scales, zeros, sz_dtype, n,
-                                            group_size, y, y_dtype, stream),
-                      fn);
-  if (x_dtype == W4_BF16 && w4::gemm_fits(m, k, group_size))
-    return hip_status(w4::launch_w4a16_gemm(x, m, k, packed, scales, zeros, sz_dtype, n,
-                                            group_size, y, y_dtype, stream),
-                      fn);
-  return hip_status(w4::launch_w4a16_generic(x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
-                                             group_size, y, y_dtype, stream),
-                    fn);
+                        fn);
+    case W16Path::DECODE:
+      return hip_status(w4::launch_w4a16_decode(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                                group_size, y, y_dtype, stream),
+                        fn);
+    case W16Path::GEMV:
+      return hip_status(w4::launch_w4a16_gemv(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                              group_size, y, y_dtype, stream),
+                        fn);
+    case W16Path::GEMM:
+      return hip_status(w4::launch_w4a16_gemm(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                              group_size, y, y_dtype, ws, ws_bytes, stream),
+                        fn);
+    default:
+      return hip_status(w4::launch_w4a16_generic(x, x_dtype, m, k, packed, scales, zeros, sz_dtype,
+                                                 n, group_size, y, y_dtype, stream),
+                        fn);
+  }
+}
+
+int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                 const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                 int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
+  return w4a16_common("w4a16_matmul", x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
+                      group_size, y, y_dtype, nullptr, 0, stream);
+}
+
+size_t w4a16_matmul_workspace_size(int64_t m, int64_t k, int64_t n, int32_t group_size,
+                                   int x_dtype) {
+  // Shapes the other entry points would reject need no workspace.
+  if (m <= 0 || n <= 0 || k <= 0 || k > kMaxK || group_size <= 0 || group_size % 32 != 0 ||
+      k % group_size != 0 || n > kMaxElems / k || m > 0x7fffffffLL || m > kMaxElems / k ||
+      m > kMaxElems / n)
+    return 0;
+  if (w4a16_path(x_dtype, m, k, group_size) != W16Path::GEMM) return 0;
+  return w4::gemm_workspace_bytes(m, k, n, group_size);
+}
+
+int w4a16_matmul_ws(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                    const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                    int32_t group_size, void* y, int y_dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return w4a16_common("w4a16_matmul_ws", x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
+                      group_size, y, y_dtype, workspace, workspace_bytes, stream);
 }
 
 int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,

@@ -52,16 +52,24 @@ template <> struct GS<float> {
 };
 
 // 8 codes of a packed word -> 8 bf16 weights (natural column order),
-// w = RNE(fma(q, s, b)) with b = -zp * s.
+// w = RNE(fma(q, s, b)) with b = -zp * s.  Each code is converted straight
+// from its byte of the masked word (v_cvt_f32_ubyte0..3).
 __device__ __forceinline__ u32x4 dequant8(uint32_t p, float s, float b) {
-  const uint32_t lo = p & 0x0f0f0f0fu;         // codes 0, 2, 4, 6
-  const uint32_t hi = (p >> 4) & 0x0f0f0f0fu;  // codes 1, 3, 5, 7
+  uint32_t lo = p & 0x0f0f0f0fu;         // codes 0, 2, 4, 6
+  uint32_t hi = (p >> 4) & 0x0f0f0f0fu;  // codes 1, 3, 5, 7
+  // The empty asm emits nothing; it hides the masks from the combiner, which
+  // would otherwise fold each byte's mask into a v_bfe_u32 ahead of the
+  // conversion instead of converting the byte in place.
+  asm("" : "+v"(lo), "+v"(hi));
   float w[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[2 * i] = fmaf((float)((lo >> (8 * i)) & 0xffu), s, b);
-    w[2 * i + 1] = fmaf((float)((hi >> (8 * i)) & 0xffu), s, b);
-  }
+  w[0] = fmaf((float)(uint8_t)lo, s, b);
+  w[1] = fmaf((float)(uint8_t)hi, s, b);
+  w[2] = fmaf((float)(uint8_t)(lo >> 8), s, b);
+  w[3] = fmaf((float)(uint8_t)(hi >> 8), s, b);
+  w[4] = fmaf((float)(uint8_t)(lo >> 16), s, b);
+  w[5] = fmaf((float)(uint8_t)(hi >> 16), s, b);
+  w[6] = fmaf((float)(lo >> 24), s, b);
+  w[7] = fmaf((float)(hi >> 24), s, b);
   u32x4 r;
   bf16x2 t;
   t = bf16x2{(__bf16)w[0], (__bf16)w[1]}; r.x = __builtin_bit_cast(uint32_t, t);
@@ -69,6 +77,14 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t p, float s, float b) {
   t = bf16x2{(__bf16)w[4], (__bf16)w[5]}; r.z = __builtin_bit_cast(uint32_t, t);
   t = bf16x2{(__bf16)w[6], (__bf16)w[7]}; r.w = __builtin_bit_cast(uint32_t, t);
   return r;
+}
+
+// Raw buffer resource over `base` (gfx9 word 3: 32-bit data format, no
+// swizzle).  Loads through it take a uniform base, a per-lane VGPR offset and
+// a uniform SGPR offset, so advancing a K step is a scalar add.  Offsets here
+// stay below 2^31; the range check never triggers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
 template <typename TY>
@@ -82,11 +98,23 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v) {
 
 }  // namespace
 
-template <typename TS, typename TY>
+// G64: g % 64 == 0, so a K step lies in one group, the same for every
+// lane: its index is umulhi(ks, gmagic) with gmagic = ceil(2^32 / (g / 64)),
+// or ks itself when g = 64 (gmagic = 0: 2^32 does not fit).
+// Otherwise each lane's 16 columns lie in one group (g % 32 == 0): index
+// umulhi(c16, gmagic), c16 = the 16-column piece, gmagic = ceil(2^32 /
+// (g / 16)).  Both quotients are exact while the dividend times the divisor
+// stays below 2^32, which gemm_fits guarantees.
+// Split K: workgroup (tile, s = blockIdx.y) covers K steps [s * kps,
+// min(nks, (s + 1) * kps)) and, when `part` is set, writes its float32 partial
+// tile to part + s * pstride as [M][N] (y is then unused; pstride is M * N
+// rounded up to a multiple of 4); k_splitk_reduce adds the splits.
+template <typename TS, typename TY, bool G64>
 __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
-    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
-    void* __restrict__ y, int tiles_m, int tiles_n) {
+    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int64_t ng,
+    uint32_t gmagic, void* __restrict__ y, int tiles_m, int tiles_n, int kps,
+    float* __restrict__ part, int64_t pstride) {
   typedef typename GS<TS>::T R;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sA = smem;                 // [2][BM][LDS_ROW]
@@ -111,31 +139,39 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
   const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*64, cols wn*64
 
   // ---- global -> register assignment ----------------------------------------
+  // Every address is a uniform base (advanced by the K step) plus a fixed
+  // 32-bit lane offset.  Rows past M or N repeat the last row.
   // x: 4 rounds of 64 rows; lane (t & 7) takes 16 bytes of a row's 128.
+  // Round r's base row is min(m0 + 64 r, M - 1), so lane offsets are >= 0
+  // and below 64 rows of K bf16 (< 2^30 bytes).
   const int xr = tid >> 3, xc = tid & 7;
-  const uint16_t* xt = x + m0 * K;  // tile base (uniform); per-lane offsets below
-  int xo[4];
+  __amdgpu_buffer_rsrc_t xrs[4];
+  uint32_t xo[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    int64_t row = m0 + xr + 64 * r;
-    row = row < M ? row : M - 1;
-    xo[r] = (int)((row - m0) * K) + 8 * xc;  // elements, + 64 * kstep
+    const int64_t rb = m0 + 64 * r < M ? m0 + 64 * r : M - 1;
+    const int64_t row = m0 + xr + 64 * r < M ? m0 + xr + 64 * r : M - 1;
+    xrs[r] = buf_rsrc((const char*)x + rb * K * 2);
+    xo[r] = (uint32_t)((row - rb) * K * 2) + 16u * (uint32_t)xc;
   }
-  // W: 4 lanes per row, 8 bytes (16 codes) each.
+  // W: 4 lanes per row, 8 bytes (16 codes) each; offsets below 128 rows of
+  // K/2 bytes (< 2^29).  Scales and zeros: the tile's 128 rows of K/g.
   const int wr = tid >> 2, wq4 = tid & 3;
-  int64_t wrow = n0 + wr;
-  wrow = wrow < N ? wrow : N - 1;
-  const uint32_t* wp = (const uint32_t*)(packed + wrow * (K / 2)) + 2 * wq4;  // + 8 * kstep
-  const int64_t ng = K / g;
-  const R* sp = (const R*)scales + wrow * ng;
-  const R* zp = (const R*)zeros + wrow * ng;
+  const int64_t wrow = n0 + wr < N ? n0 + wr : N - 1;
+  const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(packed + n0 * (K / 2));
+  const uint32_t wo = (uint32_t)((wrow - n0) * (K / 2)) + 8u * (uint32_t)wq4;
+  const __amdgpu_buffer_rsrc_t srs = buf_rsrc((const R*)scales + n0 * ng);
+  const __amdgpu_buffer_rsrc_t zrs = buf_rsrc((const R*)zeros + n0 * ng);
+  const uint32_t so = (uint32_t)((wrow - n0) * ng) * (uint32_t)sizeof(R);  // bytes
 
   // Global data runs D K-steps ahead of the MFMAs, in D register stages
   // (stage = K-step mod D): loads for step ks + D are issued while step ks
   // computes, and step ks + 1 is dequantized into the other LDS buffer after
   // it.  Every wait is then for loads issued D - 1 steps earlier.
   constexpr int D = W4_GEMM_DEPTH;
-  const int nks = (int)(K / BK);
+  const int ks0 = (int)blockIdx.y * kps;  // first K step of this split
+  const int nks_all = (int)(K / BK);
+  const int nks = (nks_all - ks0 < kps ? nks_all - ks0 : kps) + ks0;  // one past the last step
   u32x4 xv[D][4];
   u32x2 wv[D];
   R sv[D], zv[D];
@@ -146,11 +182,19 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     constexpr int u = decltype(stage)::value;
     ks = ks < nks ? ks : nks - 1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xv[u][r] = *(const u32x4*)(xt + xo[r] + 64 * ks);
-    wv[u] = *(const u32x2*)(wp + 8 * ks);
-    const int gi = (ks * BK + 16 * wq4) / g;
-    sv[u] = sp[gi];
-    zv[u] = zp[gi];
+    for (int r = 0; r < 4; ++r)
+      xv[u][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[r], xo[r], ks * (2 * BK), 0));
+    wv[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, wo, ks * (BK / 2), 0));
+    uint32_t vo = so, go = 0;  // group offset: uniform (G64) or per lane
+    if constexpr (G64) go = (gmagic ? __umulhi((uint32_t)ks, gmagic) : (uint32_t)ks) * (uint32_t)sizeof(R);
+    else vo += __umulhi((uint32_t)(ks * (BK / 16) + wq4), gmagic) * (uint32_t)sizeof(R);
+    if constexpr (sizeof(R) == 2) {
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b16(srs, vo, go, 0);
+      zv[u] = __builtin_amdgcn_raw_buffer_load_b16(zrs, vo, go, 0);
+    } else {
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b32(srs, vo, go, 0);
+      zv[u] = __builtin_amdgcn_raw_buffer_load_b32(zrs, vo, go, 0);
+    }
   };
   auto lstore = [&](int lstage, auto stage) {
     constexpr int u = decltype(stage)::value;
@@ -191,11 +235,14 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     }
   };
 
+  // Steps are counted from this split's first one: local step t is K step
+  // ks0 + t (gload clamps past the split's last step, whose loads are never
+  // used).
   // prologue: steps 0 .. D-1 in flight, step 0 in LDS buffer 0
-  gload(0, std::integral_constant<int, 0>{});
-  if constexpr (D > 1) gload(1, std::integral_constant<int, 1 % D>{});
-  if constexpr (D > 2) gload(2, std::integral_constant<int, 2 % D>{});
-  if constexpr (D > 3) gload(3, std::integral_constant<int, 3 % D>{});
+  gload(ks0 + 0, std::integral_constant<int, 0>{});
+  if constexpr (D > 1) gload(ks0 + 1, std::integral_constant<int, 1 % D>{});
+  if constexpr (D > 2) gload(ks0 + 2, std::integral_constant<int, 2 % D>{});
+  if constexpr (D > 3) gload(ks0 + 3, std::integral_constant<int, 3 % D>{});
   lstore(0, std::integral_constant<int, 0>{});
   __syncthreads();
 
@@ -204,22 +251,23 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
   // the idle buffer, which is never read), barrier.
   auto step = [&](int ks, auto stage) {
     constexpr int u = decltype(stage)::value;  // ks mod D
-    gload(ks + D, stage);  // reuses register stage u: step ks is already in LDS
+    gload(ks0 + ks + D, stage);  // reuses register stage u: step ks is already in LDS
     mma(ks & 1);
     lstore((ks + 1) & 1, std::integral_constant<int, (u + 1) % D>{});
     __syncthreads();
   };
-  const int nmain = nks - nks % D;
+  const int nloc = nks - ks0;  // steps of this split
+  const int nmain = nloc - nloc % D;
   for (int ks = 0; ks < nmain; ks += D) {
     step(ks, std::integral_constant<int, 0>{});
     if constexpr (D > 1) step(ks + 1, std::integral_constant<int, 1 % D>{});
     if constexpr (D > 2) step(ks + 2, std::integral_constant<int, 2 % D>{});
     if constexpr (D > 3) step(ks + 3, std::integral_constant<int, 3 % D>{});
   }
-  // tail: the remaining nks % D steps (register stage of step ks is ks mod D)
-  if (nmain < nks) step(nmain, std::integral_constant<int, 0>{});
-  if constexpr (D > 1) if (nmain + 1 < nks) step(nmain + 1, std::integral_constant<int, 1 % D>{});
-  if constexpr (D > 2) if (nmain + 2 < nks) step(nmain + 2, std::integral_constant<int, 2 % D>{});
+  // tail: the remaining nloc % D steps (register stage of step ks is ks mod D)
+  if (nmain < nloc) step(nmain, std::integral_constant<int, 0>{});
+  if constexpr (D > 1) if (nmain + 1 < nloc) step(nmain + 1, std::integral_constant<int, 1 % D>{});
+  if constexpr (D > 2) if (nmain + 2 < nloc) step(nmain + 2, std::integral_constant<int, 2 % D>{});
 
   // ---- epilogue: lane holds rows 8(r/4) + 4(lane/32) + r%4, column lane%32 --
 #pragma unroll
@@ -230,40 +278,129 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M && n < N) store1<TY>(y, m * N + n, acc[i][j][r]);
+        if (m < M && n < N) {
+          if (part != nullptr)
+            part[(int64_t)blockIdx.y * pstride + m * N + n] = acc[i][j][r];
+          else
+            store1<TY>(y, m * N + n, acc[i][j][r]);
+        }
       }
     }
 }
 
-bool gemm_fits(int64_t m, int64_t k, int g) { return m > 16 && k % BK == 0 && g % 32 == 0; }
+// y[i] = sum over s = 0 .. S-1, in that order, of part[s * pstride + i]
+// (float32), rounded once to y's type; 4 consecutive outputs per thread
+// (pstride % 4 == 0 keeps every 16-byte load aligned; the last group of
+// fewer than 4 outputs is added element by element).
+template <typename TY>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int S, int64_t MN,
+                                                       int64_t pstride, void* __restrict__ y) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= MN) return;
+  if (i4 + 4 <= MN) {
+    f32x4 a = *(const f32x4*)(part + i4);
+    for (int s = 1; s < S; ++s) a += *(const f32x4*)(part + (int64_t)s * pstride + i4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store1<TY>(y, i4 + j, a[j]);
+  } else {
+    for (int64_t i = i4; i < MN; ++i) {
+      float a = part[i];
+      for (int s = 1; s < S; ++s) a += part[(int64_t)s * pstride + i];
+      store1<TY>(y, i, a);
+    }
+  }
+}
 
-template <typename TS, typename TY>
+// The group index of a K step (g % 64 == 0) or of a 16-column piece is an
+// exact magic-number quotient while dividend x divisor < 2^32: K/64 * g/64
+// or K/16 * g/16 below 2^32.  Larger K * g go to the general kernel.
+bool gemm_fits(int64_t m, int64_t k, int g) {
+  if (!(m > 16 && k % BK == 0 && g % 32 == 0)) return false;
+  return g % 64 == 0 ? (k / 64) * (g / 64) < ((int64_t)1 << 32) : (k / 16) * (g / 16) < ((int64_t)1 << 32);
+}
+
+// ceil(2^32 / d) for d >= 2; 0 for d = 1 (the kernels then take the dividend itself).
+static uint32_t magic_ceil(uint32_t d) { return d < 2 ? 0u : (uint32_t)((((uint64_t)1 << 32) + d - 1) / d); }
+
+// Split-K plan: shapes whose 256 x 128 tiles fill fewer than half of the 256
+// CUs (the [4096, 11008] down projection below 513 tokens has 32 or 64)
+// split K so that about 256 workgroups run, at least 8 K steps each, with the
+// float32 partials within kSplitKMaxBytes.
+struct SplitK {
+  int s = 1, kps = 0;
+  int64_t pstride = 0;  // floats per split's partial: M * N rounded up to a multiple of 4
+  size_t bytes = 0;
+};
+static SplitK splitk_plan(int64_t m, int64_t k, int64_t n) {
+  SplitK p;
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int64_t nks = k / BK;
+  p.kps = (int)nks;
+  if (tiles >= 128) return p;
+  int64_t s = (256 + tiles - 1) / tiles;
+  if (s > nks / 8) s = nks / 8;
+  const int64_t pstride = (m * n + 3) / 4 * 4;
+  const int64_t fit = (int64_t)(kSplitKMaxBytes / ((size_t)pstride * 4));
+  if (s > fit) s = fit;
+  if (s < 2) return p;
+  p.kps = (int)((nks + s - 1) / s);
+  p.s = (int)((nks + p.kps - 1) / p.kps);
+  p.pstride = pstride;
+  p.bytes = (size_t)p.s * (size_t)pstride * 4;
+  return p;
+}
+
+size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int g) {
+  if (!gemm_fits(m, k, g)) return 0;
+  const SplitK p = splitk_plan(m, k, n);
+  return p.s > 1 ? p.bytes : 0;
+}
+
+template <typename TS, typename TY, bool G64>
 static hipError_t gemm_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
                           const void* scales, const void* zeros, int64_t n, int g, void* y,
-                          hipStream_t st) {
+                          void* ws, size_t ws_bytes, hipStream_t st) {
   static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
   hipError_t e = once_per_device(attr_done, [] {
-    return hipFuncSetAttribute((const void*)k_w4a16_gemm<TS, TY>,
+    return hipFuncSetAttribute((const void*)k_w4a16_gemm<TS, TY, G64>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
   });
   if (e != hipSuccess) return e;
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  k_w4a16_gemm<TS, TY><<<grid, 512, kGemmLds, st>>>(x, m, k, packed, scales, zeros, n, g, y,
-                                                   tiles_m, tiles_n);
+  const uint32_t gm = magic_ceil((uint32_t)(G64 ? g / 64 : g / 16));
+  SplitK p = splitk_plan(m, k, n);
+  if (p.s > 1 && (ws == nullptr || ws_bytes < p.bytes)) p = SplitK{1, (int)(k / BK), 0, 0};
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.s);
+  float* part = p.s > 1 ? (float*)ws : nullptr;
+  k_w4a16_gemm<TS, TY, G64><<<grid, 512, kGemmLds, st>>>(x, m, k, packed, scales, zeros, n, k / g, gm, y,
+                                                        tiles_m, tiles_n, p.kps, part, p.pstride);
+  if (p.s > 1) {
+    const int64_t mn = m * n;
+    const dim3 rgrid((unsigned)((mn + 1023) / 1024));
+    k_splitk_reduce<TY><<<rgrid, 256, 0, st>>>(part, p.s, mn, p.pstride, y);
+  }
   return hipGetLastError();
+}
+
+template <typename TS, typename TY>
+static hipError_t gemm_go_g(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
+                            const void* scales, const void* zeros, int64_t n, int g, void* y,
+                            void* ws, size_t ws_bytes, hipStream_t st) {
+  if (g % 64 == 0) return gemm_go<TS, TY, true>(x, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
+  return gemm_go<TS, TY, false>(x, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
 }
 
 hipError_t launch_w4a16_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
-                             int g, void* y, int y_dtype, hipStream_t st) {
+                             int g, void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t st) {
   const uint16_t* xb = (const uint16_t*)x;
   if (sz_dtype == W4_F16) {
-    if (y_dtype == W4_F32) return gemm_go<_Float16, float>(xb, m, k, packed, scales, zeros, n, g, y, st);
-    return gemm_go<_Float16, __bf16>(xb, m, k, packed, scales, zeros, n, g, y, st);
+    if (y_dtype == W4_F32)
+      return gemm_go_g<_Float16, float>(xb, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
+    return gemm_go_g<_Float16, __bf16>(xb, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
   }
-  if (y_dtype == W4_F32) return gemm_go<float, float>(xb, m, k, packed, scales, zeros, n, g, y, st);
-  return gemm_go<float, __bf16>(xb, m, k, packed, scales, zeros, n, g, y, st);
+  if (y_dtype == W4_F32) return gemm_go_g<float, float>(xb, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
+  return gemm_go_g<float, __bf16>(xb, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
 }
 
 }  // namespace w4

@@ -84,17 +84,22 @@ int w4_peak_stream_read(const void* src, int64_t bytes, int32_t loads_per_lane, 
                         hipStream_t stream) {
   if (src == nullptr || sink == nullptr || !w4::aligned16(src)) return W4_PEAK_EINVAL;
   if (bytes <= 0 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40)) return W4_PEAK_EINVAL;
-  if (loads_per_lane != 8 && loads_per_lane != 16) return W4_PEAK_EINVAL;
+  if (loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 && loads_per_lane != 16 &&
+      loads_per_lane != 32)
+    return W4_PEAK_EINVAL;
   const int64_t nchunks = bytes / 16;
   const int64_t per_block = 256 * (int64_t)loads_per_lane;
   const int64_t blocks = (nchunks + per_block - 1) / per_block;
   if (blocks > 0x7fffffff) return W4_PEAK_EINVAL;
   const dim3 grid((unsigned)blocks);
   const w4::u32x4* s = (const w4::u32x4*)src;
-  if (loads_per_lane == 8)
-    w4::k_stream_read<8><<<grid, 256, 0, stream>>>(s, nchunks, sink);
-  else
-    w4::k_stream_read<16><<<grid, 256, 0, stream>>>(s, nchunks, sink);
+  switch (loads_per_lane) {
+    case 2: w4::k_stream_read<2><<<grid, 256, 0, stream>>>(s, nchunks, sink); break;
+    case 4: w4::k_stream_read<4><<<grid, 256, 0, stream>>>(s, nchunks, sink); break;
+    case 8: w4::k_stream_read<8><<<grid, 256, 0, stream>>>(s, nchunks, sink); break;
+    case 16: w4::k_stream_read<16><<<grid, 256, 0, stream>>>(s, nchunks, sink); break;
+    default: w4::k_stream_read<32><<<grid, 256, 0, stream>>>(s, nchunks, sink); break;
+  }
   return hipGetLastError() == hipSuccess ? W4_PEAK_OK : W4_PEAK_EHIP;
 }
 

@@ -64,10 +64,15 @@ hipError_t launch_w4a16_gemv(const void* x, int64_t m, int64_t k, const uint8_t*
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
                              int g, void* y, int y_dtype, hipStream_t st);
 bool gemv_mfma_fits(int64_t m, int64_t k, int g);
+// ws: optional float32 workspace for split K (nullptr or too small: no split).
 hipError_t launch_w4a16_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
-                             int g, void* y, int y_dtype, hipStream_t st);
+                             int g, void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t st);
 bool gemm_fits(int64_t m, int64_t k, int g);
+// Bytes of workspace the GEMM uses for split K on this shape (0: it does not
+// split); never above kSplitKMaxBytes.
+constexpr size_t kSplitKMaxBytes = (size_t)32 << 20;
+size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int g);
 hipError_t launch_w4a8_gemv(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                             const uint8_t* packed, const void* scales, const void* zeros,
                             int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st);

@@ -176,6 +176,38 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
                  int32_t group_size, void* y, int y_dtype, hipStream_t stream);
 
 /*
+ * w4a16_matmul_workspace_size / w4a16_matmul_ws -- w4a16_matmul with a
+ * caller-provided device workspace ([P3] Step 2 and [P4] Step 5; the
+ * workspace changes how the product is scheduled, not what it computes).
+ *
+ * Shapes whose 256 x 128 output tiles fill fewer than half of the GPU's 256
+ * compute units (for example the [4096, 11008] down projection at 129 to 512
+ * tokens) split K across workgroups: each writes a float32 partial tile to
+ * the workspace and a second kernel adds the partials in a fixed order and
+ * rounds once to y_dtype.  Results are deterministic and meet the accuracy
+ * bound of w4a16_matmul.
+ *
+ * w4a16_matmul_workspace_size returns the bytes of workspace that let
+ * w4a16_matmul_ws split K for this shape: 0 when it would not split (it then
+ * behaves as w4a16_matmul), at most 32 MiB.  It depends only on its
+ * arguments, enqueues nothing and returns 0 for arguments the other calls
+ * reject.
+ *
+ * w4a16_matmul_ws takes w4a16_matmul's arguments plus `workspace` (device
+ * memory, 16-byte aligned, owned by the caller; its contents on entry are
+ * ignored and on return unspecified) of `workspace_bytes`.  With
+ * workspace_bytes below the queried size, or workspace NULL, it runs
+ * exactly as w4a16_matmul.  Calls that overlap on one workspace race.
+ * Errors as w4a16_matmul, plus W4_EINVAL for a misaligned workspace.
+ */
+size_t w4a16_matmul_workspace_size(int64_t m, int64_t k, int64_t n, int32_t group_size,
+                                   int x_dtype);
+int w4a16_matmul_ws(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                    const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                    int32_t group_size, void* y, int y_dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * w4a8_matmul -- y[m, n] = x_scale[m] * sum_k xq[m, k] * dequant(W)[n, k]
  * ([P1] Architecture Overview, Step 5), with xq/x_scale as produced by
  * quantize_act_int8.  Per group the integer sum of xq * (q - zp) is exact

@@ -21,7 +21,7 @@ enum { W4_PEAK_BF16 = 0, W4_PEAK_I8 = 1 };
 /*
  * w4_peak_stream_read -- reads `bytes` (a multiple of 16, > 0) of `src`
  * (16-byte aligned) once.  Workgroups of 256 lanes; each lane issues
- * loads_per_lane (8 or 16) 16-byte non-temporal loads, each wavefront load
+ * loads_per_lane (2, 4, 8, 16 or 32) 16-byte non-temporal loads, each wavefront load
  * instruction covering 1 KB contiguous -- the pattern of the decode kernels
  * (8 loads per lane reproduces their geometry on the [11008, 4096] weight).
  * The loaded words are xor-folded; `sink` (4 bytes) is written only when the

@@ -338,9 +338,29 @@ def test_peaks_library_exports_and_rejects():
     mf = raw.w4_peak_mfma_loop
     mf.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                    ctypes.c_void_p]
-    for args in ((None, 1024, 8, A, None), (A, 1000, 8, A, None), (A, 1024, 4, A, None),
+    for args in ((None, 1024, 8, A, None), (A, 1000, 8, A, None), (A, 1024, 3, A, None),
                  (U, 1024, 8, A, None), (A, 0, 8, A, None), (A, 1024, 8, None, None)):
         assert sr(*args) == -1, args
     for args in ((2, A, 512, 10, A, None), (0, None, 512, 10, A, None), (0, A, 0, 10, A, None),
                  (1, A, 512, 0, A, None), (0, U, 512, 10, A, None)):
         assert mf(*args) == -1, args
+
+
+def test_workspace_size_query(lib):
+    """w4a16_matmul_workspace_size is host-only: split K for the down
+    projection [4096, 11008] below 513 tokens (32 MiB at most), none for the
+    M = 2048 prefill, decode shapes or invalid arguments."""
+    import dequant_gemm_quantize_amd as w4
+    assert w4.w4a16_matmul_workspace_size(256, 11008, 4096, 128) == 32 << 20
+    assert 0 < w4.w4a16_matmul_workspace_size(129, 11008, 4096, 128) <= 32 << 20
+    assert w4.w4a16_matmul_workspace_size(2048, 11008, 4096, 128) == 0
+    assert w4.w4a16_matmul_workspace_size(2048, 4096, 11008, 128) == 0
+    assert w4.w4a16_matmul_workspace_size(1, 4096, 11008, 128) == 0
+    assert w4.w4a16_matmul_workspace_size(64, 11008, 4096, 128) == 0      # GEMV path
+    assert w4.w4a16_matmul_workspace_size(256, 11008, 4096, 100) == 0     # invalid group
+    assert w4.w4a16_matmul_workspace_size(256, 11008, 4096, 128, torch_float32()) == 0  # fp32 x: general kernel
+
+
+def torch_float32():
+    import torch
+    return torch.float32

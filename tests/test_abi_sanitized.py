@@ -25,9 +25,11 @@ pytestmark = pytest.mark.skipif(shutil.which("g++") is None or not os.path.exist
 def _stubs() -> str:
     src = open(os.path.join(CSRC, "w4_internal.h")).read()
     out = ['#include "w4_internal.h"', "namespace w4 {"]
-    for ret, name, args in re.findall(r"^(hipError_t|bool)\s+(\w+)\(([^;]*?)\);", src, flags=re.M | re.S):
+    for ret, name, args in re.findall(r"^(hipError_t|bool|size_t)\s+(\w+)\(([^;]*?)\);", src, flags=re.M | re.S):
         if name == "gptq_group_ok":      # the one predicate the validation depends on
             body = "return g > 0 && g % 32 == 0 && (g <= 128 ? 128 % g == 0 : g % 128 == 0);"
+        elif ret == "size_t":
+            body = "return 0;"
         else:
             body = "return hipSuccess;" if ret == "hipError_t" else "return true;"
         out.append(f"{ret} {name}({args}) {{ {body} }}")
@@ -78,6 +80,13 @@ int main() {
     expect(w4a16_matmul(A, W4_BF16, m, 4096, P, A, A, W4_F16, 11008, 128, A, W4_BF16, nullptr), W4_OK, "w4a16 ok");
   expect(w4a16_matmul(A, W4_F32, 5, 256, P, A, A, W4_F32, 96, 32, A, W4_F32, nullptr), W4_OK, "w4a16 f32");
   expect(w4a16_matmul(A, W4_BF16, BIG, 4096, P, A, A, W4_F16, BIG, 128, A, W4_BF16, nullptr), W4_EINVAL, "w4a16 huge");
+  expect(w4a16_matmul_ws(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, A, W4_BF16, A, 4096, nullptr), W4_OK, "w4a16 ws ok");
+  expect(w4a16_matmul_ws(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, A, W4_BF16, nullptr, 0, nullptr), W4_OK, "w4a16 ws null");
+  expect(w4a16_matmul_ws(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, A, W4_BF16, U, 4096, nullptr), W4_EINVAL, "w4a16 ws misaligned");
+  expect(w4a16_matmul_ws(A, W4_BF16, BIG, 4096, P, A, A, W4_F16, BIG, 128, A, W4_BF16, A, 4096, nullptr), W4_EINVAL, "w4a16 ws huge");
+  expect((int)w4a16_matmul_workspace_size(BIG, BIG, BIG, 128, W4_BF16), 0, "ws size huge");
+  expect((int)w4a16_matmul_workspace_size(256, 11008, 4096, 100, W4_BF16), 0, "ws size bad g");
+  expect((int)w4a16_matmul_workspace_size(-1, 11008, 4096, 128, W4_BF16), 0, "ws size m<0");
   for (int64_t m : {1, 4, 16, 17, 512})
     expect(w4a8_matmul((int8_t*)A, (float*)A, m, 8192, P, A, A, W4_F16, 28672, 128, A, W4_BF16, nullptr), W4_OK, "w4a8 ok");
   expect(w4a8_matmul((int8_t*)A, (float*)U, 1, 8192, P, A, A, W4_F16, 28672, 128, A, W4_BF16, nullptr), W4_OK, "w4a8 scale 4B");

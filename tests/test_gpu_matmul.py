@@ -220,6 +220,56 @@ def test_workload_prefill(w4, name, k):
 
 
 # ---------------------------------------------------------------------------
+# Split K (w4a16_matmul_ws): shapes whose output tiles fill few compute units
+# ---------------------------------------------------------------------------
+SPLITK_SHAPES = [  # (m, n, k, g): every one splits K (checked below)
+    (200, 300, 2048, 128), (129, 96, 4096, 32), (300, 130, 2048, 256), (257, 520, 4096, 64),
+    (133, 77, 1152, 96),
+]
+
+
+@pytest.mark.parametrize("m,n,k,g", SPLITK_SHAPES)
+@pytest.mark.parametrize("sz,ykind", [("f16", "bf16"), ("f32", "f32")])
+def test_w4a16_split_k(w4, m, n, k, g, sz, ykind):
+    """The split-K GEMM (workspace given) against the oracle, against the
+    same product without a workspace, and bit for bit across two calls."""
+    assert w4.w4a16_matmul_workspace_size(m, k, n, g) > 0
+    P, S, Z = make_weights(n, k, g, sz, seed=m + n + g)
+    dw = dev_weights(P, S, Z, sz)
+    x = WL.bf16_round_bits(np.random.default_rng(m * 3 + k).normal(0, 1, (m, k)).astype(np.float32))
+    xt = to_dev(x, "bf16")
+    ref = O.matmul_w4a16_f64(O.widen_bf16(x), P, S, Z, g)
+    c = Canary((m, n), TDT[ykind])
+    w4.w4a16_matmul(xt, *dw, g, out=c.tensor, workspace="auto")
+    c.check()
+    assert O.max_rel_err(y_as_f64(c.tensor), ref) <= TOL[ykind]
+    again = w4.w4a16_matmul(xt, *dw, g, out_dtype=TDT[ykind], workspace="auto")
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(to_host(again)), bits(to_host(c.tensor)))
+    plain = w4.w4a16_matmul(xt, *dw, g, out_dtype=TDT[ykind], workspace=None)
+    assert O.max_rel_err(y_as_f64(plain), ref) <= TOL[ykind]
+    # a workspace one byte short: the library runs the unsplit kernel
+    short = torch.empty(w4.w4a16_matmul_workspace_size(m, k, n, g) - 1, dtype=torch.uint8, device="cuda")
+    y2 = w4.w4a16_matmul(xt, *dw, g, out_dtype=TDT[ykind], workspace=short)
+    assert np.array_equal(bits(to_host(y2)), bits(to_host(plain)))
+
+
+@pytest.mark.parametrize("m", [129, 256, 512])
+def test_workload_down_proj_mid_m(w4, m):
+    """The Llama-7B down projection [4096, 11008] at 129 to 512 tokens, where
+    the unsplit GEMM has only 32 or 64 tiles: split K with the workspace the
+    library asks for; the oracle checks 40 sampled tokens (plus the first
+    and last) against every output column."""
+    t, (P, S, Z) = quantized("Wd", 128, "f16")
+    assert w4.w4a16_matmul_workspace_size(m, 11008, 4096, 128) > 0
+    x = WL.activation(3, m, 11008)
+    y = run_w4a16(w4, x.data, "bf16", dev_weights(P, S, Z, "f16"), 128, "bf16")
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(m).choice(m, 40, replace=False)]))
+    ref = O.matmul_w4a16_f64(x.as_f32()[rows], P, S, Z, 128)
+    assert O.max_rel_err(y_as_f64(y)[rows], ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
 # W4A8
 # ---------------------------------------------------------------------------
 def run_w4a8(w4, x_np, xkind, dw, g, ykind="bf16"):
