@@ -35,6 +35,7 @@ SIGNATURES = [
     ("w4a16_matmul_workspace_size", ctypes.c_size_t, [_I64, _I64, _I64, _I32, _I]),
     ("w4a16_matmul_ws", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP,
                              ctypes.c_size_t, _VP]),
+    ("w4a16_matmul_noalloc", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
     ("w4a8_matmul", _I, [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
     ("gptq_hessian", _I, [_VP, _I64, _I64, _VP, _VP]),
     ("gptq_inverse_cholesky", _I, [_VP, _I64, _VP, _VP, _VP]),

@@ -271,10 +271,13 @@ static W16Path w4a16_path(int x_dtype, int64_t m, int64_t k, int32_t group_size)
   return W16Path::GENERIC;
 }
 
+// ws / ws_bytes: the caller's workspace (w4a16_matmul_ws); use_scratch: the
+// library's static scratch instead (w4a16_matmul_noalloc), looked up only
+// after every argument has been validated.
 static int w4a16_common(const char* fn, const void* x, int x_dtype, int64_t m, int64_t k,
                         const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
                         int64_t n, int32_t group_size, void* y, int y_dtype, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+                        size_t ws_bytes, bool use_scratch, hipStream_t stream) {
   W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
   if (x_dtype != W4_F32 && x_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: x dtype %d must be W4_F32 or W4_BF16", fn, x_dtype);
@@ -289,7 +292,19 @@ static int w4a16_common(const char* fn, const void* x, int x_dtype, int64_t m, i
   W4_TRY(check_ptr(fn, "y", y));
   if (ws != nullptr && ws_bytes > 0 && !aligned16(ws))
     return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
-  switch (w4a16_path(x_dtype, m, k, group_size)) {
+  const W16Path path = w4a16_path(x_dtype, m, k, group_size);
+  if (use_scratch && path == W16Path::GEMM) {
+    // only a shape that splits K needs the scratch
+    ws_bytes = w4::gemm_workspace_bytes(m, k, n, group_size);
+    if (ws_bytes > w4::kSplitKMaxBytes)
+      return fail(W4_EINVAL, "%s: this shape needs %zu bytes of scratch, above the library's %zu", fn,
+                  ws_bytes, w4::kSplitKMaxBytes);
+    if (ws_bytes > 0) {
+      const hipError_t e = w4::scratch_address(&ws);
+      if (e != hipSuccess) return hip_status(e, fn);
+    }
+  }
+  switch (path) {
     case W16Path::DOT2:
       return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
@@ -317,7 +332,14 @@ int w4a16_matmul(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t
                  const void* scales, const void* zeros, int sz_dtype, int64_t n,
                  int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
   return w4a16_common("w4a16_matmul", x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
-                      group_size, y, y_dtype, nullptr, 0, stream);
+                      group_size, y, y_dtype, nullptr, 0, false, stream);
+}
+
+int w4a16_matmul_noalloc(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                         const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                         int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
+  return w4a16_common("w4a16_matmul_noalloc", x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
+                      group_size, y, y_dtype, nullptr, 0, true, stream);
 }
 
 size_t w4a16_matmul_workspace_size(int64_t m, int64_t k, int64_t n, int32_t group_size,
@@ -336,7 +358,7 @@ int w4a16_matmul_ws(const void* x, int x_dtype, int64_t m, int64_t k, const uint
                     int32_t group_size, void* y, int y_dtype, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   return w4a16_common("w4a16_matmul_ws", x, x_dtype, m, k, packed, scales, zeros, sz_dtype, n,
-                      group_size, y, y_dtype, workspace, workspace_bytes, stream);
+                      group_size, y, y_dtype, workspace, workspace_bytes, false, stream);
 }
 
 int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,

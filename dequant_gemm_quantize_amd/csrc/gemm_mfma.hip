@@ -390,6 +390,41 @@ static hipError_t gemm_go_g(const uint16_t* x, int64_t m, int64_t k, const uint8
   return gemm_go<TS, TY, false>(x, m, k, packed, scales, zeros, n, g, y, ws, ws_bytes, st);
 }
 
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (w4a16_matmul_noalloc): room for
+// the split-K partials of any shape (the plan never asks for more than
+// kSplitKMaxBytes).  Each device holds its own copy from module load until
+// the process ends; every call on a device shares it, so calls that overlap
+// on one device race.  Nothing in it must start at zero: each split writes
+// every partial it covers before the reduction reads it.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kSplitKMaxBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with hipGetSymbolAddress (the array's name in host code is only a
+// stand-in, not a device address).  Devices past 63 look it up every call.
+static std::atomic<void*> g_scratch_ptr[64];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) {
+      *out = p;
+      return hipSuccess;
+    }
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  if (dev >= 0 && dev < 64) g_scratch_ptr[dev].store(p, std::memory_order_release);
+  *out = p;
+  return hipSuccess;
+}
+
 hipError_t launch_w4a16_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
                              int g, void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t st) {

@@ -73,6 +73,9 @@ bool gemm_fits(int64_t m, int64_t k, int g);
 // split); never above kSplitKMaxBytes.
 constexpr size_t kSplitKMaxBytes = (size_t)32 << 20;
 size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int g);
+// Device address (current device) of the library's static scratch of
+// kSplitKMaxBytes, for callers that cannot allocate.
+hipError_t scratch_address(void** out);
 hipError_t launch_w4a8_gemv(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                             const uint8_t* packed, const void* scales, const void* zeros,
                             int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st);

@@ -208,6 +208,26 @@ int w4a16_matmul_ws(const void* x, int x_dtype, int64_t m, int64_t k, const uint
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * w4a16_matmul_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): w4a16_matmul_ws with the library's own scratch in place of
+ * the caller's workspace, so every shape gets the split-K schedule with no
+ * allocation, free or allocating library routine on any call.
+ *
+ * The scratch is a static device array of 32 MiB (the most any shape's
+ * split-K partials take), one per device, held from the library's first use
+ * on that device until the process ends.  Every call on a device shares it:
+ * calls that overlap on one device (different streams, or different host
+ * threads) race and must be ordered by the caller.  Arguments, results,
+ * accuracy and errors are those of w4a16_matmul; a shape whose partials
+ * would exceed the scratch returns W4_EINVAL (the split plan never asks for
+ * more, so no valid call does).
+ */
+int w4a16_matmul_noalloc(const void* x, int x_dtype, int64_t m, int64_t k, const uint8_t* packed,
+                         const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                         int32_t group_size, void* y, int y_dtype, hipStream_t stream);
+
+/*
  * w4a8_matmul -- y[m, n] = x_scale[m] * sum_k xq[m, k] * dequant(W)[n, k]
  * ([P1] Architecture Overview, Step 5), with xq/x_scale as produced by
  * quantize_act_int8.  Per group the integer sum of xq * (q - zp) is exact

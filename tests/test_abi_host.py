@@ -364,3 +364,14 @@ def test_workspace_size_query(lib):
 def torch_float32():
     import torch
     return torch.float32
+
+
+def test_noalloc_validates_before_any_hip_call(lib):
+    """The allocation-free entry point checks every argument before it looks
+    up its scratch (a HIP call): on a machine without a GPU an invalid call
+    still reports W4_EINVAL with the argument's message."""
+    assert lib.w4a16_matmul_noalloc(A, 2, 256, 11008, A, A, A, 1, 4096, 128, None, 2, None) == -1
+    assert "y is NULL" in _err(lib)
+    assert lib.w4a16_matmul_noalloc(A, 2, 256, 11008, A, A, A, 1, 4096, 100, A, 2, None) == -1
+    assert "group_size" in _err(lib)
+    assert lib.w4a16_matmul_noalloc(None, 2, 0, 11008, None, None, None, 1, 4096, 128, None, 2, None) == 0

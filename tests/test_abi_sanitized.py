@@ -84,6 +84,10 @@ int main() {
   expect(w4a16_matmul_ws(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, A, W4_BF16, nullptr, 0, nullptr), W4_OK, "w4a16 ws null");
   expect(w4a16_matmul_ws(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, A, W4_BF16, U, 4096, nullptr), W4_EINVAL, "w4a16 ws misaligned");
   expect(w4a16_matmul_ws(A, W4_BF16, BIG, 4096, P, A, A, W4_F16, BIG, 128, A, W4_BF16, A, 4096, nullptr), W4_EINVAL, "w4a16 ws huge");
+  expect(w4a16_matmul_noalloc(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, A, W4_BF16, nullptr), W4_OK, "noalloc ok");
+  expect(w4a16_matmul_noalloc(A, W4_BF16, 256, 11008, P, A, A, W4_F16, 4096, 128, nullptr, W4_BF16, nullptr), W4_EINVAL, "noalloc y null");
+  expect(w4a16_matmul_noalloc(A, W4_BF16, BIG, 4096, P, A, A, W4_F16, BIG, 128, A, W4_BF16, nullptr), W4_EINVAL, "noalloc huge");
+  expect(w4a16_matmul_noalloc(A, W4_BF16, 0, 4096, P, A, A, W4_F16, 64, 128, A, W4_BF16, nullptr), W4_OK, "noalloc empty");
   expect((int)w4a16_matmul_workspace_size(BIG, BIG, BIG, 128, W4_BF16), 0, "ws size huge");
   expect((int)w4a16_matmul_workspace_size(256, 11008, 4096, 100, W4_BF16), 0, "ws size bad g");
   expect((int)w4a16_matmul_workspace_size(-1, 11008, 4096, 128, W4_BF16), 0, "ws size m<0");
