@@ -256,17 +256,25 @@ int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
 // Which kernel w4a16_matmul runs for a (validated) shape.
 enum class W16Path { DOT2, DECODE, GEMV, GEMM, GENERIC };
 
-static W16Path w4a16_path(int x_dtype, int64_t m, int64_t k, int32_t group_size) {
+
+static W16Path w4a16_path(int x_dtype, int64_t m, int64_t k, int64_t n, int32_t group_size,
+                          bool split_ok) {
   // Kernel choice (bf16 activations): one token, groups of at least 128, K up
   // to 12288 -> the dot2 GEMV; up to four tokens with the activations fitting
   // in LDS, groups of a multiple of 128 -> the LDS decode kernel; up to 128
   // tokens, groups of a multiple of 128 -> the MFMA GEMV (in launches of up
-  // to 64 tokens); more tokens -> the MFMA GEMM; everything else (fp32
-  // activations, smaller group sizes at few tokens) -> the general kernel.
+  // to 64 tokens), except that with a workspace, from 65 tokens on at K >=
+  // 8192, shapes whose GEMM splits K take the split-K GEMM (the [4096, 11008]
+  // down projection at 65 to 128 tokens: 37-39 us against 51-79 us); more
+  // tokens -> the MFMA GEMM; everything else (fp32 activations, smaller
+  // group sizes at few tokens) -> the general kernel.
   if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size)) return W16Path::DOT2;
   if (x_dtype == W4_BF16 && m <= 4 && group_size % 128 == 0 && w4::decode_lds_fits(m, k))
     return W16Path::DECODE;
-  if (x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size)) return W16Path::GEMV;
+  const bool gemv = x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size);
+  if (gemv && split_ok && m >= 65 && k >= 8192 && w4::gemm_workspace_bytes(m, k, n, group_size) > 0)
+    return W16Path::GEMM;
+  if (gemv) return W16Path::GEMV;
   if (x_dtype == W4_BF16 && w4::gemm_fits(m, k, group_size)) return W16Path::GEMM;
   return W16Path::GENERIC;
 }
@@ -292,7 +300,10 @@ static int w4a16_common(const char* fn, const void* x, int x_dtype, int64_t m, i
   W4_TRY(check_ptr(fn, "y", y));
   if (ws != nullptr && ws_bytes > 0 && !aligned16(ws))
     return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
-  const W16Path path = w4a16_path(x_dtype, m, k, group_size);
+  // the split-K GEMM is chosen only when its partials have room
+  const size_t split_bytes = (x_dtype == W4_BF16) ? w4::gemm_workspace_bytes(m, k, n, group_size) : 0;
+  const bool split_ok = split_bytes > 0 && (use_scratch || (ws != nullptr && ws_bytes >= split_bytes));
+  const W16Path path = w4a16_path(x_dtype, m, k, n, group_size, split_ok);
   if (use_scratch && path == W16Path::GEMM) {
     // only a shape that splits K needs the scratch
     ws_bytes = w4::gemm_workspace_bytes(m, k, n, group_size);
@@ -349,7 +360,7 @@ size_t w4a16_matmul_workspace_size(int64_t m, int64_t k, int64_t n, int32_t grou
       k % group_size != 0 || n > kMaxElems / k || m > 0x7fffffffLL || m > kMaxElems / k ||
       m > kMaxElems / n)
     return 0;
-  if (w4a16_path(x_dtype, m, k, group_size) != W16Path::GEMM) return 0;
+  if (w4a16_path(x_dtype, m, k, n, group_size, true) != W16Path::GEMM) return 0;
   return w4::gemm_workspace_bytes(m, k, n, group_size);
 }
 

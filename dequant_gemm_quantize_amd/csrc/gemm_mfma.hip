@@ -35,11 +35,11 @@ namespace {
 #ifndef W4_GEMM_DEPTH
 #define W4_GEMM_DEPTH 4
 #endif
-constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int BM = 256, BN = 128, BK = 64;  // BN: the split-K tiles; wide tiles take 192
 constexpr int LDS_ROW = BK + 8;  // bf16 elements per LDS row (+16 bytes of padding)
 constexpr int A_STAGE = BM * LDS_ROW;
-constexpr int B_STAGE = BN * LDS_ROW;
-constexpr size_t kGemmLds = (size_t)2 * (A_STAGE + B_STAGE) * 2;
+// LDS of a workgroup with N tiles of 64 * NJ columns (NJ = 2: 128, NJ = 3: 192)
+constexpr size_t gemm_lds(int nj) { return (size_t)2 * (A_STAGE + 64 * nj * LDS_ROW) * 2; }
 
 template <typename TS> struct GS;
 template <> struct GS<_Float16> {
@@ -109,16 +109,26 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v) {
 // min(nks, (s + 1) * kps)) and, when `part` is set, writes its float32 partial
 // tile to part + s * pstride as [M][N] (y is then unused; pstride is M * N
 // rounded up to a multiple of 4); k_splitk_reduce adds the splits.
-template <typename TS, typename TY, bool G64>
+// NJ: the workgroup tile is BM x 64 NJ (NJ = 2 or 3); each wave owns 64 x
+// 32 NJ of it (2 x NJ MFMA tiles).  Weight rows are loaded and dequantized
+// by BK / CPL lanes each, CPL = 16 codes (NJ = 2: all 512 threads) or 32
+// codes (NJ = 3: the first 384 threads, six whole waves).
+template <typename TS, typename TY, bool G64, int NJ>
 __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int64_t ng,
     uint32_t gmagic, void* __restrict__ y, int tiles_m, int tiles_n, int kps,
     float* __restrict__ part, int64_t pstride) {
   typedef typename GS<TS>::T R;
+  constexpr int BNt = 64 * NJ;              // tile columns
+  constexpr int B_STAGE = BNt * LDS_ROW;
+  constexpr int CPL = NJ == 2 ? 16 : 32;    // codes per weight lane and K step
+  constexpr int LPR = BK / CPL;             // lanes per weight row
+  constexpr int WTHR = BNt * LPR;           // threads that load weights (512 or 384)
+  typedef typename std::conditional<CPL == 16, u32x2, u32x4>::type WV;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sA = smem;                 // [2][BM][LDS_ROW]
-  uint16_t* sB = smem + 2 * A_STAGE;   // [2][BN][LDS_ROW]
+  uint16_t* sB = smem + 2 * A_STAGE;   // [2][BNt][LDS_ROW]
 
   // ---- tile of this workgroup -------------------------------------------
   const int bid = blockIdx.x;
@@ -128,15 +138,19 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     tm = xcd + 8 * (j % per);
     tn = j / per;
   } else {
+    // consecutive ids cycle through the M blocks, so with an even number of
+    // them each XCD keeps to every other M block of x (measured faster here
+    // than grouping an N block's M blocks on one XCD: x is re-read every K
+    // step, the weights once per M block)
     tm = bid % tiles_m;
     tn = bid / tiles_m;
   }
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNt;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*64, cols wn*64
+  const int wm = wave >> 1, wn = wave & 1;  // wave block: rows wm*64, cols wn*32*NJ
 
   // ---- global -> register assignment ----------------------------------------
   // Every address is a uniform base (advanced by the K step) plus a fixed
@@ -154,12 +168,13 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     xrs[r] = buf_rsrc((const char*)x + rb * K * 2);
     xo[r] = (uint32_t)((row - rb) * K * 2) + 16u * (uint32_t)xc;
   }
-  // W: 4 lanes per row, 8 bytes (16 codes) each; offsets below 128 rows of
-  // K/2 bytes (< 2^29).  Scales and zeros: the tile's 128 rows of K/g.
-  const int wr = tid >> 2, wq4 = tid & 3;
+  // W: LPR lanes per row, CPL / 2 bytes each; offsets below 192 rows of
+  // K/2 bytes (< 2^30).  Scales and zeros: the tile's rows of K/g.
+  const bool wact = tid < WTHR;  // wave-uniform (WTHR is a multiple of 64)
+  const int wr = wact ? tid / LPR : 0, wq4 = tid % LPR;
   const int64_t wrow = n0 + wr < N ? n0 + wr : N - 1;
   const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(packed + n0 * (K / 2));
-  const uint32_t wo = (uint32_t)((wrow - n0) * (K / 2)) + 8u * (uint32_t)wq4;
+  const uint32_t wo = (uint32_t)((wrow - n0) * (K / 2)) + (uint32_t)(CPL / 2) * (uint32_t)wq4;
   const __amdgpu_buffer_rsrc_t srs = buf_rsrc((const R*)scales + n0 * ng);
   const __amdgpu_buffer_rsrc_t zrs = buf_rsrc((const R*)zeros + n0 * ng);
   const uint32_t so = (uint32_t)((wrow - n0) * ng) * (uint32_t)sizeof(R);  // bytes
@@ -173,7 +188,7 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
   const int nks_all = (int)(K / BK);
   const int nks = (nks_all - ks0 < kps ? nks_all - ks0 : kps) + ks0;  // one past the last step
   u32x4 xv[D][4];
-  u32x2 wv[D];
+  WV wv[D];
   R sv[D], zv[D];
   // Loads past the last K step are clamped to it (a few redundant loads)
   // so that the main loop has no conditional loads: the compiler can then
@@ -184,10 +199,18 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       xv[u][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs[r], xo[r], ks * (2 * BK), 0));
-    wv[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, wo, ks * (BK / 2), 0));
+    if (!wact) return;
+    if constexpr (CPL == 16)
+      wv[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wrs, wo, ks * (BK / 2), 0));
+    else
+      wv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, ks * (BK / 2), 0));
     uint32_t vo = so, go = 0;  // group offset: uniform (G64) or per lane
-    if constexpr (G64) go = (gmagic ? __umulhi((uint32_t)ks, gmagic) : (uint32_t)ks) * (uint32_t)sizeof(R);
-    else vo += __umulhi((uint32_t)(ks * (BK / 16) + wq4), gmagic) * (uint32_t)sizeof(R);
+    if constexpr (G64) {
+      go = (gmagic ? __umulhi((uint32_t)ks, gmagic) : (uint32_t)ks) * (uint32_t)sizeof(R);
+    } else {
+      const uint32_t piece = (uint32_t)(ks * LPR + wq4);  // CPL-column piece of the row
+      vo += (gmagic ? __umulhi(piece, gmagic) : piece) * (uint32_t)sizeof(R);
+    }
     if constexpr (sizeof(R) == 2) {
       sv[u] = __builtin_amdgcn_raw_buffer_load_b16(srs, vo, go, 0);
       zv[u] = __builtin_amdgcn_raw_buffer_load_b16(zrs, vo, go, 0);
@@ -201,36 +224,37 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
     uint16_t* a = sA + lstage * A_STAGE;
 #pragma unroll
     for (int r = 0; r < 4; ++r) *(u32x4*)(a + (xr + 64 * r) * LDS_ROW + 8 * xc) = xv[u][r];
+    if (!wact) return;
     const float s = GS<TS>::f(sv[u]);
     const float b = -GS<TS>::f(zv[u]) * s;
-    uint16_t* bp = sB + lstage * B_STAGE + wr * LDS_ROW + 16 * wq4;
-    *(u32x4*)(bp + 0) = dequant8(wv[u].x, s, b);
-    *(u32x4*)(bp + 8) = dequant8(wv[u].y, s, b);
+    uint16_t* bp = sB + lstage * B_STAGE + wr * LDS_ROW + CPL * wq4;
+#pragma unroll
+    for (int t = 0; t < CPL / 8; ++t) *(u32x4*)(bp + 8 * t) = dequant8(wv[u][t], s, b);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int l32 = lane & 31, lk = 8 * (lane >> 5);
   auto mma = [&](int lstage) {
     const uint16_t* a = sA + lstage * A_STAGE + (wm * 64 + l32) * LDS_ROW + lk;
-    const uint16_t* b = sB + lstage * B_STAGE + (wn * 64 + l32) * LDS_ROW + lk;
+    const uint16_t* b = sB + lstage * B_STAGE + (wn * 32 * NJ + l32) * LDS_ROW + lk;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[2], bfr[NJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(a + 32 * i * LDS_ROW + 16 * kk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = *(const bf16x8*)(b + 32 * j * LDS_ROW + 16 * kk);
+      for (int j = 0; j < NJ; ++j) bfr[j] = *(const bf16x8*)(b + 32 * j * LDS_ROW + 16 * kk);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -273,8 +297,8 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + 32 * j + l32;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t n = n0 + wn * 32 * NJ + 32 * j + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -356,24 +380,55 @@ size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int g) {
   return p.s > 1 ? p.bytes : 0;
 }
 
+// Tiles 192 wide move 18% fewer LDS bytes per flop (the kernel's limit at
+// large M) and take 1.36x as long each (measured on [11008, 4096] at
+// M = 2048: 115.5 us per round of 256 wide tiles against 85 us for 128-wide
+// ones); they are chosen when their rounds of 256 workgroups, weighted 1.36,
+// come out below the 128-wide tiles' rounds.
+#ifndef W4_GEMM_WIDE
+#define W4_GEMM_WIDE 1
+#endif
+static bool wide_tiles(int64_t m, int64_t n) {
+  if (!W4_GEMM_WIDE) return false;
+  const int64_t tm = (m + BM - 1) / BM;
+  const int64_t r128 = (tm * ((n + 127) / 128) + 255) / 256;
+  const int64_t r192 = (tm * ((n + 191) / 192) + 255) / 256;
+  return (double)r192 * 1.36 < (double)r128;
+}
+
+template <typename TS, typename TY, bool G64, int NJ>
+static hipError_t gemm_launch(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
+                              const void* scales, const void* zeros, int64_t n, int g, void* y,
+                              const SplitK& p, float* part, hipStream_t st) {
+  static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
+  hipError_t e = once_per_device(attr_done, [] {
+    return hipFuncSetAttribute((const void*)k_w4a16_gemm<TS, TY, G64, NJ>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds(NJ));
+  });
+  if (e != hipSuccess) return e;
+  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + 64 * NJ - 1) / (64 * NJ));
+  // the quotient of a K step (g % 64 == 0) or of a lane's CPL-column piece
+  const int cpl = NJ == 2 ? 16 : 32;
+  const uint32_t gm = magic_ceil((uint32_t)(G64 ? g / 64 : g / cpl));
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.s);
+  k_w4a16_gemm<TS, TY, G64, NJ><<<grid, 512, gemm_lds(NJ), st>>>(x, m, k, packed, scales, zeros, n, k / g, gm,
+                                                                y, tiles_m, tiles_n, p.kps, part, p.pstride);
+  return hipGetLastError();
+}
+
 template <typename TS, typename TY, bool G64>
 static hipError_t gemm_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
                           const void* scales, const void* zeros, int64_t n, int g, void* y,
                           void* ws, size_t ws_bytes, hipStream_t st) {
-  static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
-  hipError_t e = once_per_device(attr_done, [] {
-    return hipFuncSetAttribute((const void*)k_w4a16_gemm<TS, TY, G64>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-  });
-  if (e != hipSuccess) return e;
-  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  const uint32_t gm = magic_ceil((uint32_t)(G64 ? g / 64 : g / 16));
   SplitK p = splitk_plan(m, k, n);
   if (p.s > 1 && (ws == nullptr || ws_bytes < p.bytes)) p = SplitK{1, (int)(k / BK), 0, 0};
-  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.s);
   float* part = p.s > 1 ? (float*)ws : nullptr;
-  k_w4a16_gemm<TS, TY, G64><<<grid, 512, kGemmLds, st>>>(x, m, k, packed, scales, zeros, n, k / g, gm, y,
-                                                        tiles_m, tiles_n, p.kps, part, p.pstride);
+  hipError_t e;
+  if (p.s == 1 && wide_tiles(m, n))
+    e = gemm_launch<TS, TY, G64, 3>(x, m, k, packed, scales, zeros, n, g, y, p, part, st);
+  else
+    e = gemm_launch<TS, TY, G64, 2>(x, m, k, packed, scales, zeros, n, g, y, p, part, st);
+  if (e != hipSuccess) return e;
   if (p.s > 1) {
     const int64_t mn = m * n;
     const dim3 rgrid((unsigned)((mn + 1023) / 1024));

@@ -79,7 +79,7 @@ template <typename TS, typename TY, bool G128>
 __global__ __launch_bounds__(NT, 512 / NT) void k_w4a8_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, int64_t K,
     const uint8_t* __restrict__ packed, const void* __restrict__ scales,
-    const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m) {
+    const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m, int tiles_n) {
   typedef typename G8<TS>::T R;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
   uint8_t* sA = smem8;                          // [2][BM][ROW]
@@ -93,8 +93,13 @@ __global__ __launch_bounds__(NT, 512 / NT) void k_w4a8_gemm(
     tm = xcd + 8 * (j % per);
     tn = j / per;
   } else {
-    tm = bid % tiles_m;
-    tn = bid / tiles_m;
+    // groups of 8 N blocks x all M blocks, M blocks of one N block 8 ids
+    // apart: those land on the same XCD, which then fetches that N block's
+    // weights from HBM once for all M blocks (the last group may be narrower)
+    const int span = 8 * tiles_m, grp = bid / span, r = bid % span;
+    const int w = tiles_n - 8 * grp < 8 ? tiles_n - 8 * grp : 8;
+    tm = r / w;
+    tn = 8 * grp + r % w;
   }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
@@ -283,10 +288,10 @@ static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t 
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (g == BK)
     k_w4a8_gemm<TS, TY, true><<<grid, NT, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g,
-                                                         y, tiles_m);
+                                                         y, tiles_m, tiles_n);
   else
     k_w4a8_gemm<TS, TY, false><<<grid, NT, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n,
-                                                          g, y, tiles_m);
+                                                          g, y, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -254,6 +254,31 @@ def test_w4a16_split_k(w4, m, n, k, g, sz, ykind):
     assert np.array_equal(bits(to_host(y2)), bits(to_host(plain)))
 
 
+def _wide(m, n):
+    """The GEMM's choice of 192-column tiles (rounds of 256 workgroups)."""
+    tm = -(-m // 256)
+    r128 = -(-tm * -(-n // 128) // 256)
+    r192 = -(-tm * -(-n // 192) // 256)
+    return r192 * 1.36 < r128
+
+
+WIDE_SHAPES = [(600, 22000, 256, 128), (520, 25000, 384, 64), (257, 45000, 256, 32)]
+
+
+@pytest.mark.parametrize("m,n,k,g", WIDE_SHAPES)
+@pytest.mark.parametrize("sz,ykind", [("f16", "bf16"), ("f32", "f32")])
+def test_w4a16_wide_tiles(w4, m, n, k, g, sz, ykind):
+    """Shapes that take the 192-column GEMM tiles (ragged N, every group
+    size path), against the oracle on 48 sampled tokens."""
+    assert _wide(m, n)
+    P, S, Z = make_weights(n, k, g, sz, seed=n + g)
+    x = WL.bf16_round_bits(np.random.default_rng(m + k).normal(0, 1, (m, k)).astype(np.float32))
+    y = run_w4a16(w4, x, "bf16", dev_weights(P, S, Z, sz), g, ykind)
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(5).choice(m, 46, replace=False)]))
+    ref = O.matmul_w4a16_f64(O.widen_bf16(x)[rows], P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y)[rows], ref) <= TOL[ykind]
+
+
 @pytest.mark.parametrize("m", [129, 256, 512])
 def test_workload_down_proj_mid_m(w4, m):
     """The Llama-7B down projection [4096, 11008] at 129 to 512 tokens, where
