@@ -289,16 +289,16 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
         out.setdefault("quantize_pack_sym", {})[name] = {
             "us": round(qsec * 1e6, 2), "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}
         if name == "Wb":
-            # range-clipping calibrators: the percentile (rank counting, g^2
-            # compares per group) and the MSE search (1000 candidates, 7 fp32
-            # VALU operations per candidate and weight)
+            # range-clipping calibrators: the percentile (a bitonic sort per
+            # group) and the MSE search (1000 candidates, 8.75 fp32 VALU
+            # instructions per candidate and weight)
             qsec = time_region(lambda i: w4.quantize_pack_int4_sym_percentile(wt, g, 99.9, torch.float16,
                                                                              out=qo), 5)
             cal = {"percentile_99.9": {"us": round(qsec * 1e6, 1),
                                        "GB/s": round(quant_bytes(n, k, g) / qsec / 1e9, 1)}}
             ncand = 1000
             qsec = time_region(lambda i: w4.quantize_pack_int4_sym_mse(wt, g, ncand, torch.float16, out=qo), 3)
-            tops = 7 * n * k * ncand / qsec / 1e12
+            tops = 8.75 * n * k * ncand / qsec / 1e12
             cal["mse_1000"] = {"us": round(qsec * 1e6, 1), "valu_TOP/s": round(tops, 2),
                                "frac_valu_peak": round(tops / VALU_PEAK_TOPS, 4)}
             out["calibrate_sym_Wb"] = cal
@@ -738,8 +738,36 @@ def cpu_baseline(args, WL, np, log, wa, wb):
            "ms_per_step": round(sec * 1e3, 3), "host_cpus": os.cpu_count(),
            "affinity_cpus": len(os.sched_getaffinity(0)), "numpy": np.__version__}
     log(f"cpu baseline: {res['value']} GB/s over {steps} steps")
+    res["stages"] = oracle_stages(WL, np, log, wb)
     res["gptq"] = gptq_cpu(np, log)
     return res
+
+
+def oracle_stages(WL, np, log, wb, g=128, seconds=2.0):
+    """The oracle's other stages on this host (NumPy, one thread), each run
+    whole and repeated for about `seconds`, as rates on the same algorithmic
+    bytes as the GPU figures: quantize + pack of the [11008, 4096] weight
+    (bf16 in, fp16 scales), and the per-token INT8 activations of x bf16
+    [512, 8192]."""
+    import oracle.w4_oracle as O
+    out = {}
+
+    def rate(fn, nbytes):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        sec = (time.perf_counter() - t0) / reps
+        return {"ms": round(sec * 1e3, 2), "GB/s": round(nbytes / sec / 1e9, 3), "reps": reps}
+
+    n, k = 11008, 4096
+    out["quantize_pack_Wb"] = rate(lambda: O.quantize_pack_int4(wb.data, wb.kind, g, "f16"), quant_bytes(n, k, g))
+    x = WL.activation(5, 512, 8192).as_f32()
+    out["act_quant_int8_512x8192"] = rate(lambda: O.act_quant_int8(x), 512 * 8192 * (2 + 1) + 4 * 512)
+    log(f"oracle stages: {json.dumps(out)}")
+    return out
 
 
 def gptq_cpu(np, log, rows=64, g=128):
