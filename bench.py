@@ -59,9 +59,9 @@ def quant_bytes(n, k, g, w_bytes=2, sz_bytes=2):
     return n * k * w_bytes + n * k // 2 + 2 * n * (k // g) * sz_bytes
 
 
-# Sources that decide which kernel runs the [11008,4096] decode product and
-# what it does; stored byte counters are used only while these are unchanged.
-DECODE_SOURCES = ("api.cpp", "w4_common.h", "w4_internal.h", "gemv_dot2.hip")
+# Sources of the kernel that runs the [11008,4096] decode product (and of its
+# launch); stored counters and kernel traces are used only while these are unchanged.
+DECODE_SOURCES = ("w4_common.h", "gemv_dot2.hip")
 
 
 def src_hash(files=DECODE_SOURCES):
