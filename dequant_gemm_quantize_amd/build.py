@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libw4.so")
 PEAKS_SOURCES = ["peaks.hip"]
 PEAKS_LIB_PATH = os.path.join(HERE, "libw4peaks.so")
 
-SOURCES = ["api.cpp", "quant.hip", "gemv_generic.hip", "gemv_dot2.hip", "gemv_mfma.hip", "gemv_decode.hip", "gemm_mfma.hip", "gemm_w4a8.hip", "gemv_w4a8.hip", "gemv_w4a8_mfma.hip", "gptq.hip"]
+SOURCES = ["api.cpp", "quant.hip", "gemv_generic.hip", "gemv_dot2.hip", "gemv_mfma.hip", "gemv_quad.hip", "gemv_decode.hip", "gemm_mfma.hip", "gemm_w4a8.hip", "gemv_w4a8.hip", "gemv_w4a8_mfma.hip", "gptq.hip"]
 
 ARCH = os.environ.get("W4_OFFLOAD_ARCH", "gfx950")
 

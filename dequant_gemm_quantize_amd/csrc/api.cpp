@@ -254,13 +254,16 @@ int quantize_act_int8(const void* x, int x_dtype, int64_t m, int64_t k, int8_t* 
 }
 
 // Which kernel w4a16_matmul runs for a (validated) shape.
-enum class W16Path { DOT2, DECODE, GEMV, GEMM, GENERIC };
+enum class W16Path { DOT2, QUAD, DECODE, GEMV, GEMM, GENERIC };
 
 
 static W16Path w4a16_path(int x_dtype, int64_t m, int64_t k, int64_t n, int32_t group_size,
                           bool split_ok) {
   // Kernel choice (bf16 activations): one token, groups of at least 128, K up
-  // to 12288 -> the dot2 GEMV; up to four tokens with the activations fitting
+  // to 12288 -> the dot2 GEMV; two to four tokens at K = 4096, groups of a
+  // multiple of 32 -> the 4x4x4 matrix-core GEMV (Llama-7B [11008,4096] at
+  // 2 / 3 / 4 tokens: 7.8 / 7.9 / 8.3 us against 8.3 / 8.9 / 9.3 us on the
+  // LDS decode kernel); other K up to four tokens with the activations fitting
   // in LDS, groups of a multiple of 128 -> the LDS decode kernel; up to 128
   // tokens, groups of a multiple of 128 -> the MFMA GEMV (in launches of up
   // to 64 tokens), except that with a workspace, from 65 tokens on at K >=
@@ -269,6 +272,7 @@ static W16Path w4a16_path(int x_dtype, int64_t m, int64_t k, int64_t n, int32_t 
   // tokens -> the MFMA GEMM; everything else (fp32 activations, smaller
   // group sizes at few tokens) -> the general kernel.
   if (x_dtype == W4_BF16 && w4::dot2_fits(m, k, group_size)) return W16Path::DOT2;
+  if (x_dtype == W4_BF16 && w4::quad_fits(m, k, group_size)) return W16Path::QUAD;
   if (x_dtype == W4_BF16 && m <= 4 && group_size % 128 == 0 && w4::decode_lds_fits(m, k))
     return W16Path::DECODE;
   const bool gemv = x_dtype == W4_BF16 && w4::gemv_mfma_fits(m, k, group_size);
@@ -318,6 +322,10 @@ static int w4a16_common(const char* fn, const void* x, int x_dtype, int64_t m, i
   switch (path) {
     case W16Path::DOT2:
       return hip_status(w4::launch_w4a16_dot2(x, m, k, packed, scales, zeros, sz_dtype, n,
+                                              group_size, y, y_dtype, stream),
+                        fn);
+    case W16Path::QUAD:
+      return hip_status(w4::launch_w4a16_quad(x, m, k, packed, scales, zeros, sz_dtype, n,
                                               group_size, y, y_dtype, stream),
                         fn);
     case W16Path::DECODE:

@@ -1,5 +1,6 @@
-// Decode-time fused dequantize-matmul for 1 <= M <= 4 tokens (bf16 x) whose
-// activations fit in LDS, groups that are multiples of 128 columns.
+// Decode-time fused dequantize-matmul for 2 <= M <= 4 tokens (bf16 x) whose
+// activations fit in LDS, groups that are multiples of 128 columns, at the
+// shapes the 4x4x4 matrix-core GEMV does not take (K other than 4096).
 // HBM-bound: the kernels exist to stream the packed codes at full bandwidth.
 //
 // Math.  For a 128-column block b of weight row n (inside one group, scale s,
@@ -61,8 +62,8 @@ template <> struct RawSZ<float> {
 };
 
 // ---------------------------------------------------------------------------
-// The decode kernels (used when the activations fit the LDS budget of
-// 64 KB: M <= 4 at K = 4096, M = 1 at K = 8192).  Two details cut registers
+// The decode kernel (used when the activations fit the LDS budget of
+// 64 KB).  Two details cut registers
 // and VALU work:
 //  * the block's codes are expanded in the order (0,4), (1,5), (2,6), (3,7)
 //    of each 8-code word -- seven instructions per word (shift + and-or) --
@@ -151,8 +152,7 @@ __device__ __forceinline__ void decode_blocks(const u32x4* __restrict__ wrow,
 //   zb[16][nblk]  uint32  bf16 pair -(128 + zp) of (tile row, block)
 //   x [M][nw*16]  16-byte groups of the wave's activations, interleaved order
 // followed by part[WAVES][64] f32x4 for the final cross-wave sum.  A wave
-// fills only the blocks it uses, except on the fast path (one block per
-// group) where it stores the whole scale / zero-point tile unconditionally.
+// fills only the blocks it uses.
 __host__ __device__ inline int64_t decode_wave_blocks(int64_t k, int waves) {
   const int64_t nblk = k / 128;
   return (nblk + waves - 1) / waves;  // upper bound of blocks per wave
@@ -164,10 +164,7 @@ size_t decode_lds_bytes(int64_t m, int64_t k, int waves) {
   return (size_t)(waves * decode_wave_bytes(m, k, waves) + waves * 64 * 16);
 }
 
-// Staging of one wave: XPER 16-byte activation loads and SPER 16-byte loads
-// of each of the scale / zero-point tiles per lane (compile-time, exact), or
-// 0 for element loops.
-template <typename TS, typename TY, int WAVES, int XPER, int SPER>
+template <typename TS, typename TY, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode(
     const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
     const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N, int g,
@@ -197,71 +194,29 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode(
   const R* sg = (const R*)scales;
   const R* zg = (const R*)zeros;
   const u32x4* xg = (const u32x4*)x;
-  const int64_t tile0 = n0 * ng;                 // first scale element of the tile
-  const int64_t last = N * ng - 1;               // last valid scale element
   const u32x4* wrow = (const u32x4*)(packed + n * (K / 2)) + kg;
 
-  // ---- 1. staging loads, 2. codes of the first chunk -----------------------
-  constexpr bool fast = XPER > 0;
-  constexpr int kXP = XPER > 0 ? XPER : 1, kSP = SPER > 0 ? SPER : 1;
-  u32x4 xv[kXP], sv[kSP], zv[kSP];
-  if (fast) {
-    // activations: groups (m, b0*16 .. b1*16) of every token m < M
-#pragma unroll
-    for (int r = 0; r < kXP; ++r) {
-      const int i = lane + 64 * r;               // group index inside the slice
-      const int m = i / (nwb * 16), c = i - m * (nwb * 16);
-      xv[r] = xg[(int64_t)m * (K / 8) + b0 * 16 + c];
-    }
-    // scale / zero-point tile: 16 rows x ng elements, contiguous in memory
-    constexpr int per16 = 16 / (int)sizeof(R);   // elements per 16-byte load
-#pragma unroll
-    for (int r = 0; r < kSP; ++r) {
-      int64_t e = tile0 + (int64_t)(lane + 64 * r) * per16;
-      e = e + per16 - 1 <= last ? e : last + 1 - per16;  // ragged last tile: stay in bounds
-      sv[r] = *(const u32x4*)(sg + e);
-      zv[r] = *(const u32x4*)(zg + e);
-    }
-  }
+  // ---- 1. codes of the first chunk ---------------------------------------
   const bool first_full = nwb >= kChunk;
   u32x4 wq0[kChunk];
   if (first_full) decode_loads<kChunk>(wrow, b0, wq0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 3. LDS stores of the wave's slices (no workgroup barrier) -----------
-  if (fast) {
-#pragma unroll
-    for (int r = 0; r < kXP; ++r) xs_l[lane + 64 * r] = interleave8(xv[r]);
-    constexpr int per16 = 16 / (int)sizeof(R);
-    // the fast path has g == 128 (group == block == tile column): store the
-    // whole tile, every lane, no conditions
-#pragma unroll
-    for (int r = 0; r < kSP; ++r) {
-      const R* se = (const R*)&sv[r];
-      const R* ze = (const R*)&zv[r];
-      const int e0 = (lane + 64 * r) * per16;
-#pragma unroll
-      for (int t = 0; t < per16; ++t) {
-        sc_l[e0 + t] = RawSZ<TS>::scale(se[t]);
-        zb_l[e0 + t] = (0xc300u | RawSZ<TS>::zero(ze[t])) * 0x00010001u;
-      }
-    }
-  } else {
-    for (int i = lane; i < M * nwb * 16; i += 64) {
-      const int m = i / (nwb * 16), c = i - m * (nwb * 16);
-      xs_l[i] = interleave8(xg[(int64_t)m * (K / 8) + b0 * 16 + c]);
-    }
-    for (int e = lane; e < 16 * nwb; e += 64) {
-      const int row = e / nwb, b = b0 + (e - row * nwb);
-      int64_t ge = (n0 + row < N ? n0 + row : N - 1) * ng + b / bpg;
-      sc_l[row * nblk + b] = RawSZ<TS>::scale(sg[ge]);
-      zb_l[row * nblk + b] = (0xc300u | RawSZ<TS>::zero(zg[ge])) * 0x00010001u;
-    }
+  // ---- 2. LDS stores of the wave's slices (no workgroup barrier) -----------
+  for (int i = lane; i < M * nwb * 16; i += 64) {
+    const int m = i / (nwb * 16), c = i - m * (nwb * 16);
+    xs_l[i] = interleave8(xg[(int64_t)m * (K / 8) + b0 * 16 + c]);
+  }
+  for (int e = lane; e < 16 * nwb; e += 64) {
+    const int row = e / nwb, b = b0 + (e - row * nwb);
+    int64_t ge = (n0 + row < N ? n0 + row : N - 1) * ng + b / bpg;
+    sc_l[row * nblk + b] = RawSZ<TS>::scale(sg[ge]);
+    zb_l[row * nblk + b] = (0xc300u | RawSZ<TS>::zero(zg[ge])) * 0x00010001u;
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS stores are done
   __builtin_amdgcn_wave_barrier();
 
-  // ---- 4. MFMAs over the wave's blocks (block-relative LDS indices) --------
+  // ---- 3. MFMAs over the wave's blocks (block-relative LDS indices) --------
   const int jx = j < M ? j : 0;  // operand rows m >= M repeat token 0 (never stored)
   const u32x4* xl = xs_l + jx * (nwb * 16) + kg * 4;  // indexed by block relative to b0
   const float* s_l = sc_l + j * nblk + b0;   // indexed by block relative to b0
@@ -278,108 +233,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode(
   if (kChunk > 2 && c0 + 2 <= b1) { decode_blocks<2>(wrow, xl, s_l, z_l, c0, c0 - b0, acc); c0 += 2; }
   if (c0 < b1) decode_blocks<1>(wrow, xl, s_l, z_l, c0, c0 - b0, acc);
 
-  // ---- 5. cross-wave sum of the partial tiles, store -----------------------
-  part[wave * 64 + lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    f32x4 sum = part[lane];
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) {
-      const f32x4 o = part[w * 64 + lane];
-      sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
-    }
-    if (n0 + j < N) {
-      const float v[4] = {sum.x, sum.y, sum.z, sum.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * kg + r;
-        if (m < M) store_out<TY>(y, (int64_t)m * N + n0 + j, v[r]);
-      }
-    }
-  }
-}
-
-// Fast decode kernel for the common shapes: one block per group (g = 128),
-// every wave owns exactly NWB blocks (NWB % 8 == 0), the activation slice is
-// XPER 16-byte loads per lane and the scale / zero-point tile SPER 16-byte
-// loads per lane.  Everything is compile-time, so every load is
-// straight-line code: staging loads, then the codes of the first 8 blocks,
-// then the LDS stores while the codes are in flight.
-template <typename TS, typename TY, int WAVES, int XPER, int SPER, int NWB>
-__global__ __launch_bounds__(64 * WAVES) void k_w4a16_decode_fast(
-    const uint16_t* __restrict__ x, int M, int64_t K, const uint8_t* __restrict__ packed,
-    const void* __restrict__ scales, const void* __restrict__ zeros, int64_t N,
-    void* __restrict__ y) {
-  typedef typename RawSZ<TS>::T R;
-  static_assert(NWB % kChunk == 0, "whole chunks per wave");
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = lane & 15;
-  const int kg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * kRows;
-  const int64_t n = (n0 + j < N) ? (n0 + j) : (N - 1);
-  const int nblk = NWB * WAVES;  // == K / 128 == number of groups
-  const int b0 = wave * NWB;
-  const int64_t wbytes = 16 * (int64_t)nblk * 8 + (int64_t)M * NWB * 256;
-  unsigned char* base = lds + wave * wbytes;
-  float* sc_l = (float*)base;                          // [16][nblk]
-  uint32_t* zb_l = (uint32_t*)(base + 16 * nblk * 4);  // [16][nblk]
-  u32x4* xs_l = (u32x4*)(base + 16 * nblk * 8);        // [M][NWB*16]
-  f32x4* part = (f32x4*)(lds + WAVES * wbytes);
-
-  const R* sg = (const R*)scales;
-  const R* zg = (const R*)zeros;
-  const u32x4* xg = (const u32x4*)x;
-  const u32x4* wrow = (const u32x4*)(packed + n * (K / 2)) + kg;
-  constexpr int per16 = 16 / (int)sizeof(R);
-  const int64_t tile0 = n0 * nblk;
-  const int64_t last = N * nblk - 1;
-
-  u32x4 xv[XPER], sv[SPER], zv[SPER];
-#pragma unroll
-  for (int r = 0; r < XPER; ++r) {
-    const int i = lane + 64 * r;  // group inside the wave's slice: token i / (NWB*16)
-    const int m = i / (NWB * 16), c = i - m * (NWB * 16);
-    xv[r] = xg[(int64_t)m * (K / 8) + b0 * 16 + c];
-  }
-#pragma unroll
-  for (int r = 0; r < SPER; ++r) {
-    int64_t e = tile0 + (int64_t)(lane + 64 * r) * per16;
-    e = e + per16 - 1 <= last ? e : last + 1 - per16;  // ragged last tile: stay in bounds
-    sv[r] = *(const u32x4*)(sg + e);
-    zv[r] = *(const u32x4*)(zg + e);
-  }
-  u32x4 wq0[kChunk];
-  decode_loads<kChunk>(wrow, b0, wq0);
-  __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-  for (int r = 0; r < XPER; ++r) xs_l[lane + 64 * r] = interleave8(xv[r]);
-#pragma unroll
-  for (int r = 0; r < SPER; ++r) {
-    const R* se = (const R*)&sv[r];
-    const R* ze = (const R*)&zv[r];
-    const int e0 = (lane + 64 * r) * per16;
-#pragma unroll
-    for (int t = 0; t < per16; ++t) {
-      sc_l[e0 + t] = RawSZ<TS>::scale(se[t]);
-      zb_l[e0 + t] = (0xc300u | RawSZ<TS>::zero(ze[t])) * 0x00010001u;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS stores are done
-  __builtin_amdgcn_wave_barrier();
-
-  const int jx = j < M ? j : 0;  // operand rows m >= M repeat token 0 (never stored)
-  const u32x4* xl = xs_l + jx * (NWB * 16) + kg * 4;
-  const float* s_l = sc_l + j * nblk + b0;
-  const uint32_t* z_l = zb_l + j * nblk + b0;
-
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  decode_math<kChunk>(wq0, xl, s_l, z_l, 0, acc);
-#pragma unroll
-  for (int c = kChunk; c < NWB; c += kChunk) decode_blocks<kChunk>(wrow, xl, s_l, z_l, b0 + c, c, acc);
-
+  // ---- 4. cross-wave sum of the partial tiles, store -----------------------
   part[wave * 64 + lane] = acc;
   __syncthreads();
   if (wave == 0) {
@@ -415,29 +269,11 @@ static void decode_go(dim3 grid, hipStream_t st, const uint16_t* x, int M, int64
   constexpr int W = W4_DECODE_WAVES;
   const size_t lds = decode_lds_bytes(M, k, W);
   const int64_t nblk = k / 128, ng = k / g;
-  // exact straight-line staging when every wave has the same block count,
-  // its activation slice is a whole number of 64-lane rounds and the
-  // scale / zero-point tile is a whole number of 1 KB rounds
-  const bool even = nblk % W == 0;
-  const int64_t xgroups = M * (nblk / W) * 16;
-  const int64_t tile_bytes = 16 * ng * (int64_t)sizeof(TS);
-  const bool bpg1 = (g == 128);
-  int xper = 0, sper = 0;
-  if (even && bpg1 && xgroups % 64 == 0 && tile_bytes % 1024 == 0) {
-    xper = (int)(xgroups / 64);
-    sper = (int)(tile_bytes / 1024);
-  }
-#define W4_DEC(XP, SP) \
-  k_w4a16_decode<TS, TY, W, XP, SP><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, g, y)
-#define W4_DEC_FAST(XP, SP, NWB) \
-  k_w4a16_decode_fast<TS, TY, W, XP, SP, NWB><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, y)
-  const int64_t nwb = nblk / W;
-  // (one token never gets here: it goes to the dot2 GEMV)
-  if (xper == 4 && sper == 1 && nwb == 8) W4_DEC_FAST(4, 1, 8);        // M = 2, K = 4096, fp16 s/z
-  else if (xper == 6 && sper == 1 && nwb == 8) W4_DEC_FAST(6, 1, 8);   // M = 3, K = 4096, fp16 s/z
-  else if (xper == 8 && sper == 1 && nwb == 8) W4_DEC_FAST(8, 1, 8);   // M = 4, K = 4096, fp16 s/z
-  else W4_DEC(0, 0);
-#undef W4_DEC_FAST
+#define W4_DEC() \
+  k_w4a16_decode<TS, TY, W><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, g, y)
+  // (one token never gets here: it goes to the dot2 GEMV; two to four
+  // tokens at K = 4096 go to the 4x4x4 matrix-core GEMV)
+  W4_DEC();
 #undef W4_DEC
 }
 

@@ -64,6 +64,11 @@ hipError_t launch_w4a16_gemv(const void* x, int64_t m, int64_t k, const uint8_t*
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,
                              int g, void* y, int y_dtype, hipStream_t st);
 bool gemv_mfma_fits(int64_t m, int64_t k, int g);
+// 2 <= M <= 4 tokens on the 4x4x4 matrix-core shape: K = 4096, g % 32 == 0.
+hipError_t launch_w4a16_quad(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                             const void* scales, const void* zeros, int sz_dtype, int64_t n,
+                             int g, void* y, int y_dtype, hipStream_t st);
+bool quad_fits(int64_t m, int64_t k, int g);
 // ws: optional float32 workspace for split K (nullptr or too small: no split).
 hipError_t launch_w4a16_gemm(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                              const void* scales, const void* zeros, int sz_dtype, int64_t n,

@@ -63,8 +63,11 @@ W4A16_CASES = [  # (m, n, k, g, sz, xkind) and the kernel the dispatcher picks
     (1, 300, 4096, 128, "f16", "bf16"),    # dot2
     (1, 129, 11008, 128, "f32", "bf16"),   # dot2, two rows per wave above K = 8192
     (1, 64, 8192, 256, "f16", "bf16"),     # dot2, groups of 256
-    (2, 300, 4096, 128, "f16", "bf16"),    # decode, straight-line form
-    (3, 77, 4096, 128, "f16", "bf16"),     # decode, straight-line form
+    (2, 300, 4096, 128, "f16", "bf16"),    # 4x4x4 matrix-core GEMV
+    (3, 77, 4096, 128, "f16", "bf16"),     # 4x4x4 matrix-core GEMV, ragged last row group
+    (4, 45, 4096, 32, "f32", "bf16"),      # 4x4x4 matrix-core GEMV, groups of 32
+    (2, 40, 4096, 512, "f16", "bf16"),     # 4x4x4 matrix-core GEMV, groups of 512
+    (3, 70, 2048, 128, "f16", "bf16"),     # decode, looped form
     (4, 200, 2048, 128, "f32", "bf16"),    # decode, looped form
     (4, 100, 1024, 256, "f16", "bf16"),    # decode, looped form, groups of 256
     (5, 300, 1024, 128, "f16", "bf16"),    # MFMA GEMV

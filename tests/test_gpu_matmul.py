@@ -95,8 +95,11 @@ DECODE = [(1, 33, 512, 128, "f16", "bf16"), (1, 4096, 4096, 128, "f16", "f32"),
           (128, 33, 2048, 256, "f32", "bf16"),
           # two row blocks per workgroup (N >= 8192) with a ragged last one
           (9, 8200, 1024, 128, "f16", "bf16"), (24, 8208, 1536, 256, "f32", "f32"),
-          # three tokens at K = 4096: the fast LDS decode kernel
-          (3, 70, 4096, 128, "f16", "bf16"),
+          # two to four tokens at K = 4096: the 4x4x4 matrix-core GEMV, groups
+          # of 32 .. 4096 columns, ragged last row group, fp32 scales
+          (3, 70, 4096, 128, "f16", "bf16"), (2, 33, 4096, 64, "f32", "f32"),
+          (4, 130, 4096, 4096, "f16", "bf16"), (3, 16, 4096, 256, "f16", "f32"),
+          (4, 1, 4096, 32, "f32", "bf16"), (2, 515, 4096, 1024, "f16", "bf16"),
           # one token, K not a multiple of 2048 (the dot2 kernel's partial
           # last chunk round), up to its K = 12288 limit
           (1, 50, 11008, 128, "f16", "bf16"), (1, 33, 2560, 256, "f32", "f32"),
