@@ -83,11 +83,12 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="skip the extra per-step measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
-    ap.add_argument("--kernel", choices=("decode_wb", "prefill_wb", "w4a8_m1", "w4a8_m512", "copy", "gptq",
-                                         "read"),
+    ap.add_argument("--kernel", choices=("decode_wb", "decode_m4_wb", "prefill_wb", "w4a8_m1", "w4a8_m512",
+                                         "copy", "gptq", "read", "llama32"),
                     default=None,
                     help="launch only this kernel --launches times, eagerly, for counter runs: "
-                         "decode_wb = the [11008,4096] decode product on rotated weights, "
+                         "decode_wb / decode_m4_wb = the [11008,4096] product at 1 / 4 tokens on rotated "
+                         "weights, llama32 = the 32-layer decode, --launches tokens (one graph each), "
                          "prefill_wb = the M=2048 product on [11008,4096], "
                          "w4a8_m1 / w4a8_m512 = the W4A8 product on [28672,8192], "
                          "copy = a plain device copy of --copy-mib MiB (calibrates byte counters), "
@@ -158,7 +159,7 @@ def main(argv=None):
         return e0.elapsed_time(e1) / 1e3 / iters
 
     if args.kernel is not None:
-        return kernel_only(args, w4, WL, torch, dev, to_dev, log)
+        return kernel_only(args, w4, WL, torch, dev, to_dev, log, time_region)
 
     g = 128
     log("generating Llama-7B decode weights")
@@ -612,7 +613,7 @@ def llama_decode(w4, torch, dev, time_region, log, g, layers=32, tokens=8):
     return res
 
 
-def kernel_only(args, w4, WL, torch, dev, to_dev, log):
+def kernel_only(args, w4, WL, torch, dev, to_dev, log, time_region):
     """Eager launches of one kernel and nothing else of note, so a counter
     run's per-dispatch records are easy to pick out."""
     n_launch = max(1, args.launches)
@@ -686,20 +687,25 @@ def kernel_only(args, w4, WL, torch, dev, to_dev, log):
                           "ops_per_launch": 2 * m * n * k}), flush=True)
         return 0
     g, n, k = 128, 11008, 4096
+    if args.kernel == "llama32":
+        res = llama_decode(w4, torch, dev, time_region, log, g, tokens=n_launch)
+        print(json.dumps(dict(res, kernel="llama32")), flush=True)
+        return 0
+    m = 4 if args.kernel == "decode_m4_wb" else 1
     wt = to_dev(WL.weight("Wb"))
     q = w4.quantize_pack_int4(wt, g, torch.float16)
     del wt
     R = max(1, args.rotate)
     copies = [tuple(a.clone() for a in q) for _ in range(R)]
-    x = to_dev(WL.activation(2, 1, k))
-    y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    x = to_dev(WL.activation(2 if m == 1 else 3, m, k))
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    log(f"decode_wb: {n_launch} launches over {R} weight copies")
+    log(f"{args.kernel}: {n_launch} launches over {R} weight copies")
     for i in range(n_launch):
         w4.w4a16_matmul(x, *copies[i % R], g, out=y)
     torch.cuda.synchronize()
-    print(json.dumps({"kernel": "decode_wb", "launches": n_launch,
-                      "bytes_per_launch": w4a16_bytes(1, n, k, g)}), flush=True)
+    print(json.dumps({"kernel": args.kernel, "launches": n_launch,
+                      "bytes_per_launch": w4a16_bytes(m, n, k, g)}), flush=True)
     return 0
 
 
