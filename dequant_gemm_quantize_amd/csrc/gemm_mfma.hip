@@ -242,6 +242,11 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
 
   const int l32 = lane & 31, lk = 8 * (lane >> 5);
   auto mma = [&](int lstage) {
+    // The compiler's interleaving of the fragment reads with the MFMAs
+    // (strategy 1 of __builtin_amdgcn_iglp_opt): Wb M = 2048 234-238 ->
+    // 229-233 us, Wd 220-223 -> 211-217 us, Wb M = 512 80-82 -> 73-76 us
+    // (same box, alternating runs).
+    __builtin_amdgcn_iglp_opt(1);
     const uint16_t* a = sA + lstage * A_STAGE + (wm * 64 + l32) * LDS_ROW + lk;
     const uint16_t* b = sB + lstage * B_STAGE + (wn * 32 * NJ + l32) * LDS_ROW + lk;
 #pragma unroll
