@@ -13,9 +13,12 @@
 //
 // Tiling.  Workgroup tile BM (M) x 128 (N), K steps of 128, BM / 32 waves in
 // a (BM / 64) x 2 arrangement, each a 64 x 64 output block (2 x 2 tiles of
-// v_mfma_i32_32x32x32_i8).  With BM = 128 two workgroups share a CU, one
-// wave of each per SIMD; the two drift apart between their barriers, so one
-// workgroup's conversions overlap the other's MFMAs.  The weight tile is turned into int8 (q - zp) once
+// v_mfma_i32_32x32x32_i8).  BM = 256 above 128 tokens; BM = 128 up to 128
+// tokens, where two workgroups share a CU, one wave of each per SIMD, and
+// the two drift apart between their barriers, so one workgroup's conversions
+// overlap the other's MFMAs ([28672, 8192] at 32 / 64 / 128 tokens: 76 / 80 /
+// 82 us against 100 / 104 / 105 us with BM = 256, which is faster from 256
+// tokens on: 114 against 126 us).  The weight tile is turned into int8 (q - zp) once
 // per workgroup while it is written to LDS; the activation tile is copied as
 // is.  Both are double-buffered in LDS; the global loads of x run one K step
 // ahead and those of the weights two, held in registers.
@@ -28,18 +31,19 @@ namespace w4 {
 
 namespace {
 
-#ifndef W4_W4A8_BM
-#define W4_W4A8_BM 256
-#endif
-constexpr int BM = W4_W4A8_BM, BN = 128, BK = 128;
-constexpr int NT = 2 * BM;            // threads: BM / 64 x 2 waves of 64 x 64 outputs
-constexpr int WB = BN * BK / 2 / NT;  // packed weight bytes per thread and K step
-constexpr int WL = BK / 2 / WB;       // lanes per weight row
+constexpr int BN = 128, BK = 128;
 constexpr int ROW = BK + 16;            // bytes per LDS row (+16 bytes of padding)
-constexpr int A_STAGE = BM * ROW;       // bytes
 constexpr int B_STAGE = BN * ROW;       // bytes
 constexpr int S_STAGE = BN * 4;         // fp32 group scales of the tile's rows
-constexpr size_t kW4a8Lds = (size_t)2 * (A_STAGE + B_STAGE + S_STAGE);
+// Shape constants of a workgroup tile of BM (128 or 256) tokens.
+template <int BM_> struct W8Tile {
+  static constexpr int BM = BM_;
+  static constexpr int NT = 2 * BM;            // threads: BM / 64 x 2 waves of 64 x 64 outputs
+  static constexpr int WB = BN * BK / 2 / NT;  // packed weight bytes per thread and K step
+  static constexpr int WL = BK / 2 / WB;       // lanes per weight row
+  static constexpr int A_STAGE = BM * ROW;     // bytes
+  static constexpr size_t lds = (size_t)2 * (A_STAGE + B_STAGE + S_STAGE);
+};
 
 template <typename TS> struct G8;
 template <> struct G8<_Float16> {
@@ -75,12 +79,14 @@ __device__ __forceinline__ void store1(void* y, int64_t i, float v) {
 
 }  // namespace
 
-template <typename TS, typename TY, bool G128>
-__global__ __launch_bounds__(NT, 512 / NT) void k_w4a8_gemm(
+template <typename TS, typename TY, bool G128, int BM>
+__global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, int64_t K,
     const uint8_t* __restrict__ packed, const void* __restrict__ scales,
     const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m, int tiles_n) {
   typedef typename G8<TS>::T R;
+  typedef W8Tile<BM> T8;
+  constexpr int NT = T8::NT, WB = T8::WB, WL = T8::WL, A_STAGE = T8::A_STAGE;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
   uint8_t* sA = smem8;                          // [2][BM][ROW]
   uint8_t* sB = smem8 + 2 * A_STAGE;            // [2][BN][ROW]
@@ -271,14 +277,15 @@ __global__ __launch_bounds__(NT, 512 / NT) void k_w4a8_gemm(
 
 bool w4a8_gemm_fits(int64_t m, int64_t k, int g) { return m > 16 && g % BK == 0 && k % BK == 0; }
 
-template <typename TS, typename TY>
-static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t k,
-                          const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
-                          int g, void* y, hipStream_t st) {
+template <typename TS, typename TY, int BM>
+static hipError_t w4a8_go_bm(const int8_t* xq, const float* xs, int64_t m, int64_t k,
+                             const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
+                             int g, void* y, hipStream_t st) {
+  typedef W8Tile<BM> T8;
   static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
   hipError_t e = once_per_device(attr_done, [] {
-    for (const void* f : {(const void*)k_w4a8_gemm<TS, TY, true>, (const void*)k_w4a8_gemm<TS, TY, false>}) {
-      hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4a8Lds);
+    for (const void* f : {(const void*)k_w4a8_gemm<TS, TY, true, BM>, (const void*)k_w4a8_gemm<TS, TY, false, BM>}) {
+      hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)T8::lds);
       if (r != hipSuccess) return r;
     }
     return hipSuccess;
@@ -287,12 +294,20 @@ static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t 
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (g == BK)
-    k_w4a8_gemm<TS, TY, true><<<grid, NT, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g,
-                                                         y, tiles_m, tiles_n);
+    k_w4a8_gemm<TS, TY, true, BM><<<grid, T8::NT, T8::lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g,
+                                                                 y, tiles_m, tiles_n);
   else
-    k_w4a8_gemm<TS, TY, false><<<grid, NT, kW4a8Lds, st>>>(xq, xs, m, k, packed, scales, zeros, n,
-                                                          g, y, tiles_m, tiles_n);
+    k_w4a8_gemm<TS, TY, false, BM><<<grid, T8::NT, T8::lds, st>>>(xq, xs, m, k, packed, scales, zeros, n,
+                                                                  g, y, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+template <typename TS, typename TY>
+static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t k,
+                          const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
+                          int g, void* y, hipStream_t st) {
+  if (m <= 128) return w4a8_go_bm<TS, TY, 128>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+  return w4a8_go_bm<TS, TY, 256>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
 }
 
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* xs, int64_t m, int64_t k,

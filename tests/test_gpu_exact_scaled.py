@@ -108,7 +108,8 @@ W4A8_CASES = [  # (m, n, k, g, sz)
     (1, 100, 640, 128, "f16"),     # int8 MFMA GEMV (K not a multiple of 2048)
     (8, 300, 1024, 128, "f16"),    # int8 MFMA GEMV
     (16, 129, 4096, 256, "f32"),   # int8 MFMA GEMV, groups of 256
-    (64, 256, 4096, 128, "f16"),   # int8 GEMM
+    (64, 256, 4096, 128, "f16"),   # int8 GEMM, 128-token tiles
+    (129, 130, 2048, 128, "f32"),  # int8 GEMM, 256-token tiles, ragged
     (300, 130, 1024, 256, "f16"),  # int8 GEMM, groups of 256
     (3, 48, 512, 64, "f16"),       # general kernel (groups of 64)
     (40, 64, 256, 32, "f32"),      # general kernel (groups of 32)
