@@ -266,15 +266,11 @@ template <typename TS, typename TY>
 static void decode_go(dim3 grid, hipStream_t st, const uint16_t* x, int M, int64_t k,
                       const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
                       int g, void* y) {
-  constexpr int W = W4_DECODE_WAVES;
-  const size_t lds = decode_lds_bytes(M, k, W);
-  const int64_t nblk = k / 128, ng = k / g;
-#define W4_DEC() \
-  k_w4a16_decode<TS, TY, W><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, g, y)
   // (one token never gets here: it goes to the dot2 GEMV; two to four
   // tokens at K = 4096 go to the 4x4x4 matrix-core GEMV)
-  W4_DEC();
-#undef W4_DEC
+  constexpr int W = W4_DECODE_WAVES;
+  const size_t lds = decode_lds_bytes(M, k, W);
+  k_w4a16_decode<TS, TY, W><<<grid, 64 * W, lds, st>>>(x, M, k, packed, scales, zeros, n, g, y);
 }
 
 hipError_t launch_w4a16_decode(const void* x, int64_t m, int64_t k, const uint8_t* packed,
