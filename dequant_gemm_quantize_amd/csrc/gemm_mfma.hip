@@ -79,14 +79,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t p, float s, float b) {
   return r;
 }
 
-// Raw buffer resource over `base` (gfx9 word 3: 32-bit data format, no
-// swizzle).  Loads through it take a uniform base, a per-lane VGPR offset and
-// a uniform SGPR offset, so advancing a K step is a scalar add.  Offsets here
-// stay below 2^31; the range check never triggers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
-}
-
 template <typename TY>
 __device__ __forceinline__ void store1(void* y, int64_t i, float v) {
   if constexpr (sizeof(TY) == 4) {
@@ -299,6 +291,15 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_gemm(
   if constexpr (D > 2) if (nmain + 2 < nloc) step(nmain + 2, std::integral_constant<int, 2 % D>{});
 
   // ---- epilogue: lane holds rows 8(r/4) + 4(lane/32) + r%4, column lane%32 --
+  const int64_t bm0 = m0 + wm * 64, bn0 = n0 + wn * 32 * NJ;  // the wave's block
+  if (bm0 + 64 <= M && bn0 + 32 * NJ <= N && N < (1 << 23)) {
+    if (part != nullptr)
+      store_wave_block<float, NJ, false>(part + (int64_t)blockIdx.y * pstride + bm0 * N + bn0, N, lane, acc,
+                                         nullptr);
+    else
+      store_wave_block<TY, NJ, false>((TY*)y + bm0 * N + bn0, N, lane, acc, nullptr);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
