@@ -372,7 +372,30 @@ def extras(args, w4, WL, torch, np, dev, stream, to_dev, time_region, log, copie
                         "frac_hbm": round(b / sec / 1e9 / HBM_PEAK_GBS, 4)}
     out["w4a8_70b_mlp"] = w8
     log(f"w4a8: {json.dumps(w8)}")
-    del cp8, p, s, z
+    del cp8
+
+    # One GPU's share of the same projection under 8-way column (N) sharding:
+    # rows 0..3583, the same kernels on [3584, 8192]; 24 copies (375 MB) are
+    # rotated so that the one-token launches read from HBM, not the 256 MB MALL.
+    ns = n // 8
+    cps = [tuple(a[:ns].clone() for a in (p, s, z)) for _ in range(24)]
+    ws = {}
+    for m in (1, 512):
+        xb = to_dev(WL.activation(5, m, 8192))
+        xq, xs = w4.quantize_act_int8(xb)
+        y = torch.empty((m, ns), dtype=torch.bfloat16, device=dev)
+        fn = lambda i: w4.w4a8_matmul(xq, xs, *cps[i % len(cps)], g, out=y)
+        for i in range(3):
+            fn(i)
+        sec = time_region(fn, reps)
+        b = w4a8_bytes(m, ns, k, g)
+        ws[f"M={m}"] = {"us": round(sec * 1e6, 2), "GB/s": round(b / sec / 1e9, 1),
+                        "TOP/s": round(2 * m * ns * k / sec / 1e12, 2),
+                        "frac_int8_peak": round(2 * m * ns * k / sec / 1e12 / INT8_PEAK_TOPS, 4),
+                        "frac_hbm": round(b / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    out["w4a8_70b_mlp_tp8_shard_3584x8192"] = ws
+    log(f"w4a8 tp8 shard: {json.dumps(ws)}")
+    del cps, p, s, z
 
     # single fp32 layer (latency bound)
     t1 = WL.weight("W1")
