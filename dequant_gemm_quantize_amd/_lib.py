@@ -37,6 +37,9 @@ SIGNATURES = [
                              ctypes.c_size_t, _VP]),
     ("w4a16_matmul_noalloc", _I, [_VP, _I, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
     ("w4a8_matmul", _I, [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP]),
+    ("w4a8_matmul_workspace_size", ctypes.c_size_t, [_I64, _I64, _I64, _I32]),
+    ("w4a8_matmul_ws", _I, [_VP, _VP, _I64, _I64, _VP, _VP, _VP, _I, _I64, _I32, _VP, _I, _VP,
+                            ctypes.c_size_t, _VP]),
     ("gptq_hessian", _I, [_VP, _I64, _I64, _VP, _VP]),
     ("gptq_inverse_cholesky", _I, [_VP, _I64, _VP, _VP, _VP]),
     ("gptq_quantize_pack_int4", _I, [_VP, _VP, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _I, _VP]),
@@ -358,10 +361,20 @@ def w4a16_matmul(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, ze
     return y
 
 
+def w4a8_matmul_workspace_size(m: int, k: int, n: int, group_size: int) -> int:
+    """Bytes of workspace with which w4a8_matmul splits K for this shape (0: none)."""
+    return int(load().w4a8_matmul_workspace_size(m, k, n, group_size))
+
+
 def w4a8_matmul(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                 zeros: torch.Tensor, group_size: int, out_dtype: torch.dtype = torch.bfloat16,
-                out: Optional[torch.Tensor] = None):
-    """y [M, N] = x_scale[m] * (xq [M, K] . dequant(W)^T)."""
+                out: Optional[torch.Tensor] = None, workspace="auto"):
+    """y [M, N] = x_scale[m] * (xq [M, K] . dequant(W)^T).
+
+    workspace: "auto" (default) allocates, through torch, the workspace the
+    library asks for on this shape (none for most shapes) and calls
+    w4a8_matmul_ws; a uint8 device tensor is used as given; None calls
+    w4a8_matmul, which uses none."""
     lib = load()
     m, k = _matrix(xq, "xq")
     _expect(xq, "xq", (m, k), (torch.int8,))
@@ -374,9 +387,20 @@ def w4a8_matmul(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor, s
     dev = _gpu(xq, x_scale, packed, scales, zeros)
     y = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
     _gpu(y)
-    _check(lib.w4a8_matmul(_ptr(xq), _ptr(x_scale), m, k, _ptr(packed), _ptr(scales), _ptr(zeros),
-                           _dtype_code(scales.dtype), n, group_size, _ptr(y), _dtype_code(y.dtype),
-                           _stream(dev)))
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 tensor')
+        nbytes = int(lib.w4a8_matmul_workspace_size(m, k, n, group_size))
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
+    args = (_ptr(xq), _ptr(x_scale), m, k, _ptr(packed), _ptr(scales), _ptr(zeros),
+            _dtype_code(scales.dtype), n, group_size, _ptr(y), _dtype_code(y.dtype))
+    if workspace is None:
+        _check(lib.w4a8_matmul(*args, _stream(dev)))
+    else:
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        _gpu(workspace)
+        _check(lib.w4a8_matmul_ws(*args, _ptr(workspace), workspace.numel(), _stream(dev)))
     return y
 
 

@@ -380,10 +380,11 @@ int w4a16_matmul_ws(const void* x, int x_dtype, int64_t m, int64_t k, const uint
                       group_size, y, y_dtype, workspace, workspace_bytes, false, stream);
 }
 
-int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
-                const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
-                int64_t n, int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
-  static const char* fn = "w4a8_matmul";
+// ws / ws_bytes: the caller's workspace (w4a8_matmul_ws), or none.
+static int w4a8_common(const char* fn, const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
+                       const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                       int64_t n, int32_t group_size, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
   W4_TRY(check_weights(fn, n, k, group_size, sz_dtype));
   if (y_dtype != W4_F32 && y_dtype != W4_BF16)
     return fail(W4_EINVAL, "%s: y dtype %d must be W4_F32 or W4_BF16", fn, y_dtype);
@@ -397,10 +398,13 @@ int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
   if (x_scale == nullptr) return fail(W4_EINVAL, "%s: x_scale is NULL", fn);
   if ((reinterpret_cast<uintptr_t>(x_scale) & 3u) != 0)
     return fail(W4_EINVAL, "%s: x_scale is not 4-byte aligned", fn);
+  if (ws != nullptr && ws_bytes > 0 && !aligned16(ws))
+    return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
   // Kernel choice: one to four tokens, group 128, K a multiple of 2048 up to
   // 8192 -> the dot4 GEMV; up to 16 tokens, groups of a multiple of 128 ->
-  // the int8 MFMA GEMV; more tokens -> the int8 MFMA GEMM; everything else -> the
-  // general kernel.
+  // the int8 MFMA GEMV; more tokens -> the int8 MFMA GEMM (split K over the
+  // workspace when its tiles would leave most of the GPU idle); everything
+  // else -> the general kernel.
   if (w4::w4a8_gemv_fits(m, k, group_size))
     return hip_status(w4::launch_w4a8_gemv(xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n,
                                            group_size, y, y_dtype, stream),
@@ -411,11 +415,36 @@ int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
                       fn);
   if (w4::w4a8_gemm_fits(m, k, group_size))
     return hip_status(w4::launch_w4a8_gemm(xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n,
-                                           group_size, y, y_dtype, stream),
+                                           group_size, y, y_dtype, ws, ws_bytes, stream),
                       fn);
   return hip_status(w4::launch_w4a8_generic(xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n,
                                             group_size, y, y_dtype, stream),
                     fn);
+}
+
+int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
+                const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                int64_t n, int32_t group_size, void* y, int y_dtype, hipStream_t stream) {
+  return w4a8_common("w4a8_matmul", xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n, group_size,
+                     y, y_dtype, nullptr, 0, stream);
+}
+
+size_t w4a8_matmul_workspace_size(int64_t m, int64_t k, int64_t n, int32_t group_size) {
+  // Shapes the other entry points would reject need no workspace.
+  if (m <= 0 || n <= 0 || k <= 0 || k > kMaxK || group_size <= 0 || group_size % 32 != 0 ||
+      k % group_size != 0 || n > kMaxElems / k || m > 0x7fffffffLL || m > kMaxElems / k ||
+      m > kMaxElems / n)
+    return 0;
+  if (w4::w4a8_gemv_fits(m, k, group_size) || w4::w4a8_gemv_mfma_fits(m, k, group_size)) return 0;
+  return w4::w4a8_gemm_workspace_bytes(m, k, n, group_size);
+}
+
+int w4a8_matmul_ws(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
+                   const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                   int64_t n, int32_t group_size, void* y, int y_dtype, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return w4a8_common("w4a8_matmul_ws", xq, x_scale, m, k, packed, scales, zeros, sz_dtype, n,
+                     group_size, y, y_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

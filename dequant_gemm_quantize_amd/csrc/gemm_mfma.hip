@@ -443,6 +443,16 @@ static hipError_t gemm_go(const uint16_t* x, int64_t m, int64_t k, const uint8_t
   return hipGetLastError();
 }
 
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t mn, int64_t pstride, void* y,
+                                int y_dtype, hipStream_t st) {
+  const dim3 rgrid((unsigned)((mn + 1023) / 1024));
+  if (y_dtype == W4_F32)
+    k_splitk_reduce<float><<<rgrid, 256, 0, st>>>(part, S, mn, pstride, y);
+  else
+    k_splitk_reduce<__bf16><<<rgrid, 256, 0, st>>>(part, S, mn, pstride, y);
+  return hipGetLastError();
+}
+
 template <typename TS, typename TY>
 static hipError_t gemm_go_g(const uint16_t* x, int64_t m, int64_t k, const uint8_t* packed,
                             const void* scales, const void* zeros, int64_t n, int g, void* y,

@@ -83,7 +83,8 @@ template <typename TS, typename TY, bool G128, int BM>
 __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
     const int8_t* __restrict__ xq, const float* __restrict__ xs, int64_t M, int64_t K,
     const uint8_t* __restrict__ packed, const void* __restrict__ scales,
-    const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m, int tiles_n) {
+    const void* __restrict__ zeros, int64_t N, int g, void* __restrict__ y, int tiles_m, int tiles_n,
+    int kps, float* __restrict__ part, int64_t pstride) {
   typedef typename G8<TS>::T R;
   typedef W8Tile<BM> T8;
   constexpr int NT = T8::NT, WB = T8::WB, WL = T8::WL, A_STAGE = T8::A_STAGE;
@@ -138,7 +139,10 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
   // x runs one K step ahead of the MFMAs, the weights (HBM) two.  Loads past
   // the last step are clamped to it, so the loop has no conditional loads.
   constexpr int WV = WB / 16;
-  const int nks = (int)(K / BK);
+  // Split K: workgroup (tile, s = blockIdx.y) covers K steps [ks0, nks).
+  const int ks0 = (int)blockIdx.y * kps;
+  const int nks_all = (int)(K / BK);
+  const int nks = (nks_all - ks0 < kps ? nks_all - ks0 : kps) + ks0;  // one past the split's last step
   u32x4 xv[4];
   u32x4 wv[2][WV];
   R sv[2], zv[2];
@@ -228,11 +232,13 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
     half(lstage, std::integral_constant<int, 1>{}, bfr);  // folds half 0 of this step
   };
 
-  xload(0);
-  wload(0, std::integral_constant<int, 0>{});
-  wload(1, std::integral_constant<int, 1>{});
+  // Steps are counted from the split's first one: local step t is K step
+  // ks0 + t (the loads clamp past the split's last step).
+  xload(ks0 + 0);
+  wload(ks0 + 0, std::integral_constant<int, 0>{});
+  wload(ks0 + 1, std::integral_constant<int, 1>{});
   lstore(0, std::integral_constant<int, 0>{});
-  xload(1);
+  xload(ks0 + 1);
   __syncthreads();
 
   // One K step: weights for ks + 2 in flight, MFMAs on buffer ks & 1, step
@@ -240,18 +246,19 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
   // then x for ks + 2.
   auto step = [&](int ks, auto stage) {
     constexpr int u = decltype(stage)::value;  // ks mod 2
-    wload(ks + 2, stage);     // register stage u: step ks's weights are in LDS
+    wload(ks0 + ks + 2, stage);  // register stage u: step ks's weights are in LDS
     mma(ks & 1);
     lstore((ks + 1) & 1, std::integral_constant<int, 1 - u>{});
     __syncthreads();
-    xload(ks + 2);
+    xload(ks0 + ks + 2);
   };
-  const int nmain = nks & ~1;
+  const int nloc = nks - ks0;  // steps of this split
+  const int nmain = nloc & ~1;
   for (int ks = 0; ks < nmain; ks += 2) {
     step(ks, std::integral_constant<int, 0>{});
     step(ks + 1, std::integral_constant<int, 1>{});
   }
-  if (nmain < nks) step(nmain, std::integral_constant<int, 0>{});
+  if (nmain < nloc) step(nmain, std::integral_constant<int, 0>{});
   // fold half 1 of the last step
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -262,10 +269,16 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
   // Whole 64 x 64 blocks take the store without bounds tests (M = 512:
   // 210-213 -> 195-197 us).  Not with BM = 128: there the extra live values
   // reorder the main loop's loads, and 32 to 128 tokens got 10-20% slower.
+  // With split K the token-scaled float32 partial goes to part + s * pstride
+  // as [M][N]; k_splitk_reduce adds the splits and rounds once.
+  float* pdst = part != nullptr ? part + (int64_t)blockIdx.y * pstride : nullptr;
   if constexpr (BM == 256) {
     const int64_t bm0 = m0 + wm * 64, bn0 = n0 + wn * 64;  // the wave's block
     if (bm0 + 64 <= M && bn0 + 64 <= N && N < (1 << 23)) {
-      store_wave_block<TY, 2, true>((TY*)y + bm0 * N + bn0, N, lane, acc, xs + bm0);
+      if (pdst != nullptr)
+        store_wave_block<float, 2, true>(pdst + bm0 * N + bn0, N, lane, acc, xs + bm0);
+      else
+        store_wave_block<TY, 2, true>((TY*)y + bm0 * N + bn0, N, lane, acc, xs + bm0);
       return;
     }
   }
@@ -279,7 +292,12 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t n = n0 + wn * 64 + 32 * j + l32;
-        if (n < N) store1<TY>(y, m * N + n, sa * acc[i][j][r]);
+        if (n < N) {
+          if (pdst != nullptr)
+            pdst[m * N + n] = sa * acc[i][j][r];
+          else
+            store1<TY>(y, m * N + n, sa * acc[i][j][r]);
+        }
       }
     }
   }
@@ -287,10 +305,49 @@ __global__ __launch_bounds__(2 * BM, 256 / BM) void k_w4a8_gemm(
 
 bool w4a8_gemm_fits(int64_t m, int64_t k, int g) { return m > 16 && g % BK == 0 && k % BK == 0; }
 
+// Split-K plan: shapes with fewer than 128 tiles (one GPU's 8-way column
+// shard of the [28672, 8192] projection, [3584, 8192], has 28 tiles of
+// 128 x 128 up to 128 tokens and 56 of 256 x 128 at 512) split K so that
+// about 256 workgroups run, at least 8 K steps per split, with the float32
+// partials within kSplitKMaxBytes.  Measured on the shard: 17 / 128 / 512 /
+// 1024 tokens 59 / 66 / 78 / 82 -> 19 / 29 / 37 / 59 us.  The whole
+// projection at 17 to 128 tokens (224 tiles) does not split: two splits there
+// measured 70-76 -> 79-94 us.
+struct SplitK8 {
+  int bm = 256, s = 1, kps = 0;
+  int64_t pstride = 0;  // floats per split's partial: M * N rounded up to a multiple of 4
+  size_t bytes = 0;
+};
+static SplitK8 w4a8_splitk_plan(int64_t m, int64_t k, int64_t n) {
+  SplitK8 p;
+  p.bm = m <= 128 ? 128 : 256;
+  const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + BN - 1) / BN);
+  const int64_t nks = k / BK;
+  p.kps = (int)nks;
+  if (tiles >= 128) return p;
+  int64_t s = (256 + tiles - 1) / tiles;
+  if (s > nks / 8) s = nks / 8;
+  const int64_t pstride = (m * n + 3) / 4 * 4;
+  const int64_t fit = (int64_t)(kSplitKMaxBytes / ((size_t)pstride * 4));
+  if (s > fit) s = fit;
+  if (s < 2) return p;
+  p.kps = (int)((nks + s - 1) / s);
+  p.s = (int)((nks + p.kps - 1) / p.kps);
+  p.pstride = pstride;
+  p.bytes = (size_t)p.s * (size_t)pstride * 4;
+  return p;
+}
+
+size_t w4a8_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int g) {
+  if (!w4a8_gemm_fits(m, k, g)) return 0;
+  const SplitK8 p = w4a8_splitk_plan(m, k, n);
+  return p.s > 1 ? p.bytes : 0;
+}
+
 template <typename TS, typename TY, int BM>
 static hipError_t w4a8_go_bm(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                              const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
-                             int g, void* y, hipStream_t st) {
+                             int g, void* y, const SplitK8& p, float* part, hipStream_t st) {
   typedef W8Tile<BM> T8;
   static std::atomic<uint64_t> attr_done{0};  // LDS above the 64 KB default
   hipError_t e = once_per_device(attr_done, [] {
@@ -302,33 +359,48 @@ static hipError_t w4a8_go_bm(const int8_t* xq, const float* xs, int64_t m, int64
   });
   if (e != hipSuccess) return e;
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.s);
   if (g == BK)
     k_w4a8_gemm<TS, TY, true, BM><<<grid, T8::NT, T8::lds, st>>>(xq, xs, m, k, packed, scales, zeros, n, g,
-                                                                 y, tiles_m, tiles_n);
+                                                                 y, tiles_m, tiles_n, p.kps, part, p.pstride);
   else
     k_w4a8_gemm<TS, TY, false, BM><<<grid, T8::NT, T8::lds, st>>>(xq, xs, m, k, packed, scales, zeros, n,
-                                                                  g, y, tiles_m, tiles_n);
+                                                                  g, y, tiles_m, tiles_n, p.kps, part,
+                                                                  p.pstride);
   return hipGetLastError();
 }
 
 template <typename TS, typename TY>
 static hipError_t w4a8_go(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                           const uint8_t* packed, const void* scales, const void* zeros, int64_t n,
-                          int g, void* y, hipStream_t st) {
-  if (m <= 128) return w4a8_go_bm<TS, TY, 128>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
-  return w4a8_go_bm<TS, TY, 256>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+                          int g, void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t st) {
+  SplitK8 p = w4a8_splitk_plan(m, k, n);
+  if (p.s > 1 && (ws == nullptr || ws_bytes < p.bytes)) {
+    p.s = 1;
+    p.kps = (int)(k / BK);
+    p.pstride = 0;
+    p.bytes = 0;
+  }
+  float* part = p.s > 1 ? (float*)ws : nullptr;
+  const hipError_t e =
+      m <= 128 ? w4a8_go_bm<TS, TY, 128>(xq, xs, m, k, packed, scales, zeros, n, g, y, p, part, st)
+               : w4a8_go_bm<TS, TY, 256>(xq, xs, m, k, packed, scales, zeros, n, g, y, p, part, st);
+  if (e != hipSuccess || p.s == 1) return e;
+  return launch_splitk_reduce(part, p.s, m * n, p.pstride, y, y_dtype, st);
 }
 
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                             const uint8_t* packed, const void* scales, const void* zeros,
-                            int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st) {
+                            int sz_dtype, int64_t n, int g, void* y, int y_dtype, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
   if (sz_dtype == W4_F16) {
-    if (y_dtype == W4_F32) return w4a8_go<_Float16, float>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
-    return w4a8_go<_Float16, __bf16>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+    if (y_dtype == W4_F32)
+      return w4a8_go<_Float16, float>(xq, xs, m, k, packed, scales, zeros, n, g, y, y_dtype, ws, ws_bytes, st);
+    return w4a8_go<_Float16, __bf16>(xq, xs, m, k, packed, scales, zeros, n, g, y, y_dtype, ws, ws_bytes, st);
   }
-  if (y_dtype == W4_F32) return w4a8_go<float, float>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
-  return w4a8_go<float, __bf16>(xq, xs, m, k, packed, scales, zeros, n, g, y, st);
+  if (y_dtype == W4_F32)
+    return w4a8_go<float, float>(xq, xs, m, k, packed, scales, zeros, n, g, y, y_dtype, ws, ws_bytes, st);
+  return w4a8_go<float, __bf16>(xq, xs, m, k, packed, scales, zeros, n, g, y, y_dtype, ws, ws_bytes, st);
 }
 
 }  // namespace w4

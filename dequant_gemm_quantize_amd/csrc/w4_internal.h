@@ -90,10 +90,19 @@ hipError_t launch_w4a8_gemv_mfma(const int8_t* xq, const float* xs, int64_t m, i
                                  int sz_dtype, int64_t n, int g, void* y, int y_dtype,
                                  hipStream_t st);
 bool w4a8_gemv_mfma_fits(int64_t m, int64_t k, int g);
+// ws: optional float32 workspace for split K (nullptr or too small: no split).
 hipError_t launch_w4a8_gemm(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                             const uint8_t* packed, const void* scales, const void* zeros,
-                            int sz_dtype, int64_t n, int g, void* y, int y_dtype, hipStream_t st);
+                            int sz_dtype, int64_t n, int g, void* y, int y_dtype, void* ws,
+                            size_t ws_bytes, hipStream_t st);
 bool w4a8_gemm_fits(int64_t m, int64_t k, int g);
+// Bytes of workspace the W4A8 GEMM uses for split K on this shape (0: it does
+// not split); never above kSplitKMaxBytes.
+size_t w4a8_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int g);
+// y = the sum, in order s = 0 .. S-1, of the float32 partials part + s *
+// pstride ([M][N], MN elements each), rounded once to y_dtype.
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t mn, int64_t pstride, void* y,
+                                int y_dtype, hipStream_t st);
 hipError_t launch_w4a8_generic(const int8_t* xq, const float* xs, int64_t m, int64_t k,
                                const uint8_t* packed, const void* scales, const void* zeros,
                                int sz_dtype, int64_t n, int g, void* y, int y_dtype,

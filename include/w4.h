@@ -239,6 +239,39 @@ int w4a8_matmul(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
                 int64_t n, int32_t group_size, void* y, int y_dtype, hipStream_t stream);
 
 /*
+ * w4a8_matmul_workspace_size / w4a8_matmul_ws -- w4a8_matmul with a
+ * caller-provided device workspace ([P1] Step 5; the workspace changes how
+ * the product is scheduled, not what it computes).
+ *
+ * Shapes whose output tiles would leave most of the GPU's 256 compute units
+ * idle (for example one GPU's 8-way column shard [3584, 8192] of the
+ * [28672, 8192] projection at 512 tokens: 56 tiles) split K across
+ * workgroups: each writes its token-scaled float32 partial tile to the
+ * workspace and a second kernel adds the partials in a fixed order and
+ * rounds once to y_dtype.  Results are deterministic and meet the accuracy
+ * bound of w4a8_matmul; the integer sums stay exact (a split boundary falls
+ * between 128-column K steps, and each step lies inside one group).
+ *
+ * w4a8_matmul_workspace_size returns the bytes of workspace that let
+ * w4a8_matmul_ws split K for this shape: 0 when it would not split (it then
+ * behaves as w4a8_matmul), at most 32 MiB.  It depends only on its
+ * arguments, enqueues nothing and returns 0 for arguments the other calls
+ * reject.
+ *
+ * w4a8_matmul_ws takes w4a8_matmul's arguments plus `workspace` (device
+ * memory, 16-byte aligned, owned by the caller; its contents on entry are
+ * ignored and on return unspecified) of `workspace_bytes`.  With
+ * workspace_bytes below the queried size, or workspace NULL, it runs
+ * exactly as w4a8_matmul.  Calls that overlap on one workspace race.
+ * Errors as w4a8_matmul, plus W4_EINVAL for a misaligned workspace.
+ */
+size_t w4a8_matmul_workspace_size(int64_t m, int64_t k, int64_t n, int32_t group_size);
+int w4a8_matmul_ws(const int8_t* xq, const float* x_scale, int64_t m, int64_t k,
+                   const uint8_t* packed, const void* scales, const void* zeros, int sz_dtype,
+                   int64_t n, int32_t group_size, void* y, int y_dtype, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * GPTQ second-order quantization ([P4] Step 3), in three calls.  Together
  * they produce the packed format above from a weight and calibration rows;
  * every matmul here takes the result.

@@ -361,6 +361,23 @@ def test_workspace_size_query(lib):
     assert w4.w4a16_matmul_workspace_size(256, 11008, 4096, 128, torch_float32()) == 0  # fp32 x: general kernel
 
 
+def test_w4a8_workspace_size_query(lib):
+    """w4a8_matmul_workspace_size is host-only: split K for one GPU's 8-way
+    column shard [3584, 8192] from 17 tokens on (32 MiB at most), none for the
+    whole [28672, 8192] projection at 512 tokens, the GEMV token counts or
+    invalid arguments."""
+    import dequant_gemm_quantize_amd as w4
+    for m in (17, 128, 129, 512):
+        assert 0 < w4.w4a8_matmul_workspace_size(m, 8192, 3584, 128) <= 32 << 20, m
+    assert w4.w4a8_matmul_workspace_size(512, 8192, 28672, 128) == 0
+    assert w4.w4a8_matmul_workspace_size(2048, 8192, 3584, 128) == 0
+    for m in (1, 4, 16):                                                  # GEMV paths
+        assert w4.w4a8_matmul_workspace_size(m, 8192, 3584, 128) == 0, m
+    assert w4.w4a8_matmul_workspace_size(512, 8192, 3584, 96) == 0       # not a multiple of 128: general kernel
+    assert w4.w4a8_matmul_workspace_size(512, 8192, 3584, 100) == 0      # invalid group
+    assert w4.w4a8_matmul_workspace_size(0, 8192, 3584, 128) == 0
+
+
 def torch_float32():
     import torch
     return torch.float32

@@ -94,6 +94,15 @@ int main() {
   for (int64_t m : {1, 4, 16, 17, 512})
     expect(w4a8_matmul((int8_t*)A, (float*)A, m, 8192, P, A, A, W4_F16, 28672, 128, A, W4_BF16, nullptr), W4_OK, "w4a8 ok");
   expect(w4a8_matmul((int8_t*)A, (float*)U, 1, 8192, P, A, A, W4_F16, 28672, 128, A, W4_BF16, nullptr), W4_OK, "w4a8 scale 4B");
+  expect(w4a8_matmul_ws((int8_t*)A, (float*)A, 512, 8192, P, A, A, W4_F16, 3584, 128, A, W4_BF16, A, 4096, nullptr), W4_OK, "w4a8 ws ok");
+  expect(w4a8_matmul_ws((int8_t*)A, (float*)A, 512, 8192, P, A, A, W4_F16, 3584, 128, A, W4_BF16, nullptr, 0, nullptr), W4_OK, "w4a8 ws null");
+  expect(w4a8_matmul_ws((int8_t*)A, (float*)A, 512, 8192, P, A, A, W4_F16, 3584, 128, A, W4_BF16, U, 4096, nullptr), W4_EINVAL, "w4a8 ws misaligned");
+  expect(w4a8_matmul_ws((int8_t*)A, (float*)A, BIG, 8192, P, A, A, W4_F16, BIG, 128, A, W4_BF16, A, 4096, nullptr), W4_EINVAL, "w4a8 ws huge");
+  expect(w4a8_matmul_ws((int8_t*)A, (float*)U, 1, 8192, P, A, A, W4_F16, 3584, 128, A, W4_BF16, A, 4096, nullptr), W4_OK, "w4a8 ws scale 4B");
+  expect(w4a8_matmul_ws((int8_t*)A, (float*)(buf + 2), 1, 8192, P, A, A, W4_F16, 3584, 128, A, W4_BF16, A, 4096, nullptr), W4_EINVAL, "w4a8 ws scale 2B");
+  expect((int)w4a8_matmul_workspace_size(BIG, BIG, BIG, 128), 0, "w4a8 ws size huge");
+  expect((int)w4a8_matmul_workspace_size(512, 8192, 3584, 100), 0, "w4a8 ws size bad g");
+  expect((int)w4a8_matmul_workspace_size(-1, 8192, 3584, 128), 0, "w4a8 ws size m<0");
   // GPTQ
   expect(gptq_hessian((const float*)A, 4096, 4096, (double*)A, nullptr), W4_OK, "hess ok");
   expect(gptq_hessian((const float*)A, BIG, 4096, (double*)A, nullptr), W4_EINVAL, "hess t huge");

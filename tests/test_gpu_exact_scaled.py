@@ -111,15 +111,20 @@ W4A8_CASES = [  # (m, n, k, g, sz)
     (64, 256, 4096, 128, "f16"),   # int8 GEMM, 128-token tiles
     (129, 130, 2048, 128, "f32"),  # int8 GEMM, 256-token tiles, ragged
     (300, 130, 1024, 256, "f16"),  # int8 GEMM, groups of 256
+    (129, 520, 4096, 128, "f16"),  # int8 GEMM, split K over the workspace (4 splits)
+    (300, 130, 2304, 256, "f32"),  # int8 GEMM, split K at step 9: inside a group of 256
+    (40, 1000, 8192, 128, "f16"),  # int8 GEMM, 128-token tiles, split K (8 splits)
     (3, 48, 512, 64, "f16"),       # general kernel (groups of 64)
     (40, 64, 256, 32, "f32"),      # general kernel (groups of 32)
 ]
 
 
 @pytest.mark.parametrize("m,n,k,g,sz", W4A8_CASES)
-def test_w4a8_scaled_exact(w4, m, n, k, g, sz):
+@pytest.mark.parametrize("ws", ["auto", None])
+def test_w4a8_scaled_exact(w4, m, n, k, g, sz, ws):
     """Activations: integers with |x| <= 8 and one 127 per token, so the
-    per-token scale is 1 and xq = x."""
+    per-token scale is 1 and xq = x.  ws: with the workspace the library asks
+    for (split K where the shape splits) and without one."""
     rng = np.random.default_rng(m * 104729 + n * 17 + k + g)
     w, q, e, z = scaled_weights(rng, n, k, g)
     p, s, zz = quantize_on_gpu(w4, w, g, sz, q, e, z)
@@ -127,7 +132,7 @@ def test_w4a8_scaled_exact(w4, m, n, k, g, sz):
     xi[np.arange(m), rng.integers(0, k, m)] = 127
     xq, xs = w4.quantize_act_int8(to_dev(WL.bf16_round_bits(xi.astype(np.float32)), "bf16"))
     assert (to_host(xs) == 1.0).all() and np.array_equal(to_host(xq), xi.astype(np.int8))
-    y = to_host(w4.w4a8_matmul(xq, xs, p, s, zz, g))
+    y = to_host(w4.w4a8_matmul(xq, xs, p, s, zz, g, workspace=ws))
     want = O.to_bf16(exact_product(xi, q, e, z, g).astype(np.float32))
     bad = np.argwhere(y != want)
     assert bad.size == 0, (bad[:5], y[tuple(bad[0])], want[tuple(bad[0])])

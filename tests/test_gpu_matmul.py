@@ -362,6 +362,48 @@ def test_w4a8_gemm(w4, m, n, k, g, sz, ykind):
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
 
 
+# Shapes whose int8-GEMM tiles leave most of the GPU idle split K over the
+# workspace: ragged M and N, 128- and 256-token tiles, groups of 256 cut by a
+# split boundary (K = 2304: 18 steps, splits of 9), fp32 scales.
+W8_SPLITK = [(17, 300, 4096, 128, "f16"), (40, 1000, 8192, 128, "f32"), (129, 520, 4096, 128, "f16"),
+             (300, 1000, 2304, 256, "f16"), (257, 130, 8192, 128, "f32")]
+
+
+@pytest.mark.parametrize("m,n,k,g,sz", W8_SPLITK)
+@pytest.mark.parametrize("ykind", ["bf16", "f32"])
+def test_w4a8_splitk(w4, m, n, k, g, sz, ykind):
+    assert w4.w4a8_matmul_workspace_size(m, k, n, g) > 0
+    P, S, Z = make_weights(n, k, g, sz, seed=3 * m + n + k, sigma=0.015)
+    rng = np.random.default_rng(m + 17)
+    x = rng.normal(0, 1, (m, k)).astype(np.float32)
+    x[:, rng.choice(k, max(1, k // 20), replace=False)] *= 20
+    xb = WL.bf16_round_bits(x)
+    y, xq, xs = run_w4a8(w4, xb, "bf16", dev_weights(P, S, Z, sz), g, ykind)
+    oq, os_ = O.act_quant_int8(O.widen_bf16(xb))
+    ref = O.matmul_w4a8_f64(oq, os_, P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
+    # the unsplit schedule meets the same bound
+    plain = w4.w4a8_matmul(to_dev(oq, "i8"), to_dev(os_, "f32"), *dev_weights(P, S, Z, sz), g,
+                           out_dtype=TDT[ykind], workspace=None)
+    assert O.max_rel_err(y_as_f64(plain), ref) <= TOL[ykind]
+
+
+def test_w4a8_splitk_tp8_shard(w4):
+    """One GPU's 8-way column shard of the [28672, 8192] projection (its first
+    3584 rows) at 512 tokens of heavy-tailed activations: 56 tiles, split K;
+    64 sampled tokens against the oracle."""
+    t = WL.weight("We")
+    n, k, g = 3584, 8192, 128
+    w = t.data[:n]
+    P, S, Z = O.quantize_pack_int4(w, t.kind, g, "f16")
+    assert w4.w4a8_matmul_workspace_size(512, k, n, g) > 0
+    xb = WL.activation(5, 512, k)
+    y, xq, xs = run_w4a8(w4, xb.data, xb.kind, dev_weights(P, S, Z, "f16"), g)
+    rows = np.arange(0, 512, 8)
+    ref = O.matmul_w4a8_f64(xq[rows], xs[rows], P, S, Z, g)
+    assert O.max_rel_err(y_as_f64(y)[rows], ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 64, 8192), (3, 48, 4096), (8, 48, 1024), (16, 64, 1024),
                                    (64, 256, 8192), (300, 130, 256)])
 def test_w4a8_exact_integers(w4, m, n, k):
