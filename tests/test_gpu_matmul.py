@@ -383,9 +383,18 @@ def test_w4a8_splitk(w4, m, n, k, g, sz, ykind):
     ref = O.matmul_w4a8_f64(oq, os_, P, S, Z, g)
     assert O.max_rel_err(y_as_f64(y), ref) <= TOL[ykind]
     # the unsplit schedule meets the same bound
-    plain = w4.w4a8_matmul(to_dev(oq, "i8"), to_dev(os_, "f32"), *dev_weights(P, S, Z, sz), g,
-                           out_dtype=TDT[ykind], workspace=None)
+    dw = dev_weights(P, S, Z, sz)
+    xq_d, xs_d = to_dev(oq, "i8"), to_dev(os_, "f32")
+    plain = w4.w4a8_matmul(xq_d, xs_d, *dw, g, out_dtype=TDT[ykind], workspace=None)
     assert O.max_rel_err(y_as_f64(plain), ref) <= TOL[ykind]
+    # deterministic: the split product again, bit for bit; a workspace one
+    # byte short of the query runs the unsplit kernel, bit for bit
+    nbytes = w4.w4a8_matmul_workspace_size(m, k, n, g)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    again = w4.w4a8_matmul(xq_d, xs_d, *dw, g, out_dtype=TDT[ykind], workspace=ws)
+    assert np.array_equal(bits(to_host(again)), bits(to_host(y)))
+    short = w4.w4a8_matmul(xq_d, xs_d, *dw, g, out_dtype=TDT[ykind], workspace=ws[: nbytes - 1])
+    assert np.array_equal(bits(to_host(short)), bits(to_host(plain)))
 
 
 def test_w4a8_splitk_tp8_shard(w4):
