@@ -84,13 +84,15 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
     ap.add_argument("--kernel", choices=("decode_wb", "decode_m4_wb", "prefill_wb", "w4a8_m1", "w4a8_m512",
-                                         "copy", "gptq", "read", "llama32"),
+                                         "w4a8_shard_m512", "copy", "gptq", "read", "llama32"),
                     default=None,
                     help="launch only this kernel --launches times, eagerly, for counter runs: "
                          "decode_wb / decode_m4_wb = the [11008,4096] product at 1 / 4 tokens on rotated "
                          "weights, llama32 = the 32-layer decode, --launches tokens (one graph each), "
                          "prefill_wb = the M=2048 product on [11008,4096], "
                          "w4a8_m1 / w4a8_m512 = the W4A8 product on [28672,8192], "
+                         "w4a8_shard_m512 = the same at 512 tokens on its first 3584 rows (one GPU's "
+                         "8-way column shard; split K over the workspace), "
                          "copy = a plain device copy of --copy-mib MiB (calibrates byte counters), "
                          "read = the streaming-read measurement kernel over the decode product's byte "
                          "count, rotated through a 1 GiB buffer")
@@ -692,12 +694,15 @@ def kernel_only(args, w4, WL, torch, dev, to_dev, log, time_region):
         print(json.dumps({"kernel": "prefill_wb", "launches": n_launch,
                           "flops_per_launch": 2 * 2048 * n * k}), flush=True)
         return 0
-    if args.kernel in ("w4a8_m1", "w4a8_m512"):
+    if args.kernel in ("w4a8_m1", "w4a8_m512", "w4a8_shard_m512"):
         g, n, k = 128, 28672, 8192
         m = 1 if args.kernel == "w4a8_m1" else 512
         wt = to_dev(WL.weight("We"))
         q = w4.quantize_pack_int4(wt, g, torch.float16)
         del wt
+        if args.kernel == "w4a8_shard_m512":
+            n = n // 8
+            q = tuple(a[:n].clone() for a in q)
         copies = [q] + [tuple(a.clone() for a in q) for _ in range(3)]
         xq, xs = w4.quantize_act_int8(to_dev(WL.activation(5, m, k)))
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
