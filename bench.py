@@ -84,10 +84,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the CPU oracle sample")
     ap.add_argument("--kernel", choices=("decode_wb", "decode_m4_wb", "prefill_wb", "w4a8_m1", "w4a8_m512",
-                                         "w4a8_shard_m512", "copy", "gptq", "read", "llama32"),
+                                         "w4a8_shard_m512", "decode_m8_wb", "copy", "gptq", "read", "llama32"),
                     default=None,
                     help="launch only this kernel --launches times, eagerly, for counter runs: "
-                         "decode_wb / decode_m4_wb = the [11008,4096] product at 1 / 4 tokens on rotated "
+                         "decode_wb / decode_m4_wb / decode_m8_wb = the [11008,4096] product at 1 / 4 / 8 "
+                         "tokens on rotated "
                          "weights, llama32 = the 32-layer decode, --launches tokens (one graph each), "
                          "prefill_wb = the M=2048 product on [11008,4096], "
                          "w4a8_m1 / w4a8_m512 = the W4A8 product on [28672,8192], "
@@ -719,7 +720,7 @@ def kernel_only(args, w4, WL, torch, dev, to_dev, log, time_region):
         res = llama_decode(w4, torch, dev, time_region, log, g, tokens=n_launch)
         print(json.dumps(dict(res, kernel="llama32")), flush=True)
         return 0
-    m = 4 if args.kernel == "decode_m4_wb" else 1
+    m = {"decode_m4_wb": 4, "decode_m8_wb": 8}.get(args.kernel, 1)
     wt = to_dev(WL.weight("Wb"))
     q = w4.quantize_pack_int4(wt, g, torch.float16)
     del wt

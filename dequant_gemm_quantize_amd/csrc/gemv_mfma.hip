@@ -139,13 +139,17 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
 #pragma unroll
         for (int j = 0; j < 4; ++j) xf[i][j] = xp[16 * blk(i) + j];
     } else {
+      // a uniform base (this slice of x) plus a 32-bit lane offset: token
+      // tok's row starts tok * 2K bytes in, computed as (tok * K/128) << 8
+      // with full-rate 24-bit multiplies (tok < 64, K/128 <= 2^16)
+      const char* xb = (const char*)(x + k0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         int tok = 16 * tb + 4 * q + h;
         tok = tok < M ? tok : M - 1;
-        const u32x4* xp = (const u32x4*)(x + (int64_t)tok * K + k0) + l16;
+        const uint32_t xo = (__umul24((uint32_t)tok, (uint32_t)(K / 128)) << 8) + 16u * (uint32_t)l16;
 #pragma unroll
-        for (int i = 0; i < kBlocks; ++i) xr[i][q] = xp[16 * blk(i)];
+        for (int i = 0; i < kBlocks; ++i) xr[i][q] = *(const u32x4*)(xb + xo + 256u * (uint32_t)blk(i));
       }
     }
   };
@@ -165,11 +169,16 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
     }
   };
 
-  int64_t rows[RB];
+  // Rows of the workgroup that exist (rows past N repeat the last one and
+  // are never stored).  Every weight-side load below is a uniform base at
+  // row r0 plus a 32-bit lane offset of at most 16 RB rows, formed with
+  // full-rate 24-bit multiplies (row < 64, K/2 <= 2^22, ng <= 2^16).
+  const int nvr = (int)(N - r0 < 16 * RB ? N - r0 : 16 * RB);
+  uint32_t srow[RB];  // byte offset of the lane's scale row
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int64_t r = r0 + 16 * rb + l16;
-    rows[rb] = r < N ? r : N - 1;
+    const int rr = 16 * rb + l16 < nvr ? 16 * rb + l16 : nvr - 1;
+    srow[rb] = __umul24((uint32_t)rr, (uint32_t)ng * (uint32_t)sizeof(R));
   }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const NibConst nk = NibConst::make();
@@ -189,8 +198,10 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if (G128 && (!SL || (ng % kBlocks == 0 && nb == kBlocks))) {  // 4 aligned, in-range scales
-        const V4 s4 = *(const V4*)((const R*)scales + rows[rb] * ng + k0 / 128);
-        const V4 z4 = *(const V4*)((const R*)zeros + rows[rb] * ng + k0 / 128);
+        const char* sb = (const char*)((const R*)scales + r0 * ng + k0 / 128);
+        const char* zb = (const char*)((const R*)zeros + r0 * ng + k0 / 128);
+        const V4 s4 = *(const V4*)(sb + srow[rb]);
+        const V4 z4 = *(const V4*)(zb + srow[rb]);
 #pragma unroll
         for (int i = 0; i < kBlocks; ++i) {
           sv[rb][i] = GV<TS>::at(s4, i);
@@ -200,8 +211,10 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
 #pragma unroll
         for (int i = 0; i < kBlocks; ++i) {
           const int gi = (int)((k0 + 128 * blk(i)) / g);
-          sv[rb][i] = ((const R*)scales)[rows[rb] * ng + gi];
-          zv[rb][i] = ((const R*)zeros)[rows[rb] * ng + gi];
+          const char* sb = (const char*)((const R*)scales + r0 * ng + gi);
+          const char* zb = (const char*)((const R*)zeros + r0 * ng + gi);
+          sv[rb][i] = *(const R*)(sb + srow[rb]);
+          zv[rb][i] = *(const R*)(zb + srow[rb]);
         }
       }
     }
@@ -209,15 +222,18 @@ __global__ __launch_bounds__((MT >= 2 || SL) ? 512 : 1024) void k_w4a16_gemv(
     // workgroup, 16-byte chunk l16 of the slice's run (chunks past the
     // slice's blocks repeat its last chunk)
     u32x4 cr[RB][4];
+    {
+      const char* cb = (const char*)(packed + r0 * (K / 2) + k0 / 2);
+      const uint32_t c16 = 16u * (uint32_t)(l16 < 4 * nb ? l16 : 4 * nb - 1);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t rj = r0 + 16 * rb + 4 * j + h;
-        rj = rj < N ? rj : N - 1;
-        const int c = l16 < 4 * nb ? l16 : 4 * nb - 1;
-        cr[rb][j] = __builtin_nontemporal_load((const u32x4*)(packed + rj * (K / 2) + k0 / 2) + c);
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int rr = 16 * rb + 4 * j + h < nvr ? 16 * rb + 4 * j + h : nvr - 1;
+          const uint32_t co = __umul24((uint32_t)rr, (uint32_t)(K / 2)) + c16;
+          cr[rb][j] = __builtin_nontemporal_load((const u32x4*)(cb + co));
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // regroup through the wave's LDS region into operand order: lane (l16,
     // h) takes row l16, chunk 4 i + h of block i (row t's chunk c at slot
