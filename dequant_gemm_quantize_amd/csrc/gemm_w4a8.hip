@@ -22,6 +22,11 @@
 // per workgroup while it is written to LDS; the activation tile is copied as
 // is.  Both are double-buffered in LDS; the global loads of x run one K step
 // ahead and those of the weights two, held in registers.
+// Split K (a caller's workspace, shapes with fewer than 128 tiles): workgroup
+// (tile, s) covers a contiguous range of K steps and writes its token-scaled
+// float32 partial tile to the workspace; k_splitk_reduce adds the splits in
+// order and rounds once.  A split boundary falls between K steps, so every
+// integer sum stays exact.
 #include <type_traits>
 
 #include "w4_common.h"
